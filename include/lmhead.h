@@ -1,0 +1,221 @@
+/*
+ * lmhead.h -- C ABI of liblmhead.so: weight-only-quantized LM-head logits on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The library computes, for a language-model head whose weight W[V, K] is
+ * stored as symmetric int4 (q in [-8, 7]) or int8 (q in [-128, 127]) codes with
+ * one fp16/bf16 scale per group of G input columns,
+ *
+ *     y[m, v] = sum_k x[m, k] * q[v, k] * s[v, k / G]   (+ bias[v])
+ *
+ * straight from the packed codes, never forming the dense weight (vLLM PR
+ * #48870 "Fused WNA16 GEMM for tied quantized lm_head logits", Purpose: a fused
+ * dequant-GEMM in place of dequantize-then-F.linear).  Around it sit the
+ * load-time quantizer (page "radiance_lmhead_int4.py", docstring "How"
+ * paragraph and quantize_int4_rows), the packer into this library's own
+ * layout, and the top-K exact rescoring step (vLLM PR #48870, review comment,
+ * point 2).
+ *
+ * Conventions for every entry point
+ *   - All data pointers are DEVICE pointers (hipMalloc'd or torch CUDA/HIP
+ *     tensors) unless stated otherwise; the caller allocates and owns every
+ *     buffer, including workspaces.  The library never allocates, frees or
+ *     copies between host and device.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
+ *     is enqueued on it and the call returns without synchronising.
+ *   - Every argument is validated on the host before anything is launched; on
+ *     an error nothing is enqueued and the status says why.  A launch the HIP
+ *     runtime rejects returns LMH_E_HIP.  No exception crosses the ABI.
+ *   - Inputs must be finite; NaN/Inf inputs give unspecified (but memory-safe)
+ *     results.
+ *   - Data pointers must be 16-byte aligned unless stated otherwise.
+ *   - M == 0 or V == 0 is a valid empty call: LMH_OK, nothing launched.
+ *   - Calls are thread-safe; concurrent calls on different streams are fine.
+ *
+ * dtype codes: LMH_F32 = 0, LMH_F16 = 1 (IEEE binary16), LMH_BF16 = 2.
+ *
+ * Packed blob layout (lmhead_pack writes it, lmhead_logits reads it)
+ *   span  = 128 columns for int4, 64 for int8;  NC = K / span;  NG = K / G.
+ *   Rows are taken in blocks of 64 (NB = ceil(V/64), V_pad = 64*NB); rows
+ *   V..V_pad-1 are padding with q = 0 and scale 0.
+ *   Weight region, byte offset of the 16-byte slot for
+ *     (block b, superchunk c, slot t in 0..3, row r in 0..63):
+ *         (((b*NC + c)*4 + t)*64 + r) * 16
+ *   int4: the slot is four little-endian 32-bit words j = 0..3; word j holds
+ *     columns 128c + 32j + 8t + i, i = 0..7, as unsigned nibbles q + 8; the
+ *     nibble at bits 4p..4p+3 holds column i = 2p for p < 4 and i = 2(p-4)+1
+ *     for p >= 4 (even columns in the low half-word, odd in the high one).
+ *   int8: word j holds columns 64c + 32(j>>1) + 8t + 4(j&1) + i, i = 0..3, in
+ *     byte i, as unsigned bytes q + 128.
+ *   Scale region, starting at byte V_pad*K*bits/8: 16-bit scales (fp16 or
+ *     bf16 bit patterns), element offset (b*NG + g)*64 + r.
+ *   Total size: V_pad*K*bits/8 + V_pad*NG*2 bytes (lmhead_packed_bytes).
+ *   Why: a lane that owns a row reads one 16-byte slot per 32 (int8: 16)
+ *   columns, 64 consecutive rows read 1 KiB contiguously, and the same slot,
+ *   read by 16 rows x 4 slots, is exactly one 16x16x32 MFMA B-operand tile
+ *   for each of its 32-column words.
+ *
+ * Supported shapes: bits in {4, 8}; K % span == 0; G % 32 == 0; K % G == 0;
+ * G divides the span or is a multiple of it (int4: G in {32, 64} or a
+ * multiple of 128; int8: G = 32 or a multiple of 64); K <= 65536; V < 2^31;
+ * M <= 65535.
+ */
+#ifndef LMHEAD_H
+#define LMHEAD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    LMH_OK = 0,
+    LMH_E_NULL = 1,        /* a required pointer is NULL */
+    LMH_E_SHAPE = 2,       /* a size is out of range or sizes disagree */
+    LMH_E_DTYPE = 3,       /* a dtype code is not allowed for that argument */
+    LMH_E_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+    LMH_E_UNSUPPORTED = 5, /* a valid request this build does not implement */
+    LMH_E_WORKSPACE = 6,   /* workspace missing or smaller than required */
+    LMH_E_HIP = 7          /* the HIP runtime reported an error */
+};
+
+enum { LMH_F32 = 0, LMH_F16 = 1, LMH_BF16 = 2 };
+enum { LMH_CLIP_RTN = 0, LMH_CLIP_MSE = 1 };
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* lmhead_status_string(int status);
+
+/* ABI version of this header; bumped when any signature or the layout changes. */
+int lmhead_abi_version(void);
+
+/*
+ * lmhead_packed_bytes -- size in bytes of the packed blob for a V x K head,
+ * or 0 if the shape is not supported.  Host-only; launches nothing.
+ */
+size_t lmhead_packed_bytes(int64_t V, int64_t K, int bits, int64_t group);
+
+/*
+ * lmhead_quantize -- load-time symmetric per-group quantizer.
+ *   Defined by page "radiance_lmhead_int4.py" (docstring "How" paragraph;
+ *   module constants CLIP_RATIOS, QMAX, ZP_BIAS; quantize_int4_rows), extended
+ *   to int8 and to fp16 scales.  For each row v and group g of G columns:
+ *     amax = max |w|; amax == 0 gives s = 0 and q = 0 for the group;
+ *     for each clip ratio r (RTN: 1.0 only; MSE: 1.0, 0.95, 0.9, 0.85, 0.8):
+ *       s_r = to16( max( fl32(amax * fl32(r / qmax)), floor ) ), floor = 1e-8
+ *             for bf16 scales and 2^-24 for fp16 scales, to16 = round to the
+ *             scale type, nearest-even;
+ *       q_r = clamp( rint( fl32(w / s_r) ), qmin, qmax )  (IEEE division,
+ *             ties to even);
+ *       err_r = sum over k ascending of (q_r*s_r - w)^2, fp64, one fused
+ *             multiply-add per element;
+ *     keep the first r whose err_r is strictly smaller than all earlier ones.
+ *   qmax/qmin = 7/-8 (int4) or 127/-128 (int8).  Results are bit-exact
+ *   (deterministic, no atomics).
+ *   w      [V, K] row-major, w_dtype LMH_F32 / LMH_F16 / LMH_BF16.
+ *   q_out  [V, K] int8 row-major (the code q itself, not biased).
+ *   s_out  [V, K/G] 16-bit scale bit patterns, scale_dtype LMH_F16 / LMH_BF16.
+ *   clip   LMH_CLIP_RTN or LMH_CLIP_MSE.
+ *   Shape rules: G % 32 == 0 and K % G == 0 (the packing span is not needed).
+ *   A scale that overflows the scale type is a precondition violation.
+ */
+int lmhead_quantize(const void* w, int w_dtype, int64_t V, int64_t K, int bits, int64_t group,
+                    int scale_dtype, int clip, int8_t* q_out, void* s_out, void* stream);
+
+/*
+ * lmhead_pack -- write the packed blob (layout above) from the canonical
+ *   codes q [V, K] int8 and scales s [V, K/G] (16-bit patterns).  Codes outside
+ *   [qmin, qmax] are a precondition violation.  Deterministic: the same input
+ *   gives the same bytes (packing twice is harmless).
+ *   packed_out must hold lmhead_packed_bytes(V, K, bits, group) bytes.
+ */
+int lmhead_pack(const int8_t* q, const void* s, int64_t V, int64_t K, int bits, int64_t group,
+                void* packed_out, void* stream);
+
+/*
+ * lmhead_logits_workspace_bytes -- device workspace that lmhead_logits needs
+ *   for M rows of x: 0 for fp16 x; for bf16 x, room for x converted to fp16
+ *   with a per-row power-of-two scale (M*K*2 and M*4 bytes, each rounded up
+ *   to a multiple of 256).
+ */
+size_t lmhead_logits_workspace_bytes(int64_t M, int64_t K, int x_dtype);
+
+/*
+ * lmhead_logits -- y[m, v] = sum_k x[m,k] * q[v,k] * s[v,k/G] (+ bias[v]).
+ *   The fused weight-only-quantized logits of vLLM PR #48870 (Purpose; perf
+ *   table: W4-g64 / W8-g128 heads at M = 1, 32, 256), read straight from the
+ *   packed blob.  The codes q enter the arithmetic exactly; each group's
+ *   partial sum is accumulated in fp32 and multiplied by its scale in fp32.
+ *   x       [M, K] row-major, x_dtype LMH_F16 or LMH_BF16 (bf16 rows are
+ *           converted to fp16 with an exact power-of-two row scale first; this
+ *           needs the workspace).
+ *   packed  the blob for (V, K, bits, group, scale_dtype).
+ *   bias    [V] fp32 or NULL.
+ *   y       [M, ldy] fp32 row-major, ldy >= V; columns V..ldy-1 are not
+ *           written.  Needs only 4-byte alignment.
+ *   workspace / ws_bytes: at least lmhead_logits_workspace_bytes(M, K, x_dtype)
+ *           (may be NULL/0 for fp16 x).
+ *   Small M runs a split-free GEMV (one lane per vocabulary row); larger M
+ *   runs a 16x16x32 fp16 MFMA kernel.  The result does not depend on the
+ *   stream or on other calls.
+ */
+int lmhead_logits(const void* x, int x_dtype, int64_t M, const void* packed, int64_t V, int64_t K,
+                  int bits, int64_t group, int scale_dtype, const float* bias, float* y,
+                  int64_t ldy, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * lmhead_logits_path -- lmhead_logits with the kernel chosen by the caller:
+ *   path 0 = automatic (exactly lmhead_logits), 1 = the lane-per-row GEMV
+ *   (M <= 4, else LMH_E_UNSUPPORTED), 2 = the MFMA kernel (any M).  Both
+ *   kernels compute the same function; this entry point exists to test and
+ *   time each of them on the same shapes.
+ */
+int lmhead_logits_path(const void* x, int x_dtype, int64_t M, const void* packed, int64_t V,
+                       int64_t K, int bits, int64_t group, int scale_dtype, const float* bias,
+                       float* y, int64_t ldy, void* workspace, size_t ws_bytes, int path,
+                       void* stream);
+
+/*
+ * lmhead_dense_logits -- y[m, v] = sum_k x[m,k] * W[v,k] with an unquantized
+ *   16-bit weight: the bandwidth control of the fp16 logits GEMV (vLLM PR
+ *   #48870, review comment, point 1).  fp32 accumulation.
+ *   x [M, K] and W [V, K] row-major, both LMH_F16 or both LMH_BF16; K % 8 == 0.
+ *   y [M, ldy] fp32, ldy >= V (4-byte alignment).  M <= 8.
+ */
+int lmhead_dense_logits(const void* x, int x_dtype, int64_t M, const void* w, int w_dtype,
+                        int64_t V, int64_t K, float* y, int64_t ldy, void* stream);
+
+/*
+ * lmhead_topk_workspace_bytes -- device workspace lmhead_topk_rescore needs.
+ */
+size_t lmhead_topk_workspace_bytes(int64_t M, int64_t V, int topk);
+
+/*
+ * lmhead_topk_rescore -- exact rescoring of the top-K quantized logits (vLLM
+ *   PR #48870, review comment, point 2: take the top-K of the quantized logits,
+ *   recompute those K rows exactly from the unquantized weight, scatter back).
+ *   For each row m of y [M, ldy] (fp32, in/out):
+ *     I = the topk largest of y[m, 0..V), ordered by value descending, then
+ *         index ascending;
+ *     for v in I: y[m, v] = sum_k x[m,k] * w_ref[v,k] in fp32 (fixed
+ *         summation order; error within gamma_K * sum |x w|);
+ *     idx_out[m, t] = I[t]  (int32), val_out[m, t] = the new y[m, I[t]];
+ *     top1_out[m] = the first (lowest-index) maximum of the updated row.
+ *   x [M, K] LMH_F16 or LMH_BF16; w_ref [V, K] LMH_F16, LMH_BF16 or LMH_F32,
+ *   row-major (only the topk selected rows are read).  1 <= topk <= 64 and
+ *   topk <= V.  Any of idx_out / val_out / top1_out may be NULL.  Alignment:
+ *   x 2 bytes, w_ref and y 4 bytes, workspace 16 bytes.
+ *   workspace: at least lmhead_topk_workspace_bytes(M, V, topk) bytes.
+ *   Deterministic (no atomics).
+ */
+int lmhead_topk_rescore(const void* x, int x_dtype, int64_t M, const void* w_ref, int w_dtype,
+                        int64_t V, int64_t K, float* y, int64_t ldy, int topk, int32_t* idx_out,
+                        float* val_out, int32_t* top1_out, void* workspace, size_t ws_bytes,
+                        void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LMHEAD_H */

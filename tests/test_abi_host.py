@@ -1,0 +1,149 @@
+"""Host-side checks of the C ABI (no GPU needed, nothing launched).
+
+  * liblmhead.so loads and exports every function include/lmhead.h declares;
+  * the size helpers agree with the layout definition (and with the oracle);
+  * every validation error path returns its status before any HIP call.
+Calls here only pass arguments the library must reject, or empty (M == 0 / V == 0)
+requests, so no kernel is ever launched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+import weight_only_quantized_lmhead_amd as lmh
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lmhead.h")
+
+OK, E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_UNSUP, E_WS, E_HIP = range(8)
+F32, F16, BF16 = 0, 1, 2
+P = 0x10000  # a fake, 16-byte-aligned non-null address: never dereferenced on these paths
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lmhead_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = lmh.lib()
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in lmhead.h but not exported"
+    assert L.lmhead_abi_version() == 1
+
+
+def test_status_strings():
+    L = lmh.lib()
+    for s in range(8):
+        assert L.lmhead_status_string(s).startswith(b"LMH_")
+    assert b"unknown" in L.lmhead_status_string(99)
+
+
+@pytest.mark.parametrize("V,K,bits,G", [(151936, 1024, 4, 64), (151936, 1024, 8, 128),
+                                        (151936, 2048, 8, 2048), (248064, 5120, 4, 128),
+                                        (50304, 512, 4, 64), (1, 128, 4, 32), (65, 64, 8, 32),
+                                        (100, 256, 4, 256), (7, 384, 4, 128)])
+def test_packed_bytes_matches_layout(V, K, bits, G):
+    assert lmh.packed_bytes(V, K, bits, G) == oracle.packed_bytes(V, K, bits, G)
+
+
+@pytest.mark.parametrize("V,K,bits,G", [(10, 100, 4, 50), (10, 192, 4, 64), (10, 96, 8, 32),
+                                        (10, 384, 4, 96), (10, 128, 3, 32), (10, 128, 4, 16),
+                                        (10, 256, 8, 96)])
+def test_packed_bytes_rejects(V, K, bits, G):
+    assert lmh.lib().lmhead_packed_bytes(V, K, bits, G) == 0
+
+
+def _logits(**kw):
+    a = dict(x=P, xd=F16, M=1, packed=P, V=128, K=128, bits=4, G=64, sd=F16, bias=None, y=P,
+             ldy=128, ws=None, wsn=0, path=0, st=None)
+    a.update(kw)
+    return lmh.lib().lmhead_logits_path(a["x"], a["xd"], a["M"], a["packed"], a["V"], a["K"],
+                                        a["bits"], a["G"], a["sd"], a["bias"], a["y"], a["ldy"],
+                                        a["ws"], a["wsn"], a["path"], a["st"])
+
+
+def test_logits_validation():
+    assert _logits(bits=3) == E_UNSUP
+    assert _logits(K=100) == E_SHAPE
+    assert _logits(K=192) == E_SHAPE          # int4 needs K % 128 == 0
+    assert _logits(G=48) == E_SHAPE
+    assert _logits(K=384, G=96) == E_UNSUP    # a 96-column group straddles 128-column superchunks
+    assert _logits(xd=F32) == E_DTYPE
+    assert _logits(sd=F32) == E_DTYPE
+    assert _logits(M=-1) == E_SHAPE
+    assert _logits(M=70000) == E_SHAPE
+    assert _logits(ldy=100) == E_SHAPE
+    assert _logits(x=None) == E_NULL
+    assert _logits(packed=None) == E_NULL
+    assert _logits(y=None) == E_NULL
+    assert _logits(x=P + 8) == E_ALIGN
+    assert _logits(packed=P + 4) == E_ALIGN
+    assert _logits(y=P + 2) == E_ALIGN
+    assert _logits(xd=BF16) == E_WS           # bf16 x needs the conversion workspace
+    assert _logits(xd=BF16, ws=P, wsn=16) == E_WS
+    assert _logits(path=1, M=5) == E_UNSUP   # the GEMV serves M <= 4
+    assert _logits(path=3) == E_UNSUP
+    # empty requests are valid and launch nothing
+    assert _logits(M=0) == OK
+    assert _logits(V=0) == OK
+
+
+def test_workspace_sizes():
+    L = lmh.lib()
+    assert L.lmhead_logits_workspace_bytes(4, 1024, F16) == 0
+    n = L.lmhead_logits_workspace_bytes(3, 5120, BF16)
+    assert n >= 3 * 5120 * 2 + 3 * 4 and n % 256 == 0
+    assert L.lmhead_topk_workspace_bytes(1, 151936, 8) >= 1 * 38 * 9 * 8
+    assert L.lmhead_topk_workspace_bytes(1, 151936, 65) == 0
+
+
+def test_quantize_pack_validation():
+    L = lmh.lib()
+    q = L.lmhead_quantize
+    assert q(P, F32, 4, 128, 5, 64, F16, 0, P, P, None) == E_UNSUP
+    assert q(P, 7, 4, 128, 4, 64, F16, 0, P, P, None) == E_DTYPE
+    assert q(P, F32, 4, 128, 4, 64, F32, 0, P, P, None) == E_DTYPE
+    assert q(P, F32, 4, 128, 4, 64, F16, 2, P, P, None) == E_UNSUP
+    assert q(P, F32, 4, 100, 4, 64, F16, 0, P, P, None) == E_SHAPE
+    assert q(P, F32, 4, 128, 4, 16, F16, 0, P, P, None) == E_SHAPE
+    assert q(None, F32, 4, 128, 4, 64, F16, 0, P, P, None) == E_NULL
+    assert q(P + 4, F32, 4, 128, 4, 64, F16, 0, P, P, None) == E_ALIGN
+    assert q(P, F32, 0, 128, 4, 64, F16, 0, P, P, None) == OK
+    pk = L.lmhead_pack
+    assert pk(P, P, 4, 100, 4, 64, P, None) == E_SHAPE
+    assert pk(None, P, 4, 128, 4, 64, P, None) == E_NULL
+    assert pk(P, P, 4, 128, 4, 64, P + 1, None) == E_ALIGN
+    assert pk(P, P, 0, 128, 4, 64, P, None) == OK
+
+
+def test_dense_and_topk_validation():
+    L = lmh.lib()
+    d = L.lmhead_dense_logits
+    assert d(P, F16, 1, P, BF16, 10, 64, P, 10, None) == E_DTYPE
+    assert d(P, F32, 1, P, F32, 10, 64, P, 10, None) == E_DTYPE
+    assert d(P, F16, 5, P, F16, 10, 64, P, 10, None) == E_SHAPE
+    assert d(P, F16, 1, P, F16, 10, 60, P, 10, None) == E_SHAPE
+    assert d(P, F16, 1, P, F16, 10, 64, P, 9, None) == E_SHAPE
+    assert d(None, F16, 1, P, F16, 10, 64, P, 10, None) == E_NULL
+    assert d(P, F16, 0, P, F16, 10, 64, P, 10, None) == OK
+    t = L.lmhead_topk_rescore
+    args = lambda **k: [k.get("x", P), k.get("xd", F16), k.get("M", 1), k.get("w", P),
+                        k.get("wd", F16), k.get("V", 100), k.get("K", 64), k.get("y", P),
+                        k.get("ldy", 100), k.get("topk", 8), None, None, None, k.get("ws", P),
+                        k.get("wsn", 1 << 20), None]
+    assert t(*args(topk=0)) == E_SHAPE
+    assert t(*args(topk=65)) == E_SHAPE
+    assert t(*args(topk=101)) == E_SHAPE
+    assert t(*args(xd=F32)) == E_DTYPE
+    assert t(*args(wd=5)) == E_DTYPE
+    assert t(*args(ws=None)) == E_WS
+    assert t(*args(wsn=8)) == E_WS
+    assert t(*args(y=None)) == E_NULL
+    assert t(*args(M=0)) == OK

@@ -1,0 +1,147 @@
+"""GPU logits (GEMV and MFMA kernels) against the fp64 oracle on small heads that
+still span several row blocks, several superchunks per wave and a ragged tail."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import weight_only_quantized_lmhead_amd as lmh
+from gpu_common import DEV, OD, TD, abs_terms, bits16, check_logits, gpu, need_gpu, to_dev
+
+pytestmark = gpu
+
+GEMV, MFMA = lmh.PATH_GEMV, lmh.PATH_MFMA
+
+
+def _head(V, K, bits, G, sdt, seed, zero_rows=()):
+    w = synth.random_weight((V, K), 0.02, seed, zero_rows)
+    w[::17, ::13] *= 8.0  # outliers
+    q, s = oracle.quantize(w, bits, G, OD[sdt])
+    blob = oracle.pack(q, s, bits, G)
+    return q, s, torch.from_numpy(blob).to(DEV)
+
+
+def _run(xnp, xdt, blob, V, K, bits, G, sdt, path, bias=None, ldy=None):
+    x = to_dev(xnp, xdt)
+    M = xnp.shape[0]
+    ldy = ldy or V
+    out = torch.full((M, ldy), float("nan"), dtype=torch.float32, device=DEV)
+    b = None if bias is None else torch.from_numpy(bias).to(DEV)
+    lmh.logits(x, blob, V, K, bits, G, TD[sdt], bias=b, out=out, path=path)
+    torch.cuda.synchronize()
+    y = out.cpu().numpy()
+    if ldy > V:
+        assert np.isnan(y[:, V:]).all(), "columns past V were written"
+    return y[:, :V]
+
+
+CASES = [  # bits, G, K
+    (4, 32, 512), (4, 64, 1024), (4, 128, 512), (4, 256, 1024), (4, 1024, 1024),
+    (8, 32, 256), (8, 64, 512), (8, 128, 1024), (8, 512, 512),
+]
+
+
+@pytest.mark.parametrize("bits,G,K", CASES)
+@pytest.mark.parametrize("xdt,sdt", [("f16", "f16"), ("bf16", "bf16"), ("f16", "bf16")])
+@pytest.mark.parametrize("path,Ms", [(GEMV, (1, 2, 3, 4)), (MFMA, (1, 5, 16, 17, 40, 67))])
+def test_logits_small_vs_oracle(bits, G, K, xdt, sdt, path, Ms):
+    need_gpu()
+    V = 64 * 5 + 37
+    q, s, blob = _head(V, K, bits, G, sdt, seed=K + G + bits, zero_rows=(3, V - 1))
+    worst = 0.0
+    for M in Ms:
+        x = synth.random_x(M, K, seed=M, dtype=xdt)
+        y = _run(x, xdt, blob, V, K, bits, G, sdt, path)
+        y_or = oracle.logits(x, q, s, OD[sdt], G, x_dtype=OD[xdt])
+        y_abs = abs_terms(x, xdt, q, s, OD[sdt], G)
+        worst = max(worst, check_logits(y, y_or, y_abs, K, G, what=f"M={M} path={path}"))
+    print(f"bits={bits} G={G} K={K} x={xdt} s={sdt} path={path}: max row rel err {worst:.2e}")
+
+
+@pytest.mark.parametrize("path,M", [(GEMV, 1), (GEMV, 3), (MFMA, 8), (MFMA, 33)])
+def test_bias_and_row_stride(path, M):
+    need_gpu()
+    V, K, bits, G = 200, 512, 4, 64
+    q, s, blob = _head(V, K, bits, G, "f16", seed=5)
+    bias = synth.random_weight((1, V), 1.0, 6)[0]
+    x = synth.random_x(M, K, seed=9)
+    y = _run(x, "f16", blob, V, K, bits, G, "f16", path, bias=bias, ldy=V + 45)
+    y_or = oracle.logits(x, q, s, oracle.F16, G, bias=bias)
+    y_abs = abs_terms(x, "f16", q, s, oracle.F16, G)
+    check_logits(y, y_or, y_abs, K, G, what="bias", bias=bias)
+
+
+@pytest.mark.parametrize("bits,G", [(4, 64), (4, 128), (8, 128), (8, 32)])
+@pytest.mark.parametrize("path", [GEMV, MFMA])
+def test_one_hot_exposes_layout(bits, G, path):
+    """x = e_k gives y[v] = q[v,k] * s[v, k/G] exactly (one exact product): any
+    misplaced nibble, byte, slot or scale shows up bit for bit."""
+    need_gpu()
+    V, K = 130, 256
+    q, s, blob = _head(V, K, bits, G, "f16", seed=11)
+    sv = oracle.widen16(s, oracle.F16).astype(np.float64)
+    ks = [0, 1, 7, 8, 31, 32, 63, 64, 100, 127, 128, 200, 255]
+    for i in range(0, len(ks), 4):
+        kk = ks[i:i + 4]
+        x = np.zeros((len(kk), K), dtype=np.float16)
+        for m, k in enumerate(kk):
+            x[m, k] = 1.0
+        y = _run(x, "f16", blob, V, K, bits, G, "f16", path)
+        for m, k in enumerate(kk):
+            want = q[:, k].astype(np.float64) * sv[:, k // G]
+            assert np.array_equal(y[m].astype(np.float64), want), f"column {k}"
+
+
+@pytest.mark.parametrize("path,M", [(GEMV, 1), (GEMV, 4), (MFMA, 16), (MFMA, 64)])
+def test_invariants_zero_rows_scaling_determinism(path, M):
+    need_gpu()
+    V, K, bits, G = 320, 512, 4, 64
+    zero = (0, 64, 200, 319)
+    q, s, blob = _head(V, K, bits, G, "f16", seed=13, zero_rows=zero)
+    x = synth.random_x(M, K, seed=21)
+    y1 = _run(x, "f16", blob, V, K, bits, G, "f16", path)
+    y2 = _run(x, "f16", blob, V, K, bits, G, "f16", path)
+    assert np.array_equal(y1, y2), "two identical calls differ"
+    assert (y1[:, list(zero)] == 0).all()
+    x2 = (x.astype(np.float32) * 2).astype(np.float16)
+    y3 = _run(x2, "f16", blob, V, K, bits, G, "f16", path)
+    assert np.array_equal(y3, 2 * y1), "y(2x) != 2 y(x)"
+
+
+def test_gemv_and_mfma_agree():
+    need_gpu()
+    V, K, bits, G = 600, 1024, 4, 64
+    q, s, blob = _head(V, K, bits, G, "f16", seed=17)
+    for M in (1, 2, 3, 4):
+        x = synth.random_x(M, K, seed=30 + M)
+        a = _run(x, "f16", blob, V, K, bits, G, "f16", GEMV)
+        b = _run(x, "f16", blob, V, K, bits, G, "f16", MFMA)
+        scale = np.abs(a).max()
+        assert np.abs(a - b).max() <= 1e-5 * scale
+
+
+def test_bf16_activations_large_and_small_rows():
+    """bf16 rows far outside the fp16 range (and tiny ones) are handled by the
+    power-of-two row scale."""
+    need_gpu()
+    V, K, bits, G = 256, 512, 4, 128
+    q, s, blob = _head(V, K, bits, G, "bf16", seed=19)
+    xf = synth.random_weight((3, K), 1.0, 23)
+    xf[0] *= 1e6
+    xf[1] *= 1e-6
+    xf[2, 5] = 3e4
+    x = synth.to_bf16_bits(xf)
+    for path in (GEMV, MFMA):
+        y = _run(x, "bf16", blob, V, K, bits, G, "bf16", path)
+        y_or = oracle.logits(x, q, s, oracle.BF16, G, x_dtype=oracle.BF16)
+        y_abs = abs_terms(x, "bf16", q, s, oracle.BF16, G)
+        check_logits(y, y_or, y_abs, K, G, what=f"bf16 extremes path={path}")
+
+
+def test_empty_calls_launch_nothing():
+    need_gpu()
+    x = torch.zeros((0, 128), dtype=torch.float16, device=DEV)
+    blob = torch.zeros(lmh.packed_bytes(64, 128, 4, 64), dtype=torch.uint8, device=DEV)
+    y = lmh.logits(x, blob, 64, 128, 4, 64, torch.float16)
+    assert y.shape == (0, 64)

@@ -1,0 +1,196 @@
+"""Weight-only-quantized LM-head logits for AMD MI355X (gfx950).
+
+A thin ctypes binding over ``liblmhead.so`` (C ABI in ``include/lmhead.h``):
+argument marshalling only.  Every step of the path -- quantize, pack, logits,
+top-K rescoring -- runs in the library's HIP kernels; torch supplies device
+memory and the current stream.  There is no CPU fallback: if the library is
+missing or fails to load, importing the binding's functions raises.
+
+    import weight_only_quantized_lmhead_amd as lmh
+    q, s = lmh.quantize(w, bits=4, group=64, scale_dtype=torch.float16, clip="rtn")
+    packed = lmh.pack(q, s, bits=4, group=64)
+    y = lmh.logits(x, packed, V, K, bits=4, group=64, scale_dtype=torch.float16)
+    idx, val, top1 = lmh.topk_rescore(x, w_ref, y, topk=8)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblmhead.so")
+
+LMH_OK = 0
+_DT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+_CLIP = {"rtn": 0, "mse": 1}
+PATH_AUTO, PATH_GEMV, PATH_MFMA = 0, 1, 2
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class LmheadError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {lib().lmhead_status_string(status).decode()}")
+
+
+def lib() -> ctypes.CDLL:
+    """Load liblmhead.so (built in-tree by ``python -m weight_only_quantized_lmhead_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m weight_only_quantized_lmhead_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+        sig = {
+            "lmhead_status_string": (ctypes.c_char_p, [i32]),
+            "lmhead_abi_version": (i32, []),
+            "lmhead_packed_bytes": (sz, [i64, i64, i32, i64]),
+            "lmhead_quantize": (i32, [vp, i32, i64, i64, i32, i64, i32, i32, vp, vp, vp]),
+            "lmhead_pack": (i32, [vp, vp, i64, i64, i32, i64, vp, vp]),
+            "lmhead_logits_workspace_bytes": (sz, [i64, i64, i32]),
+            "lmhead_logits": (i32, [vp, i32, i64, vp, i64, i64, i32, i64, i32, vp, vp, i64, vp,
+                                    sz, vp]),
+            "lmhead_logits_path": (i32, [vp, i32, i64, vp, i64, i64, i32, i64, i32, vp, vp, i64,
+                                         vp, sz, i32, vp]),
+            "lmhead_dense_logits": (i32, [vp, i32, i64, vp, i32, i64, i64, vp, i64, vp]),
+            "lmhead_topk_workspace_bytes": (sz, [i64, i64, i32]),
+            "lmhead_topk_rescore": (i32, [vp, i32, i64, vp, i32, i64, i64, vp, i64, i32, vp, vp,
+                                          vp, vp, sz, vp]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != LMH_OK:
+        raise LmheadError(fn, rc)
+
+
+def _need_cuda(*ts: torch.Tensor) -> None:
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("lmhead tensors must live on the GPU")
+        if t is not None and not t.is_contiguous():
+            raise ValueError("lmhead tensors must be contiguous")
+
+
+def packed_bytes(V: int, K: int, bits: int, group: int) -> int:
+    n = lib().lmhead_packed_bytes(V, K, bits, group)
+    if n == 0:
+        raise ValueError(f"unsupported packed shape V={V} K={K} bits={bits} G={group}")
+    return int(n)
+
+
+def quantize(w: torch.Tensor, bits: int, group: int, scale_dtype: torch.dtype = torch.float16,
+             clip: str = "rtn") -> Tuple[torch.Tensor, torch.Tensor]:
+    """(q int8 [V,K], s [V,K/G] in scale_dtype) -- lmhead_quantize."""
+    _need_cuda(w)
+    V, K = w.shape
+    q = torch.empty((V, K), dtype=torch.int8, device=w.device)
+    s = torch.empty((V, K // group), dtype=scale_dtype, device=w.device)
+    _check("lmhead_quantize", lib().lmhead_quantize(
+        _ptr(w), _DT[w.dtype], V, K, bits, group, _DT[scale_dtype], _CLIP[clip], _ptr(q), _ptr(s),
+        _stream(w)))
+    return q, s
+
+
+def pack(q: torch.Tensor, s: torch.Tensor, bits: int, group: int) -> torch.Tensor:
+    """Packed blob (uint8) -- lmhead_pack."""
+    _need_cuda(q, s)
+    V, K = q.shape
+    out = torch.empty(packed_bytes(V, K, bits, group), dtype=torch.uint8, device=q.device)
+    _check("lmhead_pack", lib().lmhead_pack(_ptr(q), _ptr(s), V, K, bits, group, _ptr(out),
+                                            _stream(q)))
+    return out
+
+
+def logits_workspace(M: int, K: int, x_dtype: torch.dtype, device) -> Optional[torch.Tensor]:
+    n = int(lib().lmhead_logits_workspace_bytes(M, K, _DT[x_dtype]))
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def logits(x: torch.Tensor, packed: torch.Tensor, V: int, K: int, bits: int, group: int,
+           scale_dtype: torch.dtype, bias: Optional[torch.Tensor] = None,
+           out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+           path: int = PATH_AUTO) -> torch.Tensor:
+    """fp32 logits [M, V] (or into ``out`` [M, ldy]) -- lmhead_logits / lmhead_logits_path."""
+    _need_cuda(x, packed, bias)
+    M = x.shape[0]
+    if out is None:
+        out = torch.empty((M, V), dtype=torch.float32, device=x.device)
+    ldy = out.stride(0) if out.dim() == 2 else V
+    if workspace is None:
+        workspace = logits_workspace(M, K, x.dtype, x.device)
+    ws_n = 0 if workspace is None else workspace.numel()
+    _check("lmhead_logits", lib().lmhead_logits_path(
+        _ptr(x), _DT[x.dtype], M, _ptr(packed), V, K, bits, group, _DT[scale_dtype], _ptr(bias),
+        _ptr(out), ldy, _ptr(workspace), ws_n, path, _stream(x)))
+    return out
+
+
+def dense_logits(x: torch.Tensor, w: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp32 logits of an unquantized 16-bit weight -- lmhead_dense_logits (the control)."""
+    _need_cuda(x, w)
+    M, K = x.shape
+    V = w.shape[0]
+    if out is None:
+        out = torch.empty((M, V), dtype=torch.float32, device=x.device)
+    _check("lmhead_dense_logits", lib().lmhead_dense_logits(
+        _ptr(x), _DT[x.dtype], M, _ptr(w), _DT[w.dtype], V, K, _ptr(out), out.stride(0),
+        _stream(x)))
+    return out
+
+
+def topk_workspace(M: int, V: int, topk: int, device) -> torch.Tensor:
+    n = int(lib().lmhead_topk_workspace_bytes(M, V, topk))
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def topk_rescore(x: torch.Tensor, w_ref: torch.Tensor, y: torch.Tensor, topk: int,
+                 workspace: Optional[torch.Tensor] = None):
+    """In place on y; returns (idx int32 [M,topk], val fp32 [M,topk], top1 int32 [M])."""
+    _need_cuda(x, w_ref, y)
+    M, K = x.shape
+    V = w_ref.shape[0]
+    idx = torch.empty((M, topk), dtype=torch.int32, device=x.device)
+    val = torch.empty((M, topk), dtype=torch.float32, device=x.device)
+    top1 = torch.empty((M,), dtype=torch.int32, device=x.device)
+    if workspace is None:
+        workspace = topk_workspace(M, V, topk, x.device)
+    _check("lmhead_topk_rescore", lib().lmhead_topk_rescore(
+        _ptr(x), _DT[x.dtype], M, _ptr(w_ref), _DT[w_ref.dtype], V, K, _ptr(y), y.stride(0), topk,
+        _ptr(idx), _ptr(val), _ptr(top1), _ptr(workspace), workspace.numel(), _stream(x)))
+    return idx, val, top1
+
+
+class QuantizedHead:
+    """A packed LM head resident on the GPU: quantize + pack once, then logits per call."""
+
+    def __init__(self, w: torch.Tensor, bits: int, group: int,
+                 scale_dtype: torch.dtype = torch.float16, clip: str = "rtn"):
+        self.V, self.K = w.shape
+        self.bits, self.group, self.scale_dtype = bits, group, scale_dtype
+        q, s = quantize(w, bits, group, scale_dtype, clip)
+        self.packed = pack(q, s, bits, group)
+
+    def __call__(self, x: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        return logits(x, self.packed, self.V, self.K, self.bits, self.group, self.scale_dtype,
+                      bias=bias, out=out)

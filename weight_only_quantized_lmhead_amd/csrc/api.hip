@@ -1,0 +1,196 @@
+// C ABI of liblmhead.so (declared in include/lmhead.h).
+//
+// Every entry point validates its arguments on the host before touching the
+// HIP runtime, so each error path can be exercised without a GPU.  Work is
+// enqueued on the caller's stream; nothing here allocates or synchronises.
+#include "lmh_internal.h"
+#include "lmhead.h"
+
+namespace {
+
+using lmh::BF16;
+using lmh::F16;
+using lmh::F32;
+
+constexpr int kAbiVersion = 1;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shape rules shared by pack and logits.
+int check_layout(int64_t V, int64_t K, int bits, int64_t G) {
+    if (bits != 4 && bits != 8) return LMH_E_UNSUPPORTED;
+    if (V < 0 || V >= (int64_t(1) << 31)) return LMH_E_SHAPE;
+    if (K < 1 || K > 65536 || G < 32 || G > K) return LMH_E_SHAPE;
+    const int64_t span = lmh::span_of(bits);
+    if (K % span != 0 || K % G != 0 || G % 32 != 0) return LMH_E_SHAPE;
+    // a group is either a whole number of superchunks or divides one
+    if (!(G % span == 0 || span % G == 0)) return LMH_E_UNSUPPORTED;
+    return LMH_OK;
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? LMH_OK : LMH_E_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* lmhead_status_string(int status) {
+    switch (status) {
+    case LMH_OK: return "LMH_OK";
+    case LMH_E_NULL: return "LMH_E_NULL: a required pointer is NULL";
+    case LMH_E_SHAPE: return "LMH_E_SHAPE: size out of range or inconsistent";
+    case LMH_E_DTYPE: return "LMH_E_DTYPE: dtype not allowed for this argument";
+    case LMH_E_ALIGN: return "LMH_E_ALIGN: pointer not 16-byte aligned";
+    case LMH_E_UNSUPPORTED: return "LMH_E_UNSUPPORTED: combination not implemented";
+    case LMH_E_WORKSPACE: return "LMH_E_WORKSPACE: workspace missing or too small";
+    case LMH_E_HIP: return "LMH_E_HIP: the HIP runtime reported an error";
+    default: return "unknown lmhead status";
+    }
+}
+
+int lmhead_abi_version(void) { return kAbiVersion; }
+
+size_t lmhead_packed_bytes(int64_t V, int64_t K, int bits, int64_t group) {
+    if (check_layout(V, K, bits, group) != LMH_OK) return 0;
+    const int64_t vpad = (V + 63) / 64 * 64;
+    return (size_t)(vpad * K * bits / 8 + vpad * (K / group) * 2);
+}
+
+int lmhead_quantize(const void* w, int w_dtype, int64_t V, int64_t K, int bits, int64_t group,
+                    int scale_dtype, int clip, int8_t* q_out, void* s_out, void* stream) {
+    if (bits != 4 && bits != 8) return LMH_E_UNSUPPORTED;
+    if (w_dtype != F32 && w_dtype != F16 && w_dtype != BF16) return LMH_E_DTYPE;
+    if (scale_dtype != F16 && scale_dtype != BF16) return LMH_E_DTYPE;
+    if (clip != LMH_CLIP_RTN && clip != LMH_CLIP_MSE) return LMH_E_UNSUPPORTED;
+    if (V < 0 || K < 1 || group < 32 || group % 32 != 0 || K % group != 0) return LMH_E_SHAPE;
+    if (V * K >= (int64_t(1) << 40)) return LMH_E_SHAPE;
+    if (V == 0) return LMH_OK;
+    if (!w || !q_out || !s_out) return LMH_E_NULL;
+    if (!aligned16(w) || !aligned16(q_out)) return LMH_E_ALIGN;
+    if (((uintptr_t)s_out & 1u) != 0) return LMH_E_ALIGN;
+    return from_hip(lmh::launch_quantize(w, w_dtype, V, K, bits, group, scale_dtype,
+                                         clip == LMH_CLIP_MSE ? 5 : 1, q_out, (uint16_t*)s_out,
+                                         (hipStream_t)stream));
+}
+
+int lmhead_pack(const int8_t* q, const void* s, int64_t V, int64_t K, int bits, int64_t group,
+                void* packed_out, void* stream) {
+    const int rc = check_layout(V, K, bits, group);
+    if (rc != LMH_OK) return rc;
+    if (V == 0) return LMH_OK;
+    if (!q || !s || !packed_out) return LMH_E_NULL;
+    if (!aligned16(q) || !aligned16(packed_out)) return LMH_E_ALIGN;
+    if (((uintptr_t)s & 1u) != 0) return LMH_E_ALIGN;
+    return from_hip(lmh::launch_pack(q, (const uint16_t*)s, V, K, bits, group, (uint8_t*)packed_out,
+                                     (hipStream_t)stream));
+}
+
+size_t lmhead_logits_workspace_bytes(int64_t M, int64_t K, int x_dtype) {
+    if (x_dtype != BF16 || M <= 0 || K <= 0) return 0;
+    return (size_t)(((M * K * 2 + 255) / 256) * 256 + ((M * 4 + 255) / 256) * 256);
+}
+
+static int logits_impl(const void* x, int x_dtype, int64_t M, const void* packed, int64_t V,
+                       int64_t K, int bits, int64_t group, int scale_dtype, const float* bias,
+                       float* y, int64_t ldy, void* workspace, size_t ws_bytes, void* stream,
+                       int path) {
+    int rc = check_layout(V, K, bits, group);
+    if (rc != LMH_OK) return rc;
+    if (x_dtype != F16 && x_dtype != BF16) return LMH_E_DTYPE;
+    if (scale_dtype != F16 && scale_dtype != BF16) return LMH_E_DTYPE;
+    if (M < 0 || M > 65535) return LMH_E_SHAPE;
+    if (path < 0 || path > 2) return LMH_E_UNSUPPORTED;
+    if (M == 0 || V == 0) return LMH_OK;
+    if (ldy < V) return LMH_E_SHAPE;
+    if (!x || !packed || !y) return LMH_E_NULL;
+    if (!aligned16(x) || !aligned16(packed)) return LMH_E_ALIGN;
+    if (((uintptr_t)y & 3u) != 0 || (bias && ((uintptr_t)bias & 3u) != 0)) return LMH_E_ALIGN;
+    const size_t need = lmhead_logits_workspace_bytes(M, K, x_dtype);
+    if (need > 0) {
+        if (!workspace || ws_bytes < need) return LMH_E_WORKSPACE;
+        if (!aligned16(workspace)) return LMH_E_ALIGN;
+    }
+    if (path == 1 && M > lmh::kGemvMaxM) return LMH_E_UNSUPPORTED;
+
+    hipStream_t st = (hipStream_t)stream;
+    lmh::LogitsArgs a;
+    a.x = x;
+    a.xexp = nullptr;
+    if (x_dtype == BF16) {
+        _Float16* xh = (_Float16*)workspace;
+        int* xe = (int*)((char*)workspace + ((M * K * 2 + 255) / 256) * 256);
+        hipError_t e = lmh::launch_x_to_f16((const uint16_t*)x, (int)M, (int)K, xh, xe, st);
+        if (e != hipSuccess) return LMH_E_HIP;
+        a.x = xh;
+        a.xexp = xe;
+    }
+    a.packed = (const uint8_t*)packed;
+    a.bias = bias;
+    a.y = y;
+    a.ldy = ldy;
+    a.V = V;
+    a.K = K;
+    a.G = group;
+    a.M = (int)M;
+    a.bits = bits;
+    a.scale_bf16 = scale_dtype == BF16;
+    const bool use_gemv = path == 1 || (path == 0 && M <= lmh::kGemvMaxM);
+    return from_hip(use_gemv ? lmh::launch_gemv(a, st) : lmh::launch_mfma(a, st));
+}
+
+int lmhead_logits(const void* x, int x_dtype, int64_t M, const void* packed, int64_t V, int64_t K,
+                  int bits, int64_t group, int scale_dtype, const float* bias, float* y,
+                  int64_t ldy, void* workspace, size_t ws_bytes, void* stream) {
+    return logits_impl(x, x_dtype, M, packed, V, K, bits, group, scale_dtype, bias, y, ldy,
+                       workspace, ws_bytes, stream, 0);
+}
+
+int lmhead_logits_path(const void* x, int x_dtype, int64_t M, const void* packed, int64_t V,
+                       int64_t K, int bits, int64_t group, int scale_dtype, const float* bias,
+                       float* y, int64_t ldy, void* workspace, size_t ws_bytes, int path,
+                       void* stream) {
+    return logits_impl(x, x_dtype, M, packed, V, K, bits, group, scale_dtype, bias, y, ldy,
+                       workspace, ws_bytes, stream, path);
+}
+
+int lmhead_dense_logits(const void* x, int x_dtype, int64_t M, const void* w, int w_dtype,
+                        int64_t V, int64_t K, float* y, int64_t ldy, void* stream) {
+    if (x_dtype != F16 && x_dtype != BF16) return LMH_E_DTYPE;
+    if (w_dtype != x_dtype) return LMH_E_DTYPE;
+    if (M < 0 || M > 4 || V < 0 || V >= (int64_t(1) << 31)) return LMH_E_SHAPE;
+    if (K < 8 || K % 8 != 0 || K > 65536) return LMH_E_SHAPE;
+    if (M == 0 || V == 0) return LMH_OK;
+    if (ldy < V) return LMH_E_SHAPE;
+    if (!x || !w || !y) return LMH_E_NULL;
+    if (!aligned16(x) || !aligned16(w) || ((uintptr_t)y & 3u) != 0) return LMH_E_ALIGN;
+    return from_hip(lmh::launch_dense(x, x_dtype, (int)M, w, V, K, y, ldy, (hipStream_t)stream));
+}
+
+size_t lmhead_topk_workspace_bytes(int64_t M, int64_t V, int topk) {
+    if (M <= 0 || V <= 0 || topk < 1 || topk > 64) return 0;
+    return lmh::topk_ws_bytes(M, V, topk);
+}
+
+int lmhead_topk_rescore(const void* x, int x_dtype, int64_t M, const void* w_ref, int w_dtype,
+                        int64_t V, int64_t K, float* y, int64_t ldy, int topk, int32_t* idx_out,
+                        float* val_out, int32_t* top1_out, void* workspace, size_t ws_bytes,
+                        void* stream) {
+    if (x_dtype != F16 && x_dtype != BF16) return LMH_E_DTYPE;
+    if (w_dtype != F16 && w_dtype != BF16 && w_dtype != F32) return LMH_E_DTYPE;
+    if (M < 0 || M > 65535 || V < 0 || V >= (int64_t(1) << 31) || K < 1 || K > 65536)
+        return LMH_E_SHAPE;
+    if (topk < 1 || topk > 64) return LMH_E_SHAPE;
+    if (M == 0 || V == 0) return LMH_OK;
+    if (topk > V || ldy < V) return LMH_E_SHAPE;
+    if (!x || !w_ref || !y) return LMH_E_NULL;
+    if (((uintptr_t)x & 1u) != 0 || ((uintptr_t)w_ref & 3u) != 0 || ((uintptr_t)y & 3u) != 0)
+        return LMH_E_ALIGN;
+    const size_t need = lmh::topk_ws_bytes(M, V, topk);
+    if (!workspace || ws_bytes < need) return LMH_E_WORKSPACE;
+    if (!aligned16(workspace)) return LMH_E_ALIGN;
+    return from_hip(lmh::launch_topk_rescore(x, x_dtype, (int)M, w_ref, w_dtype, V, K, y, ldy, topk,
+                                             idx_out, val_out, top1_out, workspace,
+                                             (hipStream_t)stream));
+}
+
+}  // extern "C"

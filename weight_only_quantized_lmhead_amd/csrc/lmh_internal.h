@@ -1,0 +1,53 @@
+// Internal declarations shared by the HIP translation units of liblmhead.so.
+// Not part of the public ABI (that is include/lmhead.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lmh {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+enum Dtype { F32 = 0, F16 = 1, BF16 = 2 };
+
+// Columns covered by one 4-slot superchunk of the packed layout.
+constexpr int span_of(int bits) { return bits == 4 ? 128 : 64; }
+
+// Launch helpers (defined in the .hip files).  All return hipError_t of the
+// launch; arguments are already validated by the API layer.
+hipError_t launch_quantize(const void* w, int w_dtype, int64_t V, int64_t K, int bits, int64_t G,
+                           int scale_dtype, int nratios, int8_t* q, uint16_t* s, hipStream_t st);
+hipError_t launch_pack(const int8_t* q, const uint16_t* s, int64_t V, int64_t K, int bits,
+                       int64_t G, uint8_t* out, hipStream_t st);
+
+struct LogitsArgs {
+    const void* x;         // [M, K] fp16 (after conversion) row-major
+    const int* xexp;       // [M] power-of-two row exponents, or nullptr
+    const uint8_t* packed; // blob
+    const float* bias;     // [V] or nullptr
+    float* y;
+    int64_t ldy;
+    int64_t V, K, G;
+    int M, bits, scale_bf16;
+};
+
+hipError_t launch_x_to_f16(const uint16_t* x_bf16, int M, int K, _Float16* xh, int* xexp,
+                           hipStream_t st);
+hipError_t launch_gemv(const LogitsArgs& a, hipStream_t st);
+hipError_t launch_mfma(const LogitsArgs& a, hipStream_t st);
+hipError_t launch_dense(const void* x, int dtype, int M, const void* w, int64_t V, int64_t K,
+                        float* y, int64_t ldy, hipStream_t st);
+hipError_t launch_topk_rescore(const void* x, int x_dtype, int M, const void* w, int w_dtype,
+                               int64_t V, int64_t K, float* y, int64_t ldy, int topk,
+                               int32_t* idx, float* val, int32_t* top1, void* ws,
+                               hipStream_t st);
+size_t topk_ws_bytes(int64_t M, int64_t V, int topk);
+
+// Largest M served by the lane-per-row GEMV (beyond it the MFMA kernel runs).
+constexpr int kGemvMaxM = 4;
+
+}  // namespace lmh
