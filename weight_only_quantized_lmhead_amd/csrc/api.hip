@@ -110,7 +110,8 @@ static int logits_impl(const void* x, int x_dtype, int64_t M, const void* packed
         if (!workspace || ws_bytes < need) return LMH_E_WORKSPACE;
         if (!aligned16(workspace)) return LMH_E_ALIGN;
     }
-    if (path == 1 && M > lmh::kGemvMaxM) return LMH_E_UNSUPPORTED;
+    const bool gemv_ok = M <= lmh::kGemvMaxM && M * K <= lmh::kGemvMaxMK;
+    if (path == 1 && !gemv_ok) return LMH_E_UNSUPPORTED;
 
     hipStream_t st = (hipStream_t)stream;
     lmh::LogitsArgs a;
@@ -134,7 +135,7 @@ static int logits_impl(const void* x, int x_dtype, int64_t M, const void* packed
     a.M = (int)M;
     a.bits = bits;
     a.scale_bf16 = scale_dtype == BF16;
-    const bool use_gemv = path == 1 || (path == 0 && M <= lmh::kGemvMaxM);
+    const bool use_gemv = path == 1 || (path == 0 && gemv_ok);
     return from_hip(use_gemv ? lmh::launch_gemv(a, st) : lmh::launch_mfma(a, st));
 }
 

@@ -47,7 +47,9 @@ hipError_t launch_topk_rescore(const void* x, int x_dtype, int M, const void* w,
                                hipStream_t st);
 size_t topk_ws_bytes(int64_t M, int64_t V, int topk);
 
-// Largest M served by the lane-per-row GEMV (beyond it the MFMA kernel runs).
+// Largest M served by the lane-per-row GEMV (beyond it the MFMA kernel runs),
+// and the largest M*K it stages in LDS (64 KiB of fp16).
 constexpr int kGemvMaxM = 4;
+constexpr int64_t kGemvMaxMK = 32768;
 
 }  // namespace lmh

@@ -16,11 +16,10 @@
 // Kernels
 //   x_to_f16     bf16 x -> fp16 x * 2^-e per row (exact power-of-two scale,
 //                e chosen so max|x| lands in [2^14, 2^15)); y is scaled back.
-//   gemv         M <= 4.  A wave owns 64 vocabulary rows (one row block, one
-//                lane per row: no cross-lane reduction); the 4 waves of a
-//                workgroup split K and add their partials through LDS in a
-//                fixed order.  x is wave-uniform and is read through the
-//                scalar unit straight into v_dot2 operands.
+//   gemv         M <= 4 (and M*K <= 32768).  A wave owns 64 vocabulary rows
+//                (one row block, one lane per row, all of K: no cross-lane
+//                reduction).  x is staged in LDS once per workgroup and read
+//                as 16-byte broadcasts.
 //   mfma         larger M.  A wave owns one row block (4 MFMA column tiles of
 //                16 rows) and MT row tiles of 16 activations; each 16-byte
 //                slot load is one 16x16x32 B operand per 32-column word.
@@ -37,17 +36,30 @@ __device__ __forceinline__ float scale_to_f32(uint16_t b, int sbf16) {
     return sbf16 ? __uint_as_float((uint32_t)b << 16) : (float)__builtin_bit_cast(_Float16, b);
 }
 
+// (a & mask) | orv in one v_and_or_b32.  Written out because the compiler
+// otherwise splits it into v_and + v_or (gfx9 VOP3 cannot take two literals);
+// the mask comes from an SGPR and orv from a VGPR (one constant-bus read).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t orv) {
+    uint32_t d;
+    asm volatile("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(mask), "v"(orv));
+    return d;
+}
+
 // int4 word (8 codes; even columns in the low nibbles of each half-word) ->
-// four fp16 pairs (cols 0,1), (2,3), (4,5), (6,7), exact.
-__device__ __forceinline__ void unpack_i4(uint32_t w, h2& p0, h2& p1, h2& p2, h2& p3) {
+// four fp16 pairs (cols 0,1), (2,3), (4,5), (6,7), exact.  `magic` must hold
+// 0x64006400 (fp16 1024.0 in both halves).
+__device__ __forceinline__ void unpack_i4(uint32_t w, uint32_t magic, h2& p0, h2& p1, h2& p2,
+                                          h2& p3) {
     const uint32_t hi = w >> 8;
     const h2 b1032 = {(_Float16)-1032.0f, (_Float16)-1032.0f};
     const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
     const h2 b72 = {(_Float16)-72.0f, (_Float16)-72.0f};
-    p0 = __builtin_bit_cast(h2, (w & 0x000F000Fu) | 0x64006400u) + b1032;
-    p1 = __builtin_elementwise_fma(__builtin_bit_cast(h2, (w & 0x00F000F0u) | 0x64006400u), sixteenth, b72);
-    p2 = __builtin_bit_cast(h2, (hi & 0x000F000Fu) | 0x64006400u) + b1032;
-    p3 = __builtin_elementwise_fma(__builtin_bit_cast(h2, (hi & 0x00F000F0u) | 0x64006400u), sixteenth, b72);
+    p0 = __builtin_bit_cast(h2, and_or(w, 0x000F000Fu, magic)) + b1032;          // 1024+n -> n-8
+    p1 = __builtin_elementwise_fma(__builtin_bit_cast(h2, and_or(w, 0x00F000F0u, magic)), sixteenth,
+                                   b72);                                          // (1024+16n)/16-72
+    p2 = __builtin_bit_cast(h2, and_or(hi, 0x000F000Fu, magic)) + b1032;
+    p3 = __builtin_elementwise_fma(__builtin_bit_cast(h2, and_or(hi, 0x00F000F0u, magic)), sixteenth,
+                                   b72);
 }
 
 // int8 word (4 codes, byte i = column i, biased by 128) -> two fp16 pairs.
@@ -87,134 +99,128 @@ __global__ __launch_bounds__(256) void x_to_f16_kernel(const uint16_t* __restric
 }
 
 // ---------------------------------------------------------------------------
-// GEMV: 4 waves per 64-row block, K split in 4 contiguous superchunk ranges.
-// GPS = groups per superchunk (1 when a group spans >= 1 superchunk).
-template <int BITS, int MM, int GPS>
+// GEMV: one wave per 64-row block, one lane per row, all of K per wave (no
+// cross-lane or cross-wave reduction).  Superchunks stream through a ring of
+// D register buffers; loads past the end are clamped to the last superchunk
+// (and their contribution dropped) so every load is unconditional and the
+// compiler can keep exact vmcnt accounting (no drain at the loop head).
+// GPS = groups per superchunk (G <= span); GPS == 1 covers G >= span, the
+// scale of superchunk c then being that of group c / SPG.
+template <int BITS, int MM, int GPS, int D>
 __global__ __launch_bounds__(256) void gemv_kernel(const uint4* __restrict__ wq,
                                                    const uint16_t* __restrict__ sc,
-                                                   const h2* __restrict__ x,
+                                                   const h2* __restrict__ xg,
                                                    const int* __restrict__ xexp,
                                                    const float* __restrict__ bias,
                                                    float* __restrict__ y, int64_t ldy, int V, int K,
-                                                   int NC, int NG, int SPG, int sbf16) {
+                                                   int NB, int NC, int NG, int SPG, int sbf16) {
     constexpr int SPAN = BITS == 4 ? 128 : 64;
     constexpr int CPS = SPAN / 32;    // 32-column chunks per superchunk
-    constexpr int CPG = CPS / GPS;    // chunks per group when GPS > 1
-    __shared__ float red[4][MM][64];
+    constexpr int CPG = CPS / GPS;    // chunks per group
+    constexpr int NA = MM == 1 ? 4 : (MM == 2 ? 2 : 1);  // independent partial sums per group
+    // x (all M rows, all of K) is staged once per workgroup in LDS; every lane
+    // then reads the same 16 bytes at a time (an LDS broadcast).
+    extern __shared__ uint4 xs_raw[];
+    const h2* x = (const h2*)xs_raw;
+    {
+        const uint4* src = (const uint4*)xg;
+        const int n16 = MM * K / 8;
+        for (int i = threadIdx.x; i < n16; i += 256) xs_raw[i] = src[i];
+    }
+    __syncthreads();
     const int lane = threadIdx.x & 63;
-    const int wv = threadIdx.x >> 6;
-    const int blk = blockIdx.x;
-    const int c0 = (NC * wv) / 4, c1 = (NC * (wv + 1)) / 4;
+    const int blk = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (blk >= NB) return;  // wave-uniform; no barriers below
     const uint4* wp = wq + (int64_t)blk * NC * 256 + lane;
     const uint16_t* sp = sc + (int64_t)blk * NG * 64 + lane;
     const int Kh = K >> 1;
+    const uint32_t magic = 0x64006400u;
 
-    float acc[MM];
-    float part[MM][GPS];
+    uint4 buf[D][4];
+    uint16_t sb[D][GPS];
+    // scale bookkeeping of the prefetch stream when a group spans superchunks
+    int pf_g = 0, pf_left = SPG;
+    auto load = [&](int p, int c) {
+        const int cc = c < NC ? c : NC - 1;
 #pragma unroll
-    for (int m = 0; m < MM; ++m) {
-        acc[m] = 0.0f;
-#pragma unroll
-        for (int g = 0; g < GPS; ++g) part[m][g] = 0.0f;
-    }
-    // group bookkeeping for GPS == 1
-    int g_cur = (GPS == 1) ? c0 / SPG : 0;
-    int left = (GPS == 1) ? SPG - (c0 - g_cur * SPG) : 0;
-    float sv = 0.0f;
-    if (GPS == 1 && c0 < c1) sv = scale_to_f32(sp[(int64_t)g_cur * 64], sbf16);
-
-    uint4 cur[4], nxt[4];
-    if (c0 < c1) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) cur[t] = wp[((int64_t)c0 * 4 + t) * 64];
-    }
-    for (int c = c0; c < c1; ++c) {
-        if (c + 1 < c1) {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) nxt[t] = wp[((int64_t)(c + 1) * 4 + t) * 64];
-        }
-        float sg[GPS];
+        for (int t = 0; t < 4; ++t) buf[p][t] = wp[((int64_t)cc * 4 + t) * 64];
         if constexpr (GPS > 1) {
 #pragma unroll
-            for (int g = 0; g < GPS; ++g) sg[g] = scale_to_f32(sp[((int64_t)c * GPS + g) * 64], sbf16);
-        }
-        const int xc = c * (SPAN / 2);  // half2 index of the superchunk's first column
-#pragma unroll
-        for (int j = 0; j < CPS; ++j) {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                if constexpr (BITS == 4) {
-                    h2 p0, p1, p2, p3;
-                    unpack_i4(word_of(cur[t], j), p0, p1, p2, p3);
-                    const int xi = xc + 16 * j + 4 * t;  // cols 128c + 32j + 8t
-#pragma unroll
-                    for (int m = 0; m < MM; ++m) {
-                        const h2* xm = x + (int64_t)m * Kh + xi;
-                        float a = part[m][j / CPG];
-                        a = __builtin_amdgcn_fdot2(p0, xm[0], a, false);
-                        a = __builtin_amdgcn_fdot2(p1, xm[1], a, false);
-                        a = __builtin_amdgcn_fdot2(p2, xm[2], a, false);
-                        a = __builtin_amdgcn_fdot2(p3, xm[3], a, false);
-                        part[m][j / CPG] = a;
-                    }
-                } else {
-                    h2 p0, p1, p2, p3;
-                    unpack_i8(word_of(cur[t], 2 * j), p0, p1);
-                    unpack_i8(word_of(cur[t], 2 * j + 1), p2, p3);
-                    const int xi = xc + 16 * j + 4 * t;  // cols 64c + 32j + 8t
-#pragma unroll
-                    for (int m = 0; m < MM; ++m) {
-                        const h2* xm = x + (int64_t)m * Kh + xi;
-                        float a = part[m][j / CPG];
-                        a = __builtin_amdgcn_fdot2(p0, xm[0], a, false);
-                        a = __builtin_amdgcn_fdot2(p1, xm[1], a, false);
-                        a = __builtin_amdgcn_fdot2(p2, xm[2], a, false);
-                        a = __builtin_amdgcn_fdot2(p3, xm[3], a, false);
-                        part[m][j / CPG] = a;
-                    }
-                }
+            for (int g = 0; g < GPS; ++g) sb[p][g] = sp[((int64_t)cc * GPS + g) * 64];
+        } else {
+            sb[p][0] = sp[(int64_t)pf_g * 64];
+            if (--pf_left == 0 && pf_g + 1 < NG) {
+                ++pf_g;
+                pf_left = SPG;
             }
         }
-        if constexpr (GPS > 1) {
+    };
+
+    float acc[MM];
+#pragma unroll
+    for (int m = 0; m < MM; ++m) acc[m] = 0.0f;
+#pragma unroll
+    for (int p = 0; p < D; ++p) load(p, p);
+    for (int cb = 0; cb < NC; cb += D) {
+#pragma unroll
+        for (int p = 0; p < D; ++p) {
+            const int c = cb + p;
+            const int cl = c < NC ? c : NC - 1;
+            float part[MM][GPS][NA];
 #pragma unroll
             for (int m = 0; m < MM; ++m)
 #pragma unroll
-                for (int g = 0; g < GPS; ++g) {
-                    acc[m] = fmaf(sg[g], part[m][g], acc[m]);
-                    part[m][g] = 0.0f;
+                for (int g = 0; g < GPS; ++g)
+#pragma unroll
+                    for (int a = 0; a < NA; ++a) part[m][g][a] = 0.0f;
+            const int xc = cl * (SPAN / 2);  // half2 index of the superchunk's first column
+#pragma unroll
+            for (int j = 0; j < CPS; ++j) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    h2 p0, p1, p2, p3;
+                    if constexpr (BITS == 4) {
+                        unpack_i4(word_of(buf[p][t], j), magic, p0, p1, p2, p3);
+                    } else {
+                        unpack_i8(word_of(buf[p][t], 2 * j), p0, p1);
+                        unpack_i8(word_of(buf[p][t], 2 * j + 1), p2, p3);
+                    }
+                    const int xi = xc + 16 * j + 4 * t;  // columns span*c + 32j + 8t
+#pragma unroll
+                    for (int m = 0; m < MM; ++m) {
+                        const uint4 xv = *(const uint4*)(x + m * Kh + xi);
+                        float a = part[m][j / CPG][t % NA];
+                        a = __builtin_amdgcn_fdot2(p0, __builtin_bit_cast(h2, xv.x), a, false);
+                        a = __builtin_amdgcn_fdot2(p1, __builtin_bit_cast(h2, xv.y), a, false);
+                        a = __builtin_amdgcn_fdot2(p2, __builtin_bit_cast(h2, xv.z), a, false);
+                        a = __builtin_amdgcn_fdot2(p3, __builtin_bit_cast(h2, xv.w), a, false);
+                        part[m][j / CPG][t % NA] = a;
+                    }
                 }
-        } else {
-            if (--left == 0 || c + 1 == c1) {
+            }
+            const bool real = c < NC;
+#pragma unroll
+            for (int g = 0; g < GPS; ++g) {
+                const float sv = real ? scale_to_f32(sb[p][g], sbf16) : 0.0f;
 #pragma unroll
                 for (int m = 0; m < MM; ++m) {
-                    acc[m] = fmaf(sv, part[m][0], acc[m]);
-                    part[m][0] = 0.0f;
-                }
-                if (left == 0 && c + 1 < c1) {
-                    ++g_cur;
-                    left = SPG;
-                    sv = scale_to_f32(sp[(int64_t)g_cur * 64], sbf16);
+                    float q = part[m][g][0];
+#pragma unroll
+                    for (int a = 1; a < NA; ++a) q += part[m][g][a];
+                    acc[m] = fmaf(sv, q, acc[m]);
                 }
             }
-        }
-        if (c + 1 < c1) {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) cur[t] = nxt[t];
+            load(p, c + D);
         }
     }
+    const int v = blk * 64 + lane;
+    if (v < V) {
+        const float b = bias ? bias[v] : 0.0f;
 #pragma unroll
-    for (int m = 0; m < MM; ++m) red[wv][m][lane] = acc[m];
-    __syncthreads();
-    if (wv == 0) {
-        const int v = blk * 64 + lane;
-        if (v < V) {
-            const float b = bias ? bias[v] : 0.0f;
-#pragma unroll
-            for (int m = 0; m < MM; ++m) {
-                float r = ((red[0][m][lane] + red[1][m][lane]) + red[2][m][lane]) + red[3][m][lane];
-                if (xexp) r = ldexpf(r, xexp[m]);
-                y[(int64_t)m * ldy + v] = r + b;
-            }
+        for (int m = 0; m < MM; ++m) {
+            float r = acc[m];
+            if (xexp) r = ldexpf(r, xexp[m]);
+            y[(int64_t)m * ldy + v] = r + b;
         }
     }
 }
@@ -296,7 +302,7 @@ __global__ __launch_bounds__(256) void mfma_kernel(const uint4* __restrict__ wq,
             for (int nt = 0; nt < NT; ++nt) {
                 h2 p0, p1, p2, p3;
                 if constexpr (BITS == 4) {
-                    unpack_i4(word_of(wv[nt], j), p0, p1, p2, p3);
+                    unpack_i4(word_of(wv[nt], j), 0x64006400u, p0, p1, p2, p3);
                 } else {
                     unpack_i8(word_of(wv[nt], 2 * j), p0, p1);
                     unpack_i8(word_of(wv[nt], 2 * j + 1), p2, p3);
@@ -430,16 +436,18 @@ inline int gps_of(int bits, int64_t G) {
 
 template <int BITS, int MM>
 hipError_t gemv_dispatch_gps(const LogitsArgs& a, int gps, hipStream_t st) {
+    constexpr int D = 1;
     const int NB = (int)((a.V + 63) / 64);
     const int NC = (int)(a.K / span_of(BITS));
     const int NG = (int)(a.K / a.G);
     const int SPG = gps == 1 ? (int)(a.G / span_of(BITS)) : 1;
     const uint4* wq = (const uint4*)a.packed;
     const uint16_t* sc = (const uint16_t*)(a.packed + (int64_t)NB * 64 * a.K * BITS / 8);
-#define LMH_GEMV(G_)                                                                           \
-    hipLaunchKernelGGL((gemv_kernel<BITS, MM, G_>), dim3(NB), dim3(256), 0, st, wq, sc,        \
-                       (const h2*)a.x, a.xexp, a.bias, a.y, a.ldy, (int)a.V, (int)a.K, NC, NG, \
-                       SPG, a.scale_bf16)
+    const size_t lds = (size_t)MM * a.K * 2;
+#define LMH_GEMV(G_)                                                                              \
+    hipLaunchKernelGGL((gemv_kernel<BITS, MM, G_, D>), dim3((NB + 3) / 4), dim3(256), lds, st,   \
+                       wq, sc, (const h2*)a.x, a.xexp, a.bias, a.y, a.ldy, (int)a.V, (int)a.K,    \
+                       NB, NC, NG, SPG, a.scale_bf16)
     if (gps == 1) LMH_GEMV(1);
     else if constexpr (BITS == 8) LMH_GEMV(2);
     else if (gps == 2) LMH_GEMV(2);
