@@ -50,6 +50,7 @@ def main() -> int:
     ap.add_argument("--workload", default=None, help="synthetic workload name (default: the headline)")
     ap.add_argument("--ms", default=None, help="comma-separated M list (default: the workload's)")
     ap.add_argument("--topk", type=int, default=8)
+    ap.add_argument("--path", type=int, default=0, help="0 automatic, 1 force the GEMV, 2 force the MFMA kernel")
     ap.add_argument("--hot", action="store_true", help="reuse one copy of the head (cache-hot; labelled)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -120,7 +121,8 @@ def main() -> int:
     m_hd = Ms[0]  # the headline call: the decode case
 
     def call(M, i):
-        lmh.logits(xs[M], blobs[i % R], w.V, w.K, w.bits, w.group, sdt, out=outs[M], workspace=wss[M])
+        lmh.logits(xs[M], blobs[i % R], w.V, w.K, w.bits, w.group, sdt, out=outs[M], workspace=wss[M],
+                   path=args.path)
 
     def rescore():
         lmh.topk_rescore(xs[m_rs], Wref, outs[m_rs], args.topk, workspace=tws)
@@ -164,7 +166,8 @@ def main() -> int:
         gbs = B / (t_us * 1e-6) / 1e9
         tfl = F / (t_us * 1e-6) / 1e12
         per_call[f"M={M}"] = {
-            "us": round(t_us, 3), "kernel": "gemv" if M <= 4 and M * w.K <= 32768 else "mfma",
+            "us": round(t_us, 3),
+            "kernel": {1: "gemv", 2: "mfma"}.get(args.path, "gemv" if M == 1 and w.K <= 32768 else "mfma"),
             "algorithmic_bytes": B, "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
             "TFLOP/s": round(tfl, 2), "frac_mfma_f16_peak": round(tfl / MFMA_F16_PEAK_TFLOPS, 4),
         }

@@ -156,9 +156,10 @@ size_t lmhead_logits_workspace_bytes(int64_t M, int64_t K, int x_dtype);
  *           written.  Needs only 4-byte alignment.
  *   workspace / ws_bytes: at least lmhead_logits_workspace_bytes(M, K, x_dtype)
  *           (may be NULL/0 for fp16 x).
- *   Small M runs a split-free GEMV (one lane per vocabulary row); larger M
- *   runs a 16x16x32 fp16 MFMA kernel.  The result does not depend on the
- *   stream or on other calls.
+ *   M = 1 runs a GEMV with one lane per vocabulary row (all of K per wave);
+ *   M >= 2 runs a 16x16x32 fp16 MFMA kernel (its code unpacking is shared by
+ *   all activation rows).  The result does not depend on the stream or on
+ *   other calls.
  */
 int lmhead_logits(const void* x, int x_dtype, int64_t M, const void* packed, int64_t V, int64_t K,
                   int bits, int64_t group, int scale_dtype, const float* bias, float* y,

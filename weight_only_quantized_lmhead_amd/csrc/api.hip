@@ -135,7 +135,7 @@ static int logits_impl(const void* x, int x_dtype, int64_t M, const void* packed
     a.M = (int)M;
     a.bits = bits;
     a.scale_bf16 = scale_dtype == BF16;
-    const bool use_gemv = path == 1 || (path == 0 && gemv_ok);
+    const bool use_gemv = path == 1 || (path == 0 && gemv_ok && M <= lmh::kGemvAutoMaxM);
     return from_hip(use_gemv ? lmh::launch_gemv(a, st) : lmh::launch_mfma(a, st));
 }
 

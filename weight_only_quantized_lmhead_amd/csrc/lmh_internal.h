@@ -47,9 +47,11 @@ hipError_t launch_topk_rescore(const void* x, int x_dtype, int M, const void* w,
                                hipStream_t st);
 size_t topk_ws_bytes(int64_t M, int64_t V, int topk);
 
-// Largest M served by the lane-per-row GEMV (beyond it the MFMA kernel runs),
-// and the largest M*K it stages in LDS (64 KiB of fp16).
+// Largest M the lane-per-row GEMV accepts when forced (it runs by default only
+// for M = 1: from M = 2 on the MFMA kernel is faster, its unpacking being
+// shared by all rows), and the largest M*K it stages in LDS (64 KiB of fp16).
 constexpr int kGemvMaxM = 4;
+constexpr int kGemvAutoMaxM = 1;
 constexpr int64_t kGemvMaxMK = 32768;
 
 }  // namespace lmh

@@ -226,123 +226,156 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint4* __restrict__ wq,
 }
 
 // ---------------------------------------------------------------------------
-// MFMA kernel.  Grid: x = row blocks (one per wave, 4 per workgroup), y = row
-// tiles of MT*16 activations.  Lane (r = lane & 15, t = lane >> 4) reads slot
-// t of vocabulary row 16*nt + r; word j of that slot is the 8-value B operand
-// (k = 8t .. 8t+7 of the 32-column chunk) of one v_mfma_f32_16x16x32_f16, and
-// the A operand is x[m0 + 16*mt + r][chunk + 8t .. +8].  The 16x16 result
-// lands as D[4t + e][r]: activation row 4t + e, vocabulary row r.
+// MFMA kernel.  A workgroup = 4 waves = 4 row blocks (256 vocabulary rows) x
+// MT*16 activation rows (grid.y tiles M).  For each superchunk the workgroup
+// stages the activation tile x[m0 .. m0+16MT, span columns] in LDS (double
+// buffered; rows padded to span+8 halves so the 16-row A-operand reads hit 16
+// distinct bank groups), while each wave streams its own row block's 16-byte
+// slots: the current superchunk in registers, the next one in flight.
+// Lane (r = lane & 15, t = lane >> 4) reads slot t of vocabulary row 16*nt + r:
+// word j is the 8-value B operand (k = 8t .. 8t+7 of 32-column chunk j) of one
+// v_mfma_f32_16x16x32_f16, and the A operand is x[16*mt + r][chunk + 8t .. +8]
+// from LDS.  The 16x16 result lands as D[4t + e][r]: activation row 4t + e,
+// vocabulary row r.  Per scale group: the B operands of the 4 column tiles are
+// unpacked once, then per row tile a CPG-long MFMA chain is started from zero
+// and folded into the fp32 accumulator with the group scale of the lane's row.
 template <int BITS, int MT, int GPS>
-__global__ __launch_bounds__(256) void mfma_kernel(const uint4* __restrict__ wq,
-                                                   const uint16_t* __restrict__ sc,
-                                                   const _Float16* __restrict__ x,
-                                                   const int* __restrict__ xexp,
-                                                   const float* __restrict__ bias,
-                                                   float* __restrict__ y, int64_t ldy, int V, int K,
-                                                   int M, int NB, int NC, int NG, int SPG,
-                                                   int sbf16) {
+__global__ __launch_bounds__(256, MT >= 4 ? 1 : 2) void mfma_kernel(
+    const uint4* __restrict__ wq, const uint16_t* __restrict__ sc, const _Float16* __restrict__ x,
+    const int* __restrict__ xexp, const float* __restrict__ bias, float* __restrict__ y,
+    int64_t ldy, int V, int K, int M, int NB, int NC, int NG, int SPG, int sbf16) {
     constexpr int NT = 4;
     constexpr int SPAN = BITS == 4 ? 128 : 64;
     constexpr int CPS = SPAN / 32;
     constexpr int CPG = CPS / GPS;
+    constexpr int ROWH = SPAN + 8;        // padded LDS row, in halves
+    constexpr int ROWS = MT * 16;
+    constexpr int STAGE = ROWS * ROWH;    // halves per LDS stage
+    constexpr int XV = ROWS * SPAN / 8;   // 16-byte pieces of one x tile
+    constexpr int XPT = (XV + 255) / 256; // pieces per thread
+    constexpr int P8 = SPAN / 8;          // 16-byte pieces per tile row
+    constexpr int RPU = 256 / P8;         // rows between one thread's pieces
+    __shared__ __attribute__((aligned(16))) _Float16 xs[2 * STAGE];
+
     const int lane = threadIdx.x & 63;
-    const int blk = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (blk >= NB) return;  // wave-uniform; this kernel has no barriers
+    const int wv = threadIdx.x >> 6;
+    const int blk = blockIdx.x * 4 + wv;
+    const bool live = blk < NB;
+    const int blkc = live ? blk : NB - 1;
     const int r = lane & 15, t = lane >> 4;
-    const int m0 = blockIdx.y * MT * 16;
-    const uint4* wp = wq + (int64_t)blk * NC * 256 + t * 64 + r;
-    const uint16_t* sp = sc + (int64_t)blk * NG * 64 + r;
+    const int m0 = blockIdx.y * ROWS;
+    const uint4* wp = wq + (int64_t)blkc * NC * 256 + t * 64 + r;
+    const uint16_t* sp = sc + (int64_t)blkc * NG * 64 + r;
+    const uint32_t magic = 0x64006400u;
 
-    // activation row pointers (rows past M read row 0 and are zeroed)
-    const _Float16* xr[MT];
-    bool xok[MT];
+    // x tile staging: thread i copies the 16-byte pieces (row i / P8 + u*RPU,
+    // 8-column group i % P8), u < XPT; rows past M are staged as zeros
+    const int xrow0 = threadIdx.x / P8, xcol8 = threadIdx.x % P8;
+    const _Float16* xsrc = x + (int64_t)(m0 + xrow0) * K + 8 * xcol8;
+    _Float16* xdst = xs + xrow0 * ROWH + 8 * xcol8;
+    uint32_t xvalid = 0;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        const int m = m0 + 16 * mt + r;
-        xok[mt] = m < M;
-        xr[mt] = x + (int64_t)(xok[mt] ? m : 0) * K + 8 * t;
-    }
+    for (int u = 0; u < XPT; ++u)
+        if (xrow0 + u * RPU < ROWS && m0 + xrow0 + u * RPU < M) xvalid |= 1u << u;
+    uint4 xr[XPT];
+    auto xload = [&](int c) {
+#pragma unroll
+        for (int u = 0; u < XPT; ++u)
+            xr[u] = (xvalid >> u) & 1u
+                        ? *(const uint4*)(xsrc + (int64_t)u * RPU * K + (int64_t)c * SPAN)
+                        : make_uint4(0, 0, 0, 0);
+    };
+    auto xstore = [&](int buf) {
+#pragma unroll
+        for (int u = 0; u < XPT; ++u)
+            if (xrow0 + u * RPU < ROWS) *(uint4*)(xdst + buf * STAGE + u * RPU * ROWH) = xr[u];
+    };
 
-    f4 acc[MT][NT], part[MT][NT];
+    // weights: loads past the end are clamped so every load is unconditional
+    uint4 wcur[NT], wnxt[NT];
+    uint16_t scur[GPS][NT], snxt[GPS][NT];
+    int pf_g = 0, pf_left = SPG;
+    auto wload = [&](uint4 (&wd)[NT], uint16_t (&sd)[GPS][NT], int c) {
+        const int cc = c < NC ? c : NC - 1;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            acc[mt][nt] = (f4){0.f, 0.f, 0.f, 0.f};
-            part[mt][nt] = (f4){0.f, 0.f, 0.f, 0.f};
-        }
-    int g_cur = 0, left = SPG;
-    float sv[NT];
-    if (GPS == 1) {
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) sv[nt] = scale_to_f32(sp[16 * nt], sbf16);
-    }
-
-    for (int c = 0; c < NC; ++c) {
-        uint4 wv[NT];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) wv[nt] = wp[(int64_t)c * 256 + 16 * nt];
-        float sg[GPS][NT];
+        for (int nt = 0; nt < NT; ++nt) wd[nt] = wp[(int64_t)cc * 256 + 16 * nt];
         if constexpr (GPS > 1) {
 #pragma unroll
             for (int g = 0; g < GPS; ++g)
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt)
-                    sg[g][nt] = scale_to_f32(sp[((int64_t)c * GPS + g) * 64 + 16 * nt], sbf16);
-        }
+                    sd[g][nt] = sp[((int64_t)cc * GPS + g) * 64 + 16 * nt];
+        } else {
 #pragma unroll
-        for (int j = 0; j < CPS; ++j) {
-            h8 a[MT];
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                h8 v = *(const h8*)(xr[mt] + (int64_t)c * SPAN + 32 * j);
-                a[mt] = xok[mt] ? v : (h8){0, 0, 0, 0, 0, 0, 0, 0};
+            for (int nt = 0; nt < NT; ++nt) sd[0][nt] = sp[(int64_t)pf_g * 64 + 16 * nt];
+            if (--pf_left == 0 && pf_g + 1 < NG) {
+                ++pf_g;
+                pf_left = SPG;
             }
+        }
+    };
+
+    f4 acc[MT][NT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = (f4){0.f, 0.f, 0.f, 0.f};
+
+    xload(0);
+    wload(wcur, scur, 0);
+    xstore(0);
+    __syncthreads();
+    for (int c = 0; c < NC; ++c) {
+        wload(wnxt, snxt, c + 1);
+        xload(c + 1 < NC ? c + 1 : NC - 1);
+        const _Float16* xb = xs + (c & 1) * STAGE;
+#pragma unroll
+        for (int g = 0; g < GPS; ++g) {
+            h8 bop[NT][CPG];
+            float sv[NT];
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
-                h2 p0, p1, p2, p3;
-                if constexpr (BITS == 4) {
-                    unpack_i4(word_of(wv[nt], j), 0x64006400u, p0, p1, p2, p3);
-                } else {
-                    unpack_i8(word_of(wv[nt], 2 * j), p0, p1);
-                    unpack_i8(word_of(wv[nt], 2 * j + 1), p2, p3);
+#pragma unroll
+                for (int jj = 0; jj < CPG; ++jj) {
+                    const int j = g * CPG + jj;
+                    h2 p0, p1, p2, p3;
+                    if constexpr (BITS == 4) {
+                        unpack_i4(word_of(wcur[nt], j), magic, p0, p1, p2, p3);
+                    } else {
+                        unpack_i8(word_of(wcur[nt], 2 * j), p0, p1);
+                        unpack_i8(word_of(wcur[nt], 2 * j + 1), p2, p3);
+                    }
+                    bop[nt][jj] = (h8){p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
                 }
-                const h8 b = {p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                    part[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt], b, part[mt][nt], 0, 0, 0);
+                sv[nt] = scale_to_f32(scur[g][nt], sbf16);
             }
-            if constexpr (GPS > 1) {
-                if ((j + 1) % CPG == 0) {
-                    const int g = j / CPG;
 #pragma unroll
-                    for (int mt = 0; mt < MT; ++mt)
+            for (int mt = 0; mt < MT; ++mt) {
+                h8 a[CPG];
 #pragma unroll
-                        for (int nt = 0; nt < NT; ++nt) {
-                            acc[mt][nt] += sg[g][nt] * part[mt][nt];
-                            part[mt][nt] = (f4){0.f, 0.f, 0.f, 0.f};
-                        }
+                for (int jj = 0; jj < CPG; ++jj)
+                    a[jj] = *(const h8*)(xb + (16 * mt + r) * ROWH + 32 * (g * CPG + jj) + 8 * t);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    f4 pt = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[0], bop[nt][0],
+                                                                    (f4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+                    for (int jj = 1; jj < CPG; ++jj)
+                        pt = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[jj], bop[nt][jj], pt, 0, 0, 0);
+                    acc[mt][nt] += sv[nt] * pt;
                 }
             }
         }
-        if constexpr (GPS == 1) {
-            if (--left == 0) {
+        xstore((c + 1) & 1);
+        __syncthreads();
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
+        for (int nt = 0; nt < NT; ++nt) {
+            wcur[nt] = wnxt[nt];
 #pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) {
-                        acc[mt][nt] += sv[nt] * part[mt][nt];
-                        part[mt][nt] = (f4){0.f, 0.f, 0.f, 0.f};
-                    }
-                left = SPG;
-                if (++g_cur < NG) {
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt)
-                        sv[nt] = scale_to_f32(sp[(int64_t)g_cur * 64 + 16 * nt], sbf16);
-                }
-            }
+            for (int g = 0; g < GPS; ++g) scur[g][nt] = snxt[g][nt];
         }
     }
+    if (!live) return;
     // write D[4t + e][r] of each tile
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -477,8 +510,8 @@ hipError_t mfma_dispatch_mt(const LogitsArgs& a, hipStream_t st) {
     const uint4* wq = (const uint4*)a.packed;
     const uint16_t* sc = (const uint16_t*)(a.packed + (int64_t)NB * 64 * a.K * BITS / 8);
     const dim3 grid((NB + 3) / 4, (a.M + MT * 16 - 1) / (MT * 16));
-#define LMH_MFMA(G_)                                                                              \
-    hipLaunchKernelGGL((mfma_kernel<BITS, MT, G_>), grid, dim3(256), 0, st, wq, sc,              \
+#define LMH_MFMA(G_)                                                                               \
+    hipLaunchKernelGGL((mfma_kernel<BITS, MT, G_>), grid, dim3(256), 0, st, wq, sc,               \
                        (const _Float16*)a.x, a.xexp, a.bias, a.y, a.ldy, (int)a.V, (int)a.K, a.M, \
                        NB, NC, NG, SPG, a.scale_bf16)
     if (gps == 1) LMH_MFMA(1);
@@ -491,9 +524,11 @@ hipError_t mfma_dispatch_mt(const LogitsArgs& a, hipStream_t st) {
 
 template <int BITS>
 hipError_t mfma_dispatch(const LogitsArgs& a, hipStream_t st) {
+    // one 16-row activation tile for M <= 16; two (32 rows) otherwise: the
+    // 64-row tile needs one wave per SIMD and loses more to latency than it
+    // saves in unpacking (measured on the 151936 x 1024 head, M = 64..256)
     if (a.M <= 16) return mfma_dispatch_mt<BITS, 1>(a, st);
-    if (a.M <= 32) return mfma_dispatch_mt<BITS, 2>(a, st);
-    return mfma_dispatch_mt<BITS, 4>(a, st);
+    return mfma_dispatch_mt<BITS, 2>(a, st);
 }
 
 }  // namespace
