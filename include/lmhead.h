@@ -204,11 +204,15 @@ size_t lmhead_topk_workspace_bytes(int64_t M, int64_t V, int topk);
  *     idx_out[m, t] = I[t]  (int32), val_out[m, t] = the new y[m, I[t]];
  *     top1_out[m] = the first (lowest-index) maximum of the updated row.
  *   x [M, K] LMH_F16 or LMH_BF16; w_ref [V, K] LMH_F16, LMH_BF16 or LMH_F32,
- *   row-major (only the topk selected rows are read).  1 <= topk <= 64 and
- *   topk <= V.  Any of idx_out / val_out / top1_out may be NULL.  Alignment:
- *   x 2 bytes, w_ref and y 4 bytes, workspace 16 bytes.
- *   workspace: at least lmhead_topk_workspace_bytes(M, V, topk) bytes.
- *   Deterministic (no atomics).
+ *   row-major (only the topk selected rows are read).  1 <= topk <= 64,
+ *   topk <= V and V <= 2097152 (LMH_E_UNSUPPORTED beyond).  Any of idx_out /
+ *   val_out / top1_out may be NULL.  Alignment: x 2 bytes, w_ref and y
+ *   4 bytes, workspace 16 bytes.
+ *   workspace: at least lmhead_topk_workspace_bytes(M, V, topk) bytes; its
+ *   contents on entry do not matter.
+ *   Deterministic: the selection is unique under the order (-0 equals +0)
+ *   and every sum has a fixed order.  NaN logits rank below every number;
+ *   the result is then still memory-safe but otherwise unspecified.
  */
 int lmhead_topk_rescore(const void* x, int x_dtype, int64_t M, const void* w_ref, int w_dtype,
                         int64_t V, int64_t K, float* y, int64_t ldy, int topk, int32_t* idx_out,

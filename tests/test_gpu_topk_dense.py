@@ -22,8 +22,13 @@ def _gamma(n):
 
 
 @pytest.mark.parametrize("wdt,xdt", [("f16", "f16"), ("bf16", "bf16"), ("f32", "f16")])
+# V spans one to a few hundred 2048-entry blocks (fewer lists than T and more),
+# topk = 64 takes the first pass's block-wide threshold, K = 100 the
+# unvectorised rescoring
 @pytest.mark.parametrize("V,K,topk,M", [(5000, 256, 8, 1), (9000, 512, 16, 3), (300, 96, 1, 2),
-                                         (4097, 128, 64, 2), (70, 64, 64, 1)])
+                                         (4097, 128, 64, 2), (70, 64, 64, 1), (3001, 100, 8, 2),
+                                         (100000, 64, 16, 1), (200000, 32, 32, 2),
+                                         (400000, 32, 8, 1), (600000, 32, 8, 1)])
 def test_topk_rescore_vs_oracle(wdt, xdt, V, K, topk, M):
     need_gpu()
     wf = synth.random_weight((V, K), 0.05, V + K)

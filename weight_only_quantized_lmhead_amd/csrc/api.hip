@@ -183,6 +183,7 @@ int lmhead_topk_rescore(const void* x, int x_dtype, int64_t M, const void* w_ref
     if (topk < 1 || topk > 64) return LMH_E_SHAPE;
     if (M == 0 || V == 0) return LMH_OK;
     if (topk > V || ldy < V) return LMH_E_SHAPE;
+    if (V > lmh::topk_max_v()) return LMH_E_UNSUPPORTED;
     if (!x || !w_ref || !y) return LMH_E_NULL;
     if (((uintptr_t)x & 1u) != 0 || ((uintptr_t)w_ref & 3u) != 0 || ((uintptr_t)y & 3u) != 0)
         return LMH_E_ALIGN;

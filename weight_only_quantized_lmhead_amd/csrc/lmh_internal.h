@@ -46,6 +46,7 @@ hipError_t launch_topk_rescore(const void* x, int x_dtype, int M, const void* w,
                                int32_t* idx, float* val, int32_t* top1, void* ws,
                                hipStream_t st);
 size_t topk_ws_bytes(int64_t M, int64_t V, int topk);
+int64_t topk_max_v();  // largest row length lmhead_topk_rescore supports
 
 // Largest M the lane-per-row GEMV accepts when forced (it runs by default only
 // for M = 1: from M = 2 on the MFMA kernel is faster, its unpacking being
