@@ -4,7 +4,9 @@
 
 Compiles every csrc/*.hip with hipcc for gfx950 in parallel and links the
 shared library next to this file.  Packed fp32 instructions are disabled
-(-packed-fp32-ops) so the compiler never emits v_pk_{add,mul,fma}_f32.
+(-packed-fp32-ops) so the compiler never emits v_pk_{add,mul,fma}_f32, and
+MFMA results are kept in ordinary VGPRs (-amdgpu-mfma-vgpr-form) so the
+fp32 scale epilogue reads them without accumulator-register copies.
 """
 from __future__ import annotations
 
@@ -27,6 +29,10 @@ HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 FLAGS = [
     "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
+    # the direct global->LDS load helper writes M0 in inline asm and lists it
+    # as clobbered; M0 is reserved, so the compiler warns on every use
+    "-Wno-inline-asm",
     "-I", INCLUDE, "-I", CSRC,
 ]
 

@@ -99,7 +99,7 @@ static int logits_impl(const void* x, int x_dtype, int64_t M, const void* packed
     if (x_dtype != F16 && x_dtype != BF16) return LMH_E_DTYPE;
     if (scale_dtype != F16 && scale_dtype != BF16) return LMH_E_DTYPE;
     if (M < 0 || M > 65535) return LMH_E_SHAPE;
-    if (path < 0 || path > 2) return LMH_E_UNSUPPORTED;
+    if (path < 0 || path > 3) return LMH_E_UNSUPPORTED;
     if (M == 0 || V == 0) return LMH_OK;
     if (ldy < V) return LMH_E_SHAPE;
     if (!x || !packed || !y) return LMH_E_NULL;
@@ -110,6 +110,8 @@ static int logits_impl(const void* x, int x_dtype, int64_t M, const void* packed
         if (!workspace || ws_bytes < need) return LMH_E_WORKSPACE;
         if (!aligned16(workspace)) return LMH_E_ALIGN;
     }
+    // the MFMA launch has one workgroup per (256 rows, 16..32 activations)
+    if ((V + 255) / 256 * ((M + 15) / 16) >= (int64_t(1) << 30)) return LMH_E_UNSUPPORTED;
     const bool gemv_ok = M <= lmh::kGemvMaxM && M * K <= lmh::kGemvMaxMK;
     if (path == 1 && !gemv_ok) return LMH_E_UNSUPPORTED;
 
@@ -136,7 +138,11 @@ static int logits_impl(const void* x, int x_dtype, int64_t M, const void* packed
     a.bits = bits;
     a.scale_bf16 = scale_dtype == BF16;
     const bool use_gemv = path == 1 || (path == 0 && gemv_ok && M <= lmh::kGemvAutoMaxM);
-    return from_hip(use_gemv ? lmh::launch_gemv(a, st) : lmh::launch_mfma(a, st));
+    if (use_gemv) return from_hip(lmh::launch_gemv(a, st));
+    // automatic: the LDS-staged kernel where it measured fastest (33..64 rows
+    // on the 151936 x 1024 int4 head), the register-fed one elsewhere
+    const bool use_lds = path == 3 || (path == 0 && M > 32 && M <= 64);
+    return from_hip(use_lds ? lmh::launch_mfma_lds(a, st) : lmh::launch_mfma(a, st));
 }
 
 int lmhead_logits(const void* x, int x_dtype, int64_t M, const void* packed, int64_t V, int64_t K,

@@ -39,6 +39,7 @@ hipError_t launch_x_to_f16(const uint16_t* x_bf16, int M, int K, _Float16* xh, i
                            hipStream_t st);
 hipError_t launch_gemv(const LogitsArgs& a, hipStream_t st);
 hipError_t launch_mfma(const LogitsArgs& a, hipStream_t st);
+hipError_t launch_mfma_lds(const LogitsArgs& a, hipStream_t st);
 hipError_t launch_dense(const void* x, int dtype, int M, const void* w, int64_t V, int64_t K,
                         float* y, int64_t ldy, hipStream_t st);
 hipError_t launch_topk_rescore(const void* x, int x_dtype, int M, const void* w, int w_dtype,

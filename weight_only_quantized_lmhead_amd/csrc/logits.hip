@@ -244,6 +244,11 @@ __global__ __launch_bounds__(256, MT >= 4 ? 1 : 2) void mfma_kernel(
     const uint4* __restrict__ wq, const uint16_t* __restrict__ sc, const _Float16* __restrict__ x,
     const int* __restrict__ xexp, const float* __restrict__ bias, float* __restrict__ y,
     int64_t ldy, int V, int K, int M, int NB, int NC, int NG, int SPG, int sbf16) {
+    // grid (row groups, activation tiles): all row groups of one activation
+    // tile run before the next tile's; the last-level cache serves the
+    // re-read weights (an XCD-grouped order, which reads them from HBM once,
+    // measured slower on the 151936 x 1024 head at M = 256)
+    const int rg = blockIdx.x, mtile = blockIdx.y;
     constexpr int NT = 4;
     constexpr int SPAN = BITS == 4 ? 128 : 64;
     constexpr int CPS = SPAN / 32;
@@ -259,11 +264,11 @@ __global__ __launch_bounds__(256, MT >= 4 ? 1 : 2) void mfma_kernel(
 
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
-    const int blk = blockIdx.x * 4 + wv;
+    const int blk = rg * 4 + wv;
     const bool live = blk < NB;
     const int blkc = live ? blk : NB - 1;
     const int r = lane & 15, t = lane >> 4;
-    const int m0 = blockIdx.y * ROWS;
+    const int m0 = mtile * ROWS;
     const uint4* wp = wq + (int64_t)blkc * NC * 256 + t * 64 + r;
     const uint16_t* sp = sc + (int64_t)blkc * NG * 64 + r;
     const uint32_t magic = 0x64006400u;
@@ -396,6 +401,253 @@ __global__ __launch_bounds__(256, MT >= 4 ? 1 : 2) void mfma_kernel(
     }
 }
 
+// One direct global->LDS load of 16 bytes per active lane: lane i writes
+// LDS bytes [lds + 16i, lds + 16i + 16) from its own global address `g`
+// (global_load_lds_dwordx4; `lds` must be wave-uniform).  Issued through asm
+// so that the compiler does not track it: its conservative wait analysis
+// would otherwise wait for every stage in flight before any LDS read.  The
+// caller waits with s_waitcnt vmcnt before reading the stage.  M0 is written
+// here and by nothing else in the kernels that use this helper.
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// ---------------------------------------------------------------------------
+// LDS-staged MFMA kernel (larger M).  A tile is 4 row blocks (256
+// vocabulary rows) x 16*MT activation rows with the same lane roles as
+// mfma_kernel (lane (r, t) of wave w owns row block 4*rg + w), but every
+// operand goes through LDS by direct global->LDS loads, so no registers hold
+// data in flight and the activation tile can be 64-128 rows, which shares each
+// unpacked B operand among 4-8 MFMAs.
+// Per superchunk a stage holds:
+//   W  the 4 row blocks' packed superchunks as stored (4 x 4 KiB);
+//   S  their scales for the superchunk's groups (4 x GPS x 128 B);
+//   X  the activation tile, row-major, 16-byte piece p of row m stored at
+//      piece (p ^ (m mod P8)) of that row (P8 = pieces per row), so the 16
+//      rows of one A-operand read fall in distinct banks.
+// A workgroup runs one or more tiles back to back as one stream of (tile,
+// superchunk) steps, with the loads of the next STAGES-1 steps in flight
+// (across tile boundaries too).  Tiles are numbered rg*NMT + mtile (the
+// activation tiles of a row group are adjacent); XCD x (workgroups b with
+// b % 8 == x) owns a contiguous eighth of them, dealt round-robin to its
+// workgroups, so the activation tiles of one row group run at the same time
+// on one XCD and read its weights through that XCD's L2 once.
+template <int BITS, int MT, int GPS, int STAGES>
+__global__ __launch_bounds__(256, MT <= 4 ? 2 : 1) void mfma_lds_kernel(
+    const uint4* __restrict__ wq, const uint16_t* __restrict__ sc, const _Float16* __restrict__ x,
+    const int* __restrict__ xexp, const float* __restrict__ bias, float* __restrict__ y,
+    int64_t ldy, int V, int K, int M, int NB, int NC, int NG, int SPG, int sbf16, int NMT,
+    int total) {
+    constexpr int NT = 4;
+    constexpr int SPAN = BITS == 4 ? 128 : 64;
+    constexpr int CPS = SPAN / 32;
+    constexpr int CPG = CPS / GPS;
+    constexpr int P8 = SPAN / 8;           // 16-byte pieces per activation row
+    constexpr int ROWS = MT * 16;
+    constexpr int WB = 4 * 4096;           // packed weights per stage
+    constexpr int SB = 4 * GPS * 128;      // scales per stage
+    constexpr int XB = ROWS * SPAN * 2;    // activation tile per stage
+    constexpr int STB = WB + SB + XB;
+    constexpr int NXW = ROWS * P8 / 64 / 4;  // activation loads per wave per stage
+    static_assert(ROWS * P8 % 256 == 0, "activation tile must split evenly over 4 waves");
+    constexpr int NPS = 4 + 1 + NXW;  // loads per wave per stage
+    static_assert(STAGES == 2 || STAGES == 3, "two or three stages");
+    static_assert(NPS < 64, "vmcnt holds 6 bits");
+    __shared__ __attribute__((aligned(16))) unsigned char lds[STAGES * STB];
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_offset(lds));
+
+    // this workgroup's tiles: xt0 + l, xt0 + l + L, ... < xt1
+    const int L = gridDim.x >> 3, xcd = blockIdx.x & 7, l = blockIdx.x >> 3;
+    const int perx = (total + 7) / 8;
+    const int xt0 = xcd * perx;
+    const int xt1 = min(xt0 + perx, total);
+    const int ntile = xt1 - xt0 > l ? (xt1 - xt0 - l + L - 1) / L : 0;
+    const int nsteps = ntile * NC;
+    if (nsteps == 0) return;
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int r = lane & 15, t = lane >> 4;
+    // fixed parts of this lane's activation loads: wave instruction q = wv + 4i
+    // fills LDS pieces [64q, 64q+64); piece P = row*P8 + sp holds global piece
+    // sp ^ (row % P8); rows past M read row M-1 (never stored)
+    int xrow[NXW], xcol[NXW];
+#pragma unroll
+    for (int i = 0; i < NXW; ++i) {
+        const int P = (wv + 4 * i) * 64 + lane;
+        xrow[i] = P / P8;
+        xcol[i] = 8 * ((P % P8) ^ ((P / P8) % P8));
+    }
+
+    auto tile_of = [&](int i, int& rg, int& mtile) {
+        const int tt = xt0 + l + i * L;
+        rg = tt / NMT;
+        mtile = tt - rg * NMT;
+    };
+    auto issue = [&](int stage, int s) {
+        const int i = s / NC, c = s - i * NC;
+        int rg, mtile;
+        tile_of(i, rg, mtile);
+        const int blk = min(rg * 4 + wv, NB - 1);
+        const int m0 = mtile * ROWS;
+        const uint32_t sb = lds0 + stage * STB;
+        const uint4* wc = wq + ((int64_t)blk * NC + c) * 256 + lane;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) lds_dma16(wc + k * 64, sb + wv * 4096 + k * 1024);
+        const int g0 = GPS > 1 ? c * GPS : c / SPG;
+        if (lane < GPS * 8)
+            lds_dma16((const uint4*)(sc + ((int64_t)blk * NG + g0) * 64) + lane,
+                      sb + WB + wv * GPS * 128);
+        const _Float16* xc = x + (int64_t)m0 * K + c * SPAN;
+#pragma unroll
+        for (int k = 0; k < NXW; ++k) {
+            const int rr = m0 + xrow[k] < M ? xrow[k] : M - 1 - m0;
+            lds_dma16(xc + rr * K + xcol[k], sb + WB + SB + (wv + 4 * k) * 1024);
+        }
+    };
+
+    f4 acc[MT][NT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = (f4){0.f, 0.f, 0.f, 0.f};
+    const uint32_t magic = 0x64006400u;
+
+    auto compute = [&](const unsigned char* s) {
+        uint4 wr[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+            wr[nt] = *(const uint4*)(s + wv * 4096 + (t * 64 + 16 * nt + r) * 16);
+        const uint16_t* S = (const uint16_t*)(s + WB + wv * GPS * 128);
+        const unsigned char* X = s + WB + SB;
+#pragma unroll
+        for (int g = 0; g < GPS; ++g) {
+            h8 bop[NT][CPG];
+            float sv[NT];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+                for (int jj = 0; jj < CPG; ++jj) {
+                    const int j = g * CPG + jj;
+                    h2 p0, p1, p2, p3;
+                    if constexpr (BITS == 4) {
+                        unpack_i4(word_of(wr[nt], j), magic, p0, p1, p2, p3);
+                    } else {
+                        unpack_i8(word_of(wr[nt], 2 * j), p0, p1);
+                        unpack_i8(word_of(wr[nt], 2 * j + 1), p2, p3);
+                    }
+                    bop[nt][jj] = (h8){p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+                }
+                sv[nt] = scale_to_f32(S[g * 64 + 16 * nt + r], sbf16);
+            }
+            // software pipeline over the activation tiles: the A operands of
+            // tile mt+1 are read from LDS and the scale FMAs of tile mt-1 are
+            // issued while the MFMA chains of tile mt run
+            auto load_a = [&](int mt, h8 (&a)[CPG]) {
+                const int m = 16 * mt + r;
+#pragma unroll
+                for (int jj = 0; jj < CPG; ++jj) {
+                    const int pc = 4 * (g * CPG + jj) + t;
+                    a[jj] = *(const h8*)(X + (m * P8 + (pc ^ (m % P8))) * 16);
+                }
+            };
+            h8 a0[CPG], a1[CPG];
+            f4 p0[NT], p1[NT];
+            load_a(0, a0);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                h8 (&acur)[CPG] = (mt & 1) ? a1 : a0;
+                h8 (&anxt)[CPG] = (mt & 1) ? a0 : a1;
+                f4 (&pcur)[NT] = (mt & 1) ? p1 : p0;
+                f4 (&pprv)[NT] = (mt & 1) ? p0 : p1;
+                if (mt + 1 < MT) load_a(mt + 1, anxt);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    f4 q = __builtin_amdgcn_mfma_f32_16x16x32_f16(acur[0], bop[nt][0],
+                                                                   (f4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+                    for (int jj = 1; jj < CPG; ++jj)
+                        q = __builtin_amdgcn_mfma_f32_16x16x32_f16(acur[jj], bop[nt][jj], q, 0, 0, 0);
+                    pcur[nt] = q;
+                }
+                if (mt > 0) {
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) acc[mt - 1][nt] += sv[nt] * pprv[nt];
+                }
+            }
+            {
+                f4 (&plast)[NT] = ((MT - 1) & 1) ? p1 : p0;
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) acc[MT - 1][nt] += sv[nt] * plast[nt];
+            }
+        }
+    };
+
+    // results of tile i: y[m, v] = acc * 2^xexp[m] + bias[v]; plain stores,
+    // left to drain while the next tile computes
+    auto epilogue = [&](int i) {
+        int rg, mtile;
+        tile_of(i, rg, mtile);
+        const int blk = rg * 4 + wv;
+        const int m0 = mtile * ROWS;
+        if (blk < NB) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const int v = blk * 64 + 16 * nt + r;
+                const float b = (bias && v < V) ? bias[v] : 0.0f;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int m = m0 + 16 * mt + 4 * t + e;
+                        if (m < M && v < V) {
+                            float o = acc[mt][nt][e];
+                            if (xexp) o = ldexpf(o, xexp[m]);
+                            y[(int64_t)m * ldy + v] = o + b;
+                        }
+                    }
+            }
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = (f4){0.f, 0.f, 0.f, 0.f};
+    };
+
+    // Step s: wait for this wave's loads of stage s (loads of later stages,
+    // issued after them, may still be in flight) and for its LDS reads, then
+    // meet the other waves at a bare s_barrier (a __syncthreads() fence would
+    // also wait for the later stages' loads; the empty asm statements keep
+    // the compiler from moving memory accesses across it); refill the stage
+    // read in step s-1, which every wave finished before the barrier.
+    constexpr int kWaitNewer = (NPS & 15) | ((NPS >> 4) << 14) | (7 << 4);
+    constexpr int kWaitAll = 7 << 4;
+    constexpr int AHEAD = STAGES - 1;
+    for (int s = 0; s < AHEAD && s < nsteps; ++s) issue(s, s);
+    int stage = 0, s = 0;
+    for (int i = 0; i < ntile; ++i) {
+        for (int c = 0; c < NC; ++c, ++s) {
+            if (STAGES == 3 && s + 1 < nsteps)
+                __builtin_amdgcn_s_waitcnt(kWaitNewer);
+            else
+                __builtin_amdgcn_s_waitcnt(kWaitAll);
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            if (s + AHEAD < nsteps) issue(stage == 0 ? STAGES - 1 : stage - 1, s + AHEAD);
+            compute(lds + stage * STB);
+            stage = stage + 1 == STAGES ? 0 : stage + 1;
+        }
+        epilogue(i);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Dense 16-bit control GEMV: a wave computes 4 rows at a time; lane l covers
 // columns 8l + 512i; partial sums meet in a fixed xor-shuffle tree.
@@ -522,6 +774,41 @@ hipError_t mfma_dispatch_mt(const LogitsArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
+template <int BITS, int MT, int STAGES>
+hipError_t mfma_lds_dispatch_mt(const LogitsArgs& a, hipStream_t st) {
+    const int NB = (int)((a.V + 63) / 64);
+    const int NC = (int)(a.K / span_of(BITS));
+    const int NG = (int)(a.K / a.G);
+    const int gps = gps_of(BITS, a.G);
+    const int SPG = gps == 1 ? (int)(a.G / span_of(BITS)) : 1;
+    const uint4* wq = (const uint4*)a.packed;
+    const uint16_t* sc = (const uint16_t*)(a.packed + (int64_t)NB * 64 * a.K * BITS / 8);
+    const int NMT = (a.M + MT * 16 - 1) / (MT * 16);
+    const int total = (NB + 3) / 4 * NMT;
+    // one tile per workgroup (the kernel also runs several tiles per
+    // workgroup, back to back, when the grid is smaller: measured slower on
+    // the 151936 x 1024 head, whose output stores then stall the next tile)
+    const dim3 grid((unsigned)((total + 7) / 8 * 8));
+#define LMH_MFMA_LDS(G_)                                                                           \
+    hipLaunchKernelGGL((mfma_lds_kernel<BITS, MT, G_, STAGES>), grid, dim3(256), 0, st, wq, sc,   \
+                       (const _Float16*)a.x, a.xexp, a.bias, a.y, a.ldy, (int)a.V, (int)a.K, a.M, \
+                       NB, NC, NG, SPG, a.scale_bf16, NMT, total)
+    if (gps == 1) LMH_MFMA_LDS(1);
+    else if constexpr (BITS == 8) LMH_MFMA_LDS(2);
+    else if (gps == 2) LMH_MFMA_LDS(2);
+    else LMH_MFMA_LDS(4);
+#undef LMH_MFMA_LDS
+    return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t mfma_lds_dispatch(const LogitsArgs& a, hipStream_t st) {
+    // 64-row tiles for M <= 64 (two stages, 66 KiB of LDS, two workgroups
+    // per CU), else 128-row tiles (three stages, 147 KiB, one per CU)
+    if (a.M <= 64) return mfma_lds_dispatch_mt<BITS, 4, 2>(a, st);
+    return mfma_lds_dispatch_mt<BITS, 8, 3>(a, st);
+}
+
 template <int BITS>
 hipError_t mfma_dispatch(const LogitsArgs& a, hipStream_t st) {
     // one 16-row activation tile for M <= 16; two (32 rows) otherwise: the
@@ -545,6 +832,10 @@ hipError_t launch_gemv(const LogitsArgs& a, hipStream_t st) {
 
 hipError_t launch_mfma(const LogitsArgs& a, hipStream_t st) {
     return a.bits == 4 ? mfma_dispatch<4>(a, st) : mfma_dispatch<8>(a, st);
+}
+
+hipError_t launch_mfma_lds(const LogitsArgs& a, hipStream_t st) {
+    return a.bits == 4 ? mfma_lds_dispatch<4>(a, st) : mfma_lds_dispatch<8>(a, st);
 }
 
 hipError_t launch_dense(const void* x, int dtype, int M, const void* w, int64_t V, int64_t K,
