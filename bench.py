@@ -42,6 +42,132 @@ def algorithmic_bytes(M, V, K, bits, G):
     return V * K * bits // 8 + V * (K // G) * 2 + M * K * 2 + M * V * 4
 
 
+# Sources whose change invalidates a recorded traffic measurement of the
+# logits kernels.
+TRAFFIC_SOURCES = ["weight_only_quantized_lmhead_amd/csrc/logits.hip",
+                   "weight_only_quantized_lmhead_amd/csrc/lmh_internal.h",
+                   "weight_only_quantized_lmhead_amd/build.py"]
+
+
+def sources_sha() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"logits_{workload}_hbm_traffic.md")
+
+
+def recorded_traffic(workload: str, kernel_prefix: str):
+    """HBM bytes per launch of the kernel from the committed counter summary,
+    or None when there is none or the kernel sources changed since."""
+    f = traffic_file(workload)
+    if not os.path.exists(f):
+        return None
+    for line in open(f):
+        if line.startswith("<!-- traffic "):
+            rec = json.loads(line[len("<!-- traffic "):].rsplit("-->", 1)[0])
+            if rec.get("sources_sha") != sources_sha():
+                return None
+            for k in rec["kernels"]:
+                if k["kernel"].startswith(kernel_prefix):
+                    return k
+    return None
+
+
+def _short_kernel(name: str) -> str:
+    import re
+
+    m = re.match(r"_ZN3lmh12_GLOBAL__N_1(\d+)(\w+)", name)
+    if m:
+        n = int(m.group(1))
+        base, rest = m.group(2)[:n], m.group(2)[n:]
+        targs = ",".join(re.findall(r"Li(\d+)E", rest))
+        return f"{base}<{targs}>"
+    name = name.replace("void ", "").replace("lmh::(anonymous namespace)::", "")
+    return name.split("(")[0][:60]
+
+
+def summarize(args) -> int:
+    """Write a profiles/ summary from rocprofv3 CSV output: the kernel-trace
+    statistics and, when given, the FETCH_SIZE / WRITE_SIZE counter runs
+    scaled by the copy kernel of known size (the packed-head clones)."""
+    import csv
+    import statistics
+
+    import synth
+    import weight_only_quantized_lmhead_amd as lmh
+
+    w = synth.WORKLOADS[args.workload or synth.HEADLINE]
+    out = []
+    out.append(f"# Logits hot path on {w.name} ({w.V} x {w.K}, int{w.bits}, G={w.group}), one MI355X\n")
+    out.append("Commands (from the repository root; `cd /tmp && export TMPDIR=/tmp` first):\n")
+    out.append("```")
+    out.extend(args.cmd)
+    out.append("```\n")
+    rows = list(csv.DictReader(open(args.stats)))
+    out.append("## Kernel durations (rocprofv3 --kernel-trace --stats)\n")
+    out.append("| kernel | calls | average (us) | min (us) | max (us) | share |")
+    out.append("|---|---|---|---|---|---|")
+    for r in rows:
+        out.append(f"| `{_short_kernel(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                   f"{float(r['Percentage']):.1f}% |")
+    out.append("")
+    text = "\n".join(out) + "\n"
+    if args.fetch and args.write:
+        blob = lmh.packed_bytes(w.V, w.K, w.bits, w.group)
+
+        def per_kernel(path, counter):
+            # keyed by kernel and grid size (one logits kernel serves several M)
+            vals = {}
+            for r in csv.DictReader(open(path)):
+                if r["Counter_Name"] == counter:
+                    k = _short_kernel(r["Kernel_Name"])
+                    if not k.startswith("__amd"):
+                        k = f"{k} grid {r['Grid_Size']}"
+                    vals.setdefault(k, []).append(float(r["Counter_Value"]))
+            return vals
+
+        fv, wv = per_kernel(args.fetch, "FETCH_SIZE"), per_kernel(args.write, "WRITE_SIZE")
+        # the largest copy dispatches are the packed-head clones: blob bytes each
+        copy_f = max(fv["__amd_rocclr_copyBuffer"])
+        copy_w = max(wv["__amd_rocclr_copyBuffer"])
+        kf, kw = blob / 1024 / copy_f, blob / 1024 / copy_w
+        t = ["## HBM traffic (rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE)\n",
+             f"Calibration: the copy kernel that clones the {blob}-byte packed head reads "
+             f"FETCH_SIZE = {copy_f:.1f} KiB and WRITE_SIZE = {copy_w:.1f} KiB per dispatch, so "
+             f"bytes read = FETCH_SIZE x {kf:.5f} x 1024 and bytes written = WRITE_SIZE x {kw:.5f} x 1024.\n",
+             "| kernel | dispatches | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | read (B) | written (B) | total (B) |",
+             "|---|---|---|---|---|---|---|"]
+        recs = []
+        for k in sorted(fv):
+            if not (k.startswith("gemv_kernel") or k.startswith("mfma") or k.startswith("topk")):
+                continue
+            f_ = statistics.mean(fv[k])
+            w_ = statistics.mean(wv.get(k, [0.0]))
+            rb, wb = f_ * kf * 1024, w_ * kw * 1024
+            t.append(f"| `{k}` | {len(fv[k])} | {f_:.1f} | {w_:.1f} | {rb:.0f} | {wb:.0f} | {rb + wb:.0f} |")
+            recs.append({"kernel": k, "read_bytes": round(rb), "write_bytes": round(wb),
+                         "bytes": round(rb + wb), "dispatches": len(fv[k])})
+        t.append("")
+        t.append("Per-dispatch averages over every dispatch of the kernel in the run (the counter runs "
+                 "use the M values named in the commands).  `sources_sha` below is a hash of the kernel "
+                 "sources; bench.py reports `traffic` only while it matches.\n")
+        rec = {"workload": w.name, "sources_sha": sources_sha(), "kernels": recs}
+        t.append("<!-- traffic " + json.dumps(rec) + " -->")
+        text += "\n".join(t) + "\n"
+    with open(args.out, "w") as fh:
+        fh.write(text)
+    print(text)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -54,7 +180,16 @@ def main() -> int:
     ap.add_argument("--hot", action="store_true", help="reuse one copy of the head (cache-hot; labelled)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--summarize", action="store_true",
+                    help="write a profiles/ summary from rocprofv3 CSV files instead of timing")
+    ap.add_argument("--stats", help="kernel_stats.csv of a --kernel-trace --stats run")
+    ap.add_argument("--fetch", help="counter_collection.csv of a --pmc FETCH_SIZE run")
+    ap.add_argument("--write", help="counter_collection.csv of a --pmc WRITE_SIZE run")
+    ap.add_argument("--out", help="summary file to write")
+    ap.add_argument("--cmd", action="append", default=[], help="command line to record (repeatable)")
     args = ap.parse_args()
+    if args.summarize:
+        return summarize(args)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the head would be "
@@ -176,10 +311,12 @@ def main() -> int:
 
     m1 = per_call[f"M={Ms[0]}"]
     value = m1["us"]
+    tr = recorded_traffic(w.name, "gemv_kernel") if m1["kernel"] == "gemv" else None
     roofline = {
         "bound": "hbm", "kernel": f"lmh gemv, M={Ms[0]}", "achieved": m1["GB/s"], "peak": HBM_PEAK_GBS,
-        "unit": "GB/s", "frac": m1["frac_hbm_peak"], "traffic": None,
+        "unit": "GB/s", "frac": m1["frac_hbm_peak"], "traffic": tr["bytes"] if tr else None,
         "bytes_per_launch": m1["algorithmic_bytes"],
+        "traffic_source": os.path.relpath(traffic_file(w.name), ROOT) if tr else None,
     }
 
     cpu = None
@@ -195,7 +332,7 @@ def main() -> int:
         qo, so = oracle.quantize(Wh, w.bits, w.group, od[w.scale_dtype], ratios, w_dtype=od[w.w_dtype])
         x1 = synth.activations(w, Ms[0])
         n, t_cpu = 0, 0.0
-        while n < 3 and (n == 0 or t_cpu < args.cpu_seconds):
+        while n < 50 and (n == 0 or t_cpu < args.cpu_seconds):
             c0 = time.perf_counter()
             oracle.logits(x1, qo, so, od[w.scale_dtype], w.group, x_dtype=od[w.x_dtype])
             t_cpu += time.perf_counter() - c0
