@@ -99,14 +99,19 @@ __global__ __launch_bounds__(256) void x_to_f16_kernel(const uint16_t* __restric
 }
 
 // ---------------------------------------------------------------------------
-// GEMV: one wave per 64-row block, one lane per row, all of K per wave (no
-// cross-lane or cross-wave reduction).  Superchunks stream through a ring of
-// D register buffers; loads past the end are clamped to the last superchunk
-// (and their contribution dropped) so every load is unconditional and the
-// compiler can keep exact vmcnt accounting (no drain at the loop head).
-// GPS = groups per superchunk (G <= span); GPS == 1 covers G >= span, the
-// scale of superchunk c then being that of group c / SPG.
-template <int BITS, int MM, int GPS, int D>
+// GEMV: one lane per row of a 64-row block.  KS waves share a block, each
+// taking a contiguous 1/KS of the superchunks (KS = 1: all of K, no
+// reduction; KS > 1: the KS partial sums meet in LDS and are added in wave
+// order, so the result does not depend on timing).  Splitting K puts KS times
+// as many loads in flight per row block and gives the launch KS times as many
+// waves, which spreads a ragged number of blocks evenly over the CUs.
+// Superchunks stream through a ring of D register buffers; loads past the end
+// of the wave's range are clamped to its last superchunk (and their
+// contribution dropped) so every load is unconditional and the compiler can
+// keep exact vmcnt accounting (no drain at the loop head).  GPS = groups per
+// superchunk (G <= span); GPS == 1 covers G >= span, the scale of superchunk c
+// then being that of group c / SPG.
+template <int BITS, int MM, int GPS, int D, int KS>
 __global__ __launch_bounds__(256) void gemv_kernel(const uint4* __restrict__ wq,
                                                    const uint16_t* __restrict__ sc,
                                                    const h2* __restrict__ xg,
@@ -118,6 +123,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint4* __restrict__ wq,
     constexpr int CPS = SPAN / 32;    // 32-column chunks per superchunk
     constexpr int CPG = CPS / GPS;    // chunks per group
     constexpr int NA = MM == 1 ? 4 : (MM == 2 ? 2 : 1);  // independent partial sums per group
+    static_assert(KS == 1 || KS == 2 || KS == 4, "K split over 1, 2 or 4 waves");
     // x (all M rows, all of K) is staged once per workgroup in LDS; every lane
     // then reads the same 16 bytes at a time (an LDS broadcast).
     extern __shared__ uint4 xs_raw[];
@@ -129,8 +135,14 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint4* __restrict__ wq,
     }
     __syncthreads();
     const int lane = threadIdx.x & 63;
-    const int blk = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (blk >= NB) return;  // wave-uniform; no barriers below
+    const int wv = threadIdx.x >> 6;
+    const int blk_raw = blockIdx.x * (4 / KS) + wv / KS;
+    const int ks = wv % KS;
+    if (KS == 1 && blk_raw >= NB) return;  // wave-uniform; no barriers below when KS == 1
+    const bool live = blk_raw < NB;
+    const int blk = live ? blk_raw : NB - 1;
+    const int NCs = NC / KS;      // superchunks per wave
+    const int c0 = ks * NCs;      // first superchunk of this wave
     const uint4* wp = wq + (int64_t)blk * NC * 256 + lane;
     const uint16_t* sp = sc + (int64_t)blk * NG * 64 + lane;
     const int Kh = K >> 1;
@@ -139,9 +151,11 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint4* __restrict__ wq,
     uint4 buf[D][4];
     uint16_t sb[D][GPS];
     // scale bookkeeping of the prefetch stream when a group spans superchunks
-    int pf_g = 0, pf_left = SPG;
+    // (c0 is a multiple of SPG: the host only splits K on group boundaries)
+    int pf_g = c0 / SPG, pf_left = SPG;
+    const int cend = c0 + NCs;
     auto load = [&](int p, int c) {
-        const int cc = c < NC ? c : NC - 1;
+        const int cc = c < cend ? c : cend - 1;
 #pragma unroll
         for (int t = 0; t < 4; ++t) buf[p][t] = wp[((int64_t)cc * 4 + t) * 64];
         if constexpr (GPS > 1) {
@@ -160,12 +174,12 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint4* __restrict__ wq,
 #pragma unroll
     for (int m = 0; m < MM; ++m) acc[m] = 0.0f;
 #pragma unroll
-    for (int p = 0; p < D; ++p) load(p, p);
-    for (int cb = 0; cb < NC; cb += D) {
+    for (int p = 0; p < D; ++p) load(p, c0 + p);
+    for (int cb = c0; cb < cend; cb += D) {
 #pragma unroll
         for (int p = 0; p < D; ++p) {
             const int c = cb + p;
-            const int cl = c < NC ? c : NC - 1;
+            const int cl = c < cend ? c : cend - 1;
             float part[MM][GPS][NA];
 #pragma unroll
             for (int m = 0; m < MM; ++m)
@@ -198,7 +212,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint4* __restrict__ wq,
                     }
                 }
             }
-            const bool real = c < NC;
+            const bool real = c < cend;
 #pragma unroll
             for (int g = 0; g < GPS; ++g) {
                 const float sv = real ? scale_to_f32(sb[p][g], sbf16) : 0.0f;
@@ -213,8 +227,22 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint4* __restrict__ wq,
             load(p, c + D);
         }
     }
+    if constexpr (KS > 1) {
+        __shared__ float red[4][MM][64];
+#pragma unroll
+        for (int m = 0; m < MM; ++m) red[wv][m][lane] = acc[m];
+        __syncthreads();
+        if (ks != 0) return;
+#pragma unroll
+        for (int m = 0; m < MM; ++m) {
+            float r = red[wv][m][lane];
+#pragma unroll
+            for (int k = 1; k < KS; ++k) r += red[wv + k][m][lane];
+            acc[m] = r;
+        }
+    }
     const int v = blk * 64 + lane;
-    if (v < V) {
+    if (live && v < V) {
         const float b = bias ? bias[v] : 0.0f;
 #pragma unroll
         for (int m = 0; m < MM; ++m) {
@@ -440,7 +468,7 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
 // workgroups, so the activation tiles of one row group run at the same time
 // on one XCD and read its weights through that XCD's L2 once.
 template <int BITS, int MT, int GPS, int STAGES>
-__global__ __launch_bounds__(256, MT <= 4 ? 2 : 1) void mfma_lds_kernel(
+__global__ __launch_bounds__(256, MT <= 2 ? 3 : (MT <= 4 ? 2 : 1)) void mfma_lds_kernel(
     const uint4* __restrict__ wq, const uint16_t* __restrict__ sc, const _Float16* __restrict__ x,
     const int* __restrict__ xexp, const float* __restrict__ bias, float* __restrict__ y,
     int64_t ldy, int V, int K, int M, int NB, int NC, int NG, int SPG, int sbf16, int NMT,
@@ -729,14 +757,21 @@ hipError_t gemv_dispatch_gps(const LogitsArgs& a, int gps, hipStream_t st) {
     const uint4* wq = (const uint4*)a.packed;
     const uint16_t* sc = (const uint16_t*)(a.packed + (int64_t)NB * 64 * a.K * BITS / 8);
     const size_t lds = (size_t)MM * a.K * 2;
-#define LMH_GEMV(G_)                                                                              \
-    hipLaunchKernelGGL((gemv_kernel<BITS, MM, G_, D>), dim3((NB + 3) / 4), dim3(256), lds, st,   \
-                       wq, sc, (const h2*)a.x, a.xexp, a.bias, a.y, a.ldy, (int)a.V, (int)a.K,    \
-                       NB, NC, NG, SPG, a.scale_bf16)
-    if (gps == 1) LMH_GEMV(1);
-    else if constexpr (BITS == 8) LMH_GEMV(2);
-    else if (gps == 2) LMH_GEMV(2);
-    else LMH_GEMV(4);
+    // split K over KS waves when every wave still gets at least 2 superchunks
+    // and the split falls on group boundaries
+    auto splits = [&](int ks) { return NC % (2 * ks) == 0 && (NC / ks) % SPG == 0; };
+    const int KS = splits(4) ? 4 : splits(2) ? 2 : 1;
+#define LMH_GEMV(G_, KS_)                                                                         \
+    hipLaunchKernelGGL((gemv_kernel<BITS, MM, G_, D, KS_>), dim3((NB * KS_ + 3) / 4), dim3(256),  \
+                       lds, st, wq, sc, (const h2*)a.x, a.xexp, a.bias, a.y, a.ldy, (int)a.V,     \
+                       (int)a.K, NB, NC, NG, SPG, a.scale_bf16)
+#define LMH_GEMV_KS(G_) \
+    if (KS == 4) LMH_GEMV(G_, 4); else if (KS == 2) LMH_GEMV(G_, 2); else LMH_GEMV(G_, 1)
+    if (gps == 1) { LMH_GEMV_KS(1); }
+    else if constexpr (BITS == 8) { LMH_GEMV_KS(2); }
+    else if (gps == 2) { LMH_GEMV_KS(2); }
+    else { LMH_GEMV_KS(4); }
+#undef LMH_GEMV_KS
 #undef LMH_GEMV
     return hipGetLastError();
 }
@@ -805,6 +840,7 @@ template <int BITS>
 hipError_t mfma_lds_dispatch(const LogitsArgs& a, hipStream_t st) {
     // 64-row tiles for M <= 64 (two stages, 66 KiB of LDS, two workgroups
     // per CU), else 128-row tiles (three stages, 147 KiB, one per CU)
+    if (a.M <= 32) return mfma_lds_dispatch_mt<BITS, 2, 2>(a, st);
     if (a.M <= 64) return mfma_lds_dispatch_mt<BITS, 4, 2>(a, st);
     return mfma_lds_dispatch_mt<BITS, 8, 3>(a, st);
 }
