@@ -158,8 +158,8 @@ size_t lmhead_logits_workspace_bytes(int64_t M, int64_t K, int x_dtype);
  *           (may be NULL/0 for fp16 x).
  *   M = 1 runs a GEMV with one lane per vocabulary row (all of K per wave);
  *   M >= 2 runs a 16x16x32 fp16 MFMA kernel (its code unpacking is shared by
- *   all activation rows): the register-fed one, or for 17 <= M <= 64 the
- *   LDS-staged one (see lmhead_logits_path).  Every kernel runs the same
+ *   all activation rows): the register-fed one for M <= 16, the LDS-staged
+ *   one from M = 17 on (see lmhead_logits_path).  Every kernel runs the same
  *   per-group MFMA chains and fp32 scale FMAs in the same order, so the two
  *   MFMA kernels give bit-identical results.  The result does not depend on
  *   the stream or on other calls.
@@ -173,8 +173,8 @@ int lmhead_logits(const void* x, int x_dtype, int64_t M, const void* packed, int
  *   path 0 = automatic (exactly lmhead_logits), 1 = the lane-per-row GEMV
  *   (M <= 4, else LMH_E_UNSUPPORTED), 2 = the MFMA kernel with B operands
  *   loaded straight into registers (any M), 3 = the MFMA kernel with every
- *   operand staged in LDS by direct global-to-LDS loads (any M; 32, 64 or
- *   128 activation rows per workgroup).  All kernels compute the same function;
+ *   operand staged in LDS by direct global-to-LDS loads (any M; 32 or 64
+ *   activation rows per workgroup).  All kernels compute the same function;
  *   this entry point exists to test and time each of them on the same shapes.
  */
 int lmhead_logits_path(const void* x, int x_dtype, int64_t M, const void* packed, int64_t V,

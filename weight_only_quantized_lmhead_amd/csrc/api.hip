@@ -139,9 +139,9 @@ static int logits_impl(const void* x, int x_dtype, int64_t M, const void* packed
     a.scale_bf16 = scale_dtype == BF16;
     const bool use_gemv = path == 1 || (path == 0 && gemv_ok && M <= lmh::kGemvAutoMaxM);
     if (use_gemv) return from_hip(lmh::launch_gemv(a, st));
-    // automatic: the LDS-staged kernel where it measured fastest (17..64 rows
-    // on the 151936 x 1024 int4 head), the register-fed one elsewhere
-    const bool use_lds = path == 3 || (path == 0 && M > 16 && M <= 64);
+    // automatic: the LDS-staged kernel where it measured fastest (from 17
+    // rows on, on the 151936 x 1024 int4 head), the register-fed one for 2..16
+    const bool use_lds = path == 3 || (path == 0 && M > 16);
     return from_hip(use_lds ? lmh::launch_mfma_lds(a, st) : lmh::launch_mfma(a, st));
 }
 

@@ -448,15 +448,15 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
 }
 
 // ---------------------------------------------------------------------------
-// LDS-staged MFMA kernel (larger M).  A tile is 4 row blocks (256
-// vocabulary rows) x 16*MT activation rows with the same lane roles as
-// mfma_kernel (lane (r, t) of wave w owns row block 4*rg + w), but every
+// LDS-staged MFMA kernel (larger M).  A tile is WPB row blocks (one per wave;
+// 64*WPB vocabulary rows) x 16*MT activation rows with the same lane roles as
+// mfma_kernel (lane (r, t) of wave w owns row block WPB*rg + w), but every
 // operand goes through LDS by direct global->LDS loads, so no registers hold
 // data in flight and the activation tile can be 64-128 rows, which shares each
 // unpacked B operand among 4-8 MFMAs.
 // Per superchunk a stage holds:
-//   W  the 4 row blocks' packed superchunks as stored (4 x 4 KiB);
-//   S  their scales for the superchunk's groups (4 x GPS x 128 B);
+//   W  the WPB row blocks' packed superchunks as stored (WPB x 4 KiB);
+//   S  their scales for the superchunk's groups (WPB x GPS x 128 B);
 //   X  the activation tile, row-major, 16-byte piece p of row m stored at
 //      piece (p ^ (m mod P8)) of that row (P8 = pieces per row), so the 16
 //      rows of one A-operand read fall in distinct banks.
@@ -466,9 +466,11 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
 // activation tiles of a row group are adjacent); XCD x (workgroups b with
 // b % 8 == x) owns a contiguous eighth of them, dealt round-robin to its
 // workgroups, so the activation tiles of one row group run at the same time
-// on one XCD and read its weights through that XCD's L2 once.
-template <int BITS, int MT, int GPS, int STAGES>
-__global__ __launch_bounds__(256, MT <= 2 ? 3 : (MT <= 4 ? 2 : 1)) void mfma_lds_kernel(
+// on one XCD and read its weights through that XCD's L2 once.  With WPB = 8
+// the 8 waves (two per SIMD) share one activation tile.
+template <int BITS, int MT, int GPS, int STAGES, int WPB>
+__global__ __launch_bounds__(64 * WPB, WPB == 8 ? 1 : (MT <= 2 ? 3 : (MT <= 4 ? 2 : 1)))
+void mfma_lds_kernel(
     const uint4* __restrict__ wq, const uint16_t* __restrict__ sc, const _Float16* __restrict__ x,
     const int* __restrict__ xexp, const float* __restrict__ bias, float* __restrict__ y,
     int64_t ldy, int V, int K, int M, int NB, int NC, int NG, int SPG, int sbf16, int NMT,
@@ -479,12 +481,13 @@ __global__ __launch_bounds__(256, MT <= 2 ? 3 : (MT <= 4 ? 2 : 1)) void mfma_lds
     constexpr int CPG = CPS / GPS;
     constexpr int P8 = SPAN / 8;           // 16-byte pieces per activation row
     constexpr int ROWS = MT * 16;
-    constexpr int WB = 4 * 4096;           // packed weights per stage
-    constexpr int SB = 4 * GPS * 128;      // scales per stage
+    constexpr int WB = WPB * 4096;         // packed weights per stage
+    constexpr int SB = WPB * GPS * 128;    // scales per stage
     constexpr int XB = ROWS * SPAN * 2;    // activation tile per stage
     constexpr int STB = WB + SB + XB;
-    constexpr int NXW = ROWS * P8 / 64 / 4;  // activation loads per wave per stage
-    static_assert(ROWS * P8 % 256 == 0, "activation tile must split evenly over 4 waves");
+    constexpr int NXW = ROWS * P8 / 64 / WPB;  // activation loads per wave per stage
+    static_assert(WPB == 4 || WPB == 8, "4 or 8 waves per workgroup");
+    static_assert(ROWS * P8 % (64 * WPB) == 0, "activation tile must split evenly over the waves");
     constexpr int NPS = 4 + 1 + NXW;  // loads per wave per stage
     static_assert(STAGES == 2 || STAGES == 3, "two or three stages");
     static_assert(NPS < 64, "vmcnt holds 6 bits");
@@ -505,12 +508,11 @@ __global__ __launch_bounds__(256, MT <= 2 ? 3 : (MT <= 4 ? 2 : 1)) void mfma_lds
     // fixed parts of this lane's activation loads: wave instruction q = wv + 4i
     // fills LDS pieces [64q, 64q+64); piece P = row*P8 + sp holds global piece
     // sp ^ (row % P8); rows past M read row M-1 (never stored)
-    int xrow[NXW], xcol[NXW];
+    int xrc[NXW];  // row | column << 16 (one register each)
 #pragma unroll
     for (int i = 0; i < NXW; ++i) {
-        const int P = (wv + 4 * i) * 64 + lane;
-        xrow[i] = P / P8;
-        xcol[i] = 8 * ((P % P8) ^ ((P / P8) % P8));
+        const int P = (wv + WPB * i) * 64 + lane;
+        xrc[i] = P / P8 | (8 * ((P % P8) ^ ((P / P8) % P8))) << 16;
     }
 
     auto tile_of = [&](int i, int& rg, int& mtile) {
@@ -522,7 +524,7 @@ __global__ __launch_bounds__(256, MT <= 2 ? 3 : (MT <= 4 ? 2 : 1)) void mfma_lds
         const int i = s / NC, c = s - i * NC;
         int rg, mtile;
         tile_of(i, rg, mtile);
-        const int blk = min(rg * 4 + wv, NB - 1);
+        const int blk = min(rg * WPB + wv, NB - 1);
         const int m0 = mtile * ROWS;
         const uint32_t sb = lds0 + stage * STB;
         const uint4* wc = wq + ((int64_t)blk * NC + c) * 256 + lane;
@@ -535,8 +537,9 @@ __global__ __launch_bounds__(256, MT <= 2 ? 3 : (MT <= 4 ? 2 : 1)) void mfma_lds
         const _Float16* xc = x + (int64_t)m0 * K + c * SPAN;
 #pragma unroll
         for (int k = 0; k < NXW; ++k) {
-            const int rr = m0 + xrow[k] < M ? xrow[k] : M - 1 - m0;
-            lds_dma16(xc + rr * K + xcol[k], sb + WB + SB + (wv + 4 * k) * 1024);
+            const int row = xrc[k] & 0xFFFF, col = xrc[k] >> 16;
+            const int rr = m0 + row < M ? row : M - 1 - m0;
+            lds_dma16(xc + rr * K + col, sb + WB + SB + (wv + WPB * k) * 1024);
         }
     };
 
@@ -548,27 +551,31 @@ __global__ __launch_bounds__(256, MT <= 2 ? 3 : (MT <= 4 ? 2 : 1)) void mfma_lds
     const uint32_t magic = 0x64006400u;
 
     auto compute = [&](const unsigned char* s) {
-        uint4 wr[NT];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-            wr[nt] = *(const uint4*)(s + wv * 4096 + (t * 64 + 16 * nt + r) * 16);
+        const unsigned char* W = s + wv * 4096 + (t * 64 + r) * 16;  // + nt*256: slot t, row 16nt + r
         const uint16_t* S = (const uint16_t*)(s + WB + wv * GPS * 128);
         const unsigned char* X = s + WB + SB;
+        constexpr int WPG = BITS == 4 ? CPG : 2 * CPG;  // 32-bit code words per group
 #pragma unroll
         for (int g = 0; g < GPS; ++g) {
+            // only this group's words of each slot are read (fewer live registers)
+            uint32_t wg[NT][WPG];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int u = 0; u < WPG; ++u)
+                    wg[nt][u] = *(const uint32_t*)(W + nt * 256 + 4 * (g * WPG + u));
             h8 bop[NT][CPG];
             float sv[NT];
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
                 for (int jj = 0; jj < CPG; ++jj) {
-                    const int j = g * CPG + jj;
                     h2 p0, p1, p2, p3;
                     if constexpr (BITS == 4) {
-                        unpack_i4(word_of(wr[nt], j), magic, p0, p1, p2, p3);
+                        unpack_i4(wg[nt][jj], magic, p0, p1, p2, p3);
                     } else {
-                        unpack_i8(word_of(wr[nt], 2 * j), p0, p1);
-                        unpack_i8(word_of(wr[nt], 2 * j + 1), p2, p3);
+                        unpack_i8(wg[nt][2 * jj], p0, p1);
+                        unpack_i8(wg[nt][2 * jj + 1], p2, p3);
                     }
                     bop[nt][jj] = (h8){p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
                 }
@@ -622,7 +629,7 @@ __global__ __launch_bounds__(256, MT <= 2 ? 3 : (MT <= 4 ? 2 : 1)) void mfma_lds
     auto epilogue = [&](int i) {
         int rg, mtile;
         tile_of(i, rg, mtile);
-        const int blk = rg * 4 + wv;
+        const int blk = rg * WPB + wv;
         const int m0 = mtile * ROWS;
         if (blk < NB) {
 #pragma unroll
@@ -809,7 +816,7 @@ hipError_t mfma_dispatch_mt(const LogitsArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int BITS, int MT, int STAGES>
+template <int BITS, int MT, int STAGES, int WPB>
 hipError_t mfma_lds_dispatch_mt(const LogitsArgs& a, hipStream_t st) {
     const int NB = (int)((a.V + 63) / 64);
     const int NC = (int)(a.K / span_of(BITS));
@@ -819,13 +826,14 @@ hipError_t mfma_lds_dispatch_mt(const LogitsArgs& a, hipStream_t st) {
     const uint4* wq = (const uint4*)a.packed;
     const uint16_t* sc = (const uint16_t*)(a.packed + (int64_t)NB * 64 * a.K * BITS / 8);
     const int NMT = (a.M + MT * 16 - 1) / (MT * 16);
-    const int total = (NB + 3) / 4 * NMT;
+    const int total = (NB + WPB - 1) / WPB * NMT;
     // one tile per workgroup (the kernel also runs several tiles per
     // workgroup, back to back, when the grid is smaller: measured slower on
     // the 151936 x 1024 head, whose output stores then stall the next tile)
     const dim3 grid((unsigned)((total + 7) / 8 * 8));
 #define LMH_MFMA_LDS(G_)                                                                           \
-    hipLaunchKernelGGL((mfma_lds_kernel<BITS, MT, G_, STAGES>), grid, dim3(256), 0, st, wq, sc,   \
+    hipLaunchKernelGGL((mfma_lds_kernel<BITS, MT, G_, STAGES, WPB>), grid, dim3(64 * WPB), 0, st,  \
+                       wq, sc,                                                                    \
                        (const _Float16*)a.x, a.xexp, a.bias, a.y, a.ldy, (int)a.V, (int)a.K, a.M, \
                        NB, NC, NG, SPG, a.scale_bf16, NMT, total)
     if (gps == 1) LMH_MFMA_LDS(1);
@@ -838,11 +846,13 @@ hipError_t mfma_lds_dispatch_mt(const LogitsArgs& a, hipStream_t st) {
 
 template <int BITS>
 hipError_t mfma_lds_dispatch(const LogitsArgs& a, hipStream_t st) {
-    // 64-row tiles for M <= 64 (two stages, 66 KiB of LDS, two workgroups
-    // per CU), else 128-row tiles (three stages, 147 KiB, one per CU)
-    if (a.M <= 32) return mfma_lds_dispatch_mt<BITS, 2, 2>(a, st);
-    if (a.M <= 64) return mfma_lds_dispatch_mt<BITS, 4, 2>(a, st);
-    return mfma_lds_dispatch_mt<BITS, 8, 3>(a, st);
+    // 32-row tiles for M <= 32 (3 workgroups of 4 waves per CU), else 64-row
+    // tiles (2 per CU).  Measured on the 151936 x 1024 int4 head, M = 128 and
+    // 256: 128-row tiles, with one workgroup of 4 or 8 waves per CU, lose more
+    // to the waves meeting at one barrier than they gain from sharing each
+    // unpacked operand among more MFMAs.
+    if (a.M <= 32) return mfma_lds_dispatch_mt<BITS, 2, 2, 4>(a, st);
+    return mfma_lds_dispatch_mt<BITS, 4, 2, 4>(a, st);
 }
 
 template <int BITS>
