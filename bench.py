@@ -3,10 +3,12 @@
 
 One step = one pass of the per-call hot path over one batch of synthetic input
 on the 151936 x 1024 int4 g64 fp16-scale head at the decode shape: the logits
-call at M = 1 followed by top-8 exact rescoring.  The K timed steps give
-`ms_per_step`.  Each call (logits at M = 1, 32 and 256, and the rescoring) is
-then also timed on its own as K back-to-back calls between two HIP events, as
-the metric asks ("each timed separately"); those give `per_call` and `value`.
+at M = 1 and top-8 exact rescoring, in one call (lmhead_logits_topk).  The K
+timed steps give `ms_per_step`.  Each call (logits at M = 1, 32 and 256, the
+separate rescoring, the single logits + rescoring call) is then also timed
+on its own as K back-to-back
+calls between two HIP events, as the metric asks ("each timed separately");
+those give `per_call` and `value`.
 The load-time quantize and pack run once before the timed region and are
 reported separately.
 
@@ -251,6 +253,10 @@ def main() -> int:
     wss = {M: lmh.logits_workspace(M, w.K, TD[w.x_dtype], dev) for M in Ms}
     m_rs = Ms[0]
     tws = lmh.topk_workspace(m_rs, w.V, args.topk, dev)
+    fws = lmh.logits_topk_workspace(m_rs, w.V, w.K, TD[w.x_dtype], args.topk, dev)
+    t_idx = torch.empty((m_rs, args.topk), dtype=torch.int32, device=dev)
+    t_val = torch.empty((m_rs, args.topk), dtype=torch.float32, device=dev)
+    t_top1 = torch.empty((m_rs,), dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
 
     m_hd = Ms[0]  # the headline call: the decode case
@@ -262,10 +268,15 @@ def main() -> int:
     def rescore():
         lmh.topk_rescore(xs[m_rs], Wref, outs[m_rs], args.topk, workspace=tws)
 
+    def fused(i):
+        # logits (stored) and exact top-K rescoring in one call
+        lmh.logits_topk(xs[m_rs], blobs[i % R], w.V, w.K, w.bits, w.group, sdt, Wref, args.topk,
+                        out=outs[m_rs], workspace=fws, idx=t_idx, val=t_val, top1=t_top1)
+
     def step(i):
-        # one pass of the per-call hot path at the headline M: logits, then exact top-K rescoring
-        call(m_hd, i)
-        rescore()
+        # one pass of the per-call hot path at the headline M: logits, then
+        # exact top-K rescoring (one call)
+        fused(i)
 
     # ---- the timed region: K steps, synchronised on both sides ----
     for i in range(args.warmup):
@@ -308,6 +319,8 @@ def main() -> int:
         }
     rs_us = timed_loop(lambda i: rescore(), args.steps)
     per_call[f"top{args.topk}_rescore"] = {"us": round(rs_us, 3), "M": m_rs}
+    fu_us = timed_loop(fused, args.steps)
+    per_call[f"logits+top{args.topk}_one_call"] = {"us": round(fu_us, 3), "M": m_rs}
 
     m1 = per_call[f"M={Ms[0]}"]
     value = m1["us"]

@@ -224,6 +224,31 @@ int lmhead_topk_rescore(const void* x, int x_dtype, int64_t M, const void* w_ref
                         float* val_out, int32_t* top1_out, void* workspace, size_t ws_bytes,
                         void* stream);
 
+/*
+ * lmhead_logits_topk_workspace_bytes -- device workspace lmhead_logits_topk
+ *   needs (0 for invalid arguments).
+ */
+size_t lmhead_logits_topk_workspace_bytes(int64_t M, int64_t V, int64_t K, int x_dtype, int topk);
+
+/*
+ * lmhead_logits_topk -- the quantized logits and exact top-K rescoring in one
+ *   call (vLLM PR #48870, review comment, point 2: top-K of the quantized
+ *   logits, those K rows recomputed exactly from the unquantized weight).
+ *   Result: exactly that of lmhead_logits followed by lmhead_topk_rescore on
+ *   the same y -- idx_out, val_out, top1_out and, when y is given, y with the
+ *   rescored values scattered in.  y [M, ldy] fp32 may be NULL: the logits
+ *   then live in the workspace only.  Arguments otherwise as for
+ *   lmhead_logits and lmhead_topk_rescore (same shape rules, alignment,
+ *   dtypes and V <= 2097152); topk 1..64, topk <= V.
+ *   workspace: at least lmhead_logits_topk_workspace_bytes(M, V, K, x_dtype,
+ *   topk) bytes, 16-byte aligned; contents on entry do not matter.
+ */
+int lmhead_logits_topk(const void* x, int x_dtype, int64_t M, const void* packed, int64_t V,
+                       int64_t K, int bits, int64_t group, int scale_dtype, const float* bias,
+                       const void* w_ref, int w_dtype, int topk, float* y, int64_t ldy,
+                       int32_t* idx_out, float* val_out, int32_t* top1_out, void* workspace,
+                       size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -147,3 +147,44 @@ def test_dense_and_topk_validation():
     assert t(*args(wsn=8)) == E_WS
     assert t(*args(y=None)) == E_NULL
     assert t(*args(M=0)) == OK
+
+
+def _logits_topk(**kw):
+    a = dict(x=P, xd=F16, M=1, packed=P, V=128, K=128, bits=4, G=64, sd=F16, bias=None, w=P,
+             wd=F16, topk=8, y=P, ldy=128, idx=P, val=P, top1=P, ws=P, wsn=1 << 30, st=None)
+    a.update(kw)
+    return lmh.lib().lmhead_logits_topk(a["x"], a["xd"], a["M"], a["packed"], a["V"], a["K"],
+                                        a["bits"], a["G"], a["sd"], a["bias"], a["w"], a["wd"],
+                                        a["topk"], a["y"], a["ldy"], a["idx"], a["val"],
+                                        a["top1"], a["ws"], a["wsn"], a["st"])
+
+
+def test_logits_topk_validation():
+    """Every error path of the fused entry returns before any HIP call."""
+    assert _logits_topk(bits=3) == E_UNSUP
+    assert _logits_topk(K=100) == E_SHAPE
+    assert _logits_topk(xd=F32) == E_DTYPE
+    assert _logits_topk(sd=F32) == E_DTYPE
+    assert _logits_topk(wd=7) == E_DTYPE
+    assert _logits_topk(topk=0) == E_SHAPE
+    assert _logits_topk(topk=65) == E_SHAPE
+    assert _logits_topk(topk=129, V=128) == E_SHAPE
+    assert _logits_topk(M=70000) == E_SHAPE
+    assert _logits_topk(ldy=100) == E_SHAPE
+    assert _logits_topk(V=(1 << 21) + 64, ldy=(1 << 21) + 64) == E_UNSUP
+    assert _logits_topk(x=None) == E_NULL
+    assert _logits_topk(w=None) == E_NULL
+    assert _logits_topk(x=P + 8) == E_ALIGN
+    assert _logits_topk(w=P + 2) == E_ALIGN
+    assert _logits_topk(y=P + 2) == E_ALIGN
+    assert _logits_topk(ws=None) == E_WS
+    assert _logits_topk(wsn=16) == E_WS
+    assert _logits_topk(ws=P + 8) == E_ALIGN
+    assert _logits_topk(M=0) == OK
+    assert _logits_topk(V=0) == OK
+    L = lmh.lib()
+    n1 = L.lmhead_logits_topk_workspace_bytes(1, 151936, 1024, F16, 8)
+    # the top-K lists (75 blocks of 2048 entries x 9 codes) and an fp32 logits scratch
+    assert n1 >= 75 * 9 * 8 + 151936 * 4 and n1 % 256 == 0
+    assert L.lmhead_logits_topk_workspace_bytes(1, 151936, 1024, F16, 65) == 0
+    assert L.lmhead_logits_topk_workspace_bytes(1, 151936, 1024, F32, 8) == 0

@@ -1,0 +1,88 @@
+"""GPU logits + top-K rescoring in one call (lmhead_logits_topk).
+
+The single call must give exactly what the two separate calls give
+(lmhead_logits, then lmhead_topk_rescore): the same indices in the same
+order, bit-identical rescored values, top-1 and scattered logits, with or
+without the logits stored.  The selection itself is checked against the
+oracle's top-K of the GPU's own logits (reading R5)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import weight_only_quantized_lmhead_amd as lmh
+from gpu_common import DEV, OD, TD, gpu, need_gpu, to_dev
+
+pytestmark = gpu
+
+
+def _head(V, K, bits, G, seed):
+    w = synth.random_weight((V, K), 0.02, seed)
+    q, s = oracle.quantize(w, bits, G, oracle.F16)
+    blob = torch.from_numpy(oracle.pack(q, s, bits, G)).to(DEV)
+    return w, blob
+
+
+def _separate(x, blob, V, K, bits, G, wref, topk, path):
+    y = lmh.logits(x, blob, V, K, bits, G, torch.float16, path=path)
+    idx, val, top1 = lmh.topk_rescore(x, wref, y, topk)
+    return y, idx, val, top1
+
+
+@pytest.mark.parametrize("bits,G,K", [(4, 64, 1024), (4, 128, 512), (8, 128, 1024), (4, 32, 256)])
+@pytest.mark.parametrize("M", [1, 2, 5, 40])
+@pytest.mark.parametrize("topk", [1, 8, 64])
+@pytest.mark.parametrize("xdt", ["f16", "bf16"])
+def test_one_call_equals_separate_calls(bits, G, K, M, topk, xdt):
+    need_gpu()
+    V = 64 * 83 + 21  # 84 blocks, a ragged last one
+    w, blob = _head(V, K, bits, G, seed=bits * 1000 + G + K)
+    wref = torch.from_numpy(w.astype(np.float16)).to(DEV)
+    x = to_dev(synth.random_x(M, K, seed=M + topk, dtype=xdt), xdt)
+    y0, i0, v0, t0 = _separate(x, blob, V, K, bits, G, wref, topk, path=lmh.PATH_AUTO)
+    y1 = torch.full((M, V + 7), float("nan"), device=DEV)[:, :V]
+    i1, v1, t1 = lmh.logits_topk(x, blob, V, K, bits, G, torch.float16, wref, topk, out=y1)
+    i2, v2, t2 = lmh.logits_topk(x, blob, V, K, bits, G, torch.float16, wref, topk, out=None)
+    torch.cuda.synchronize()
+    for i, v, t in ((i1, v1, t1), (i2, v2, t2)):
+        assert torch.equal(i, i0), "selection differs"
+        assert torch.equal(v, v0), "rescored values differ"
+        assert torch.equal(t, t0), "top-1 differs"
+    assert torch.equal(y1, y0), "logits (with the rescored values scattered in) differ"
+
+
+def test_selection_is_the_oracle_top_k():
+    """The indices are the oracle's top-K (value descending, index ascending)
+    of the GPU's own quantized logits."""
+    need_gpu()
+    V, K, bits, G, topk = 64 * 300 + 17, 1024, 4, 64, 16
+    w, blob = _head(V, K, bits, G, seed=91)
+    wref = torch.from_numpy(w.astype(np.float16)).to(DEV)
+    x = to_dev(synth.random_x(1, K, seed=5), "f16")
+    y = lmh.logits(x, blob, V, K, bits, G, torch.float16)
+    torch.cuda.synchronize()
+    yq = y.cpu().numpy()
+    idx, _, _ = lmh.logits_topk(x, blob, V, K, bits, G, torch.float16, wref, topk)
+    torch.cuda.synchronize()
+    want = oracle.topk(yq[0], topk)
+    assert np.array_equal(idx.cpu().numpy()[0].astype(np.int64), want)
+
+
+@pytest.mark.parametrize("V", [151936, 600000])
+def test_full_size_rows_match_separate_calls(V):
+    """A 151936 x 1024 int4 g64 head at M = 1, and a 600000-row one (pass 1
+    then takes 4096-entry blocks to stay within 256 lists)."""
+    need_gpu()
+    K, bits, G = 1024, 4, 64
+    gen = torch.Generator(device=DEV).manual_seed(V)
+    Wd = torch.randn(V, K, device=DEV, generator=gen) * 0.02
+    q, s = lmh.quantize(Wd, bits, G, torch.float16, "rtn")
+    blob = lmh.pack(q, s, bits, G)
+    wref = Wd.half()
+    del q, s, Wd
+    x = to_dev(synth.random_x(1, K, seed=3), "f16")
+    y0, i0, v0, t0 = _separate(x, blob, V, K, bits, G, wref, 8, path=lmh.PATH_AUTO)
+    i1, v1, t1 = lmh.logits_topk(x, blob, V, K, bits, G, torch.float16, wref, 8)
+    torch.cuda.synchronize()
+    assert torch.equal(i1, i0) and torch.equal(v1, v0) and torch.equal(t1, t0)

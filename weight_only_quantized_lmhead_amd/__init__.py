@@ -61,6 +61,9 @@ def lib() -> ctypes.CDLL:
             "lmhead_topk_workspace_bytes": (sz, [i64, i64, i32]),
             "lmhead_topk_rescore": (i32, [vp, i32, i64, vp, i32, i64, i64, vp, i64, i32, vp, vp,
                                           vp, vp, sz, vp]),
+            "lmhead_logits_topk_workspace_bytes": (sz, [i64, i64, i64, i32, i32]),
+            "lmhead_logits_topk": (i32, [vp, i32, i64, vp, i64, i64, i32, i64, i32, vp, vp, i32, i32,
+                                         vp, i64, vp, vp, vp, vp, sz, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -177,6 +180,40 @@ def topk_rescore(x: torch.Tensor, w_ref: torch.Tensor, y: torch.Tensor, topk: in
     _check("lmhead_topk_rescore", lib().lmhead_topk_rescore(
         _ptr(x), _DT[x.dtype], M, _ptr(w_ref), _DT[w_ref.dtype], V, K, _ptr(y), y.stride(0), topk,
         _ptr(idx), _ptr(val), _ptr(top1), _ptr(workspace), workspace.numel(), _stream(x)))
+    return idx, val, top1
+
+
+def logits_topk_workspace(M: int, V: int, K: int, x_dtype: torch.dtype, topk: int,
+                          device) -> torch.Tensor:
+    n = lib().lmhead_logits_topk_workspace_bytes(M, V, K, _DT[x_dtype], topk)
+    if n == 0:
+        raise ValueError("invalid arguments for lmhead_logits_topk_workspace_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def logits_topk(x: torch.Tensor, packed: torch.Tensor, V: int, K: int, bits: int, group: int,
+                scale_dtype: torch.dtype, w_ref: torch.Tensor, topk: int,
+                bias: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None, idx: Optional[torch.Tensor] = None,
+                val: Optional[torch.Tensor] = None, top1: Optional[torch.Tensor] = None):
+    """Logits + exact top-K rescoring in one call -- lmhead_logits_topk.  ``out``
+    (fp32 [M, >= V]) receives the logits with the rescored values scattered in;
+    when None they are not stored.  Returns (idx, val, top1)."""
+    _need_cuda(x, packed, w_ref, bias)
+    M = x.shape[0]
+    if idx is None:
+        idx = torch.empty((M, topk), dtype=torch.int32, device=x.device)
+    if val is None:
+        val = torch.empty((M, topk), dtype=torch.float32, device=x.device)
+    if top1 is None:
+        top1 = torch.empty((M,), dtype=torch.int32, device=x.device)
+    if workspace is None:
+        workspace = logits_topk_workspace(M, V, K, x.dtype, topk, x.device)
+    ldy = out.stride(0) if out is not None else 0
+    _check("lmhead_logits_topk", lib().lmhead_logits_topk(
+        _ptr(x), _DT[x.dtype], M, _ptr(packed), V, K, bits, group, _DT[scale_dtype], _ptr(bias),
+        _ptr(w_ref), _DT[w_ref.dtype], topk, _ptr(out), ldy, _ptr(idx), _ptr(val), _ptr(top1),
+        _ptr(workspace), workspace.numel(), _stream(x)))
     return idx, val, top1
 
 

@@ -6,6 +6,8 @@
 #include "lmh_internal.h"
 #include "lmhead.h"
 
+#include <algorithm>
+
 namespace {
 
 using lmh::BF16;
@@ -198,6 +200,56 @@ int lmhead_topk_rescore(const void* x, int x_dtype, int64_t M, const void* w_ref
     if (!aligned16(workspace)) return LMH_E_ALIGN;
     return from_hip(lmh::launch_topk_rescore(x, x_dtype, (int)M, w_ref, w_dtype, V, K, y, ldy, topk,
                                              idx_out, val_out, top1_out, workspace,
+                                             (hipStream_t)stream));
+}
+
+static int64_t round256(int64_t n) { return (n + 255) / 256 * 256; }
+
+// Workspace of lmhead_logits_topk: [x conversion][top-K lists][fp32 logits
+// scratch, used when y is NULL]; every region rounded up to 256 bytes.
+size_t lmhead_logits_topk_workspace_bytes(int64_t M, int64_t V, int64_t K, int x_dtype, int topk) {
+    if (M <= 0 || V <= 0 || K <= 0 || topk < 1 || topk > 64) return 0;
+    if (x_dtype != F16 && x_dtype != BF16) return 0;
+    return (size_t)(round256((int64_t)lmhead_logits_workspace_bytes(M, K, x_dtype)) +
+                    round256((int64_t)lmh::topk_ws_bytes(M, V, topk)) + round256(M * V * 4));
+}
+
+int lmhead_logits_topk(const void* x, int x_dtype, int64_t M, const void* packed, int64_t V,
+                       int64_t K, int bits, int64_t group, int scale_dtype, const float* bias,
+                       const void* w_ref, int w_dtype, int topk, float* y, int64_t ldy,
+                       int32_t* idx_out, float* val_out, int32_t* top1_out, void* workspace,
+                       size_t ws_bytes, void* stream) {
+    int rc = check_layout(V, K, bits, group);
+    if (rc != LMH_OK) return rc;
+    if (x_dtype != F16 && x_dtype != BF16) return LMH_E_DTYPE;
+    if (scale_dtype != F16 && scale_dtype != BF16) return LMH_E_DTYPE;
+    if (w_dtype != F16 && w_dtype != BF16 && w_dtype != F32) return LMH_E_DTYPE;
+    if (M < 0 || M > 65535) return LMH_E_SHAPE;
+    if (topk < 1 || topk > 64) return LMH_E_SHAPE;
+    if (M == 0 || V == 0) return LMH_OK;
+    if (topk > V) return LMH_E_SHAPE;
+    if (y && ldy < V) return LMH_E_SHAPE;
+    if (V > lmh::topk_max_v()) return LMH_E_UNSUPPORTED;
+    if ((V + 255) / 256 * ((M + 15) / 16) >= (int64_t(1) << 30)) return LMH_E_UNSUPPORTED;
+    if (!x || !packed || !w_ref) return LMH_E_NULL;
+    if (!aligned16(x) || !aligned16(packed)) return LMH_E_ALIGN;
+    if (((uintptr_t)w_ref & 3u) != 0 || (y && ((uintptr_t)y & 3u) != 0) ||
+        (bias && ((uintptr_t)bias & 3u) != 0))
+        return LMH_E_ALIGN;
+    const size_t need = lmhead_logits_topk_workspace_bytes(M, V, K, x_dtype, topk);
+    if (!workspace || ws_bytes < need) return LMH_E_WORKSPACE;
+    if (!aligned16(workspace)) return LMH_E_ALIGN;
+    char* ws = (char*)workspace;
+    const int64_t xws = round256((int64_t)lmhead_logits_workspace_bytes(M, K, x_dtype));
+    const int64_t tws = round256((int64_t)lmh::topk_ws_bytes(M, V, topk));
+    float* yy = y ? y : (float*)(ws + xws + tws);
+    const int64_t ly = y ? ldy : V;
+    // the logits (automatic kernel), then the two top-K passes over them
+    rc = logits_impl(x, x_dtype, M, packed, V, K, bits, group, scale_dtype, bias, yy, ly, ws,
+                     (size_t)xws, stream, 0);
+    if (rc != LMH_OK) return rc;
+    return from_hip(lmh::launch_topk_rescore(x, x_dtype, (int)M, w_ref, w_dtype, V, K, yy, ly, topk,
+                                             idx_out, val_out, top1_out, ws + xws,
                                              (hipStream_t)stream));
 }
 

@@ -14,6 +14,26 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 
 enum Dtype { F32 = 0, F16 = 1, BF16 = 2 };
 
+typedef unsigned long long u64;
+
+// Top-K order codes: unsigned order of the code = value descending, then index
+// ascending (-0 and +0 tie; NaN ranks below every number).  High word: the
+// value's bits mapped to an order-preserving integer; low word: 0x7FFFFFFF -
+// index.  Code 0 is never a real entry's code (it marks "no list").
+__device__ __forceinline__ u64 topk_code(float v, int idx) {
+    const float f = v == 0.0f ? 0.0f : v;  // -0 -> +0
+    const int b = __float_as_int(f);
+    const int key = (f != f) ? (int)0x80000000 : (b >= 0 ? b : b ^ 0x7FFFFFFF);
+    return ((u64)((uint32_t)key ^ 0x80000000u) << 32) | (uint32_t)(0x7FFFFFFF - idx);
+}
+
+__device__ __forceinline__ int topk_code_idx(u64 c) { return 0x7FFFFFFF - (int)(uint32_t)c; }
+
+__device__ __forceinline__ float topk_code_val(u64 c) {
+    const int key = (int)((uint32_t)(c >> 32) ^ 0x80000000u);
+    return __int_as_float(key >= 0 ? key : key ^ 0x7FFFFFFF);
+}
+
 // Columns covered by one 4-slot superchunk of the packed layout.
 constexpr int span_of(int bits) { return bits == 4 ? 128 : 64; }
 

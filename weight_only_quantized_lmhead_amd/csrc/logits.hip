@@ -768,9 +768,9 @@ hipError_t gemv_dispatch_gps(const LogitsArgs& a, int gps, hipStream_t st) {
     // and the split falls on group boundaries
     auto splits = [&](int ks) { return NC % (2 * ks) == 0 && (NC / ks) % SPG == 0; };
     const int KS = splits(4) ? 4 : splits(2) ? 2 : 1;
-#define LMH_GEMV(G_, KS_)                                                                         \
-    hipLaunchKernelGGL((gemv_kernel<BITS, MM, G_, D, KS_>), dim3((NB * KS_ + 3) / 4), dim3(256),  \
-                       lds, st, wq, sc, (const h2*)a.x, a.xexp, a.bias, a.y, a.ldy, (int)a.V,     \
+#define LMH_GEMV(G_, KS_)                                                                          \
+    hipLaunchKernelGGL((gemv_kernel<BITS, MM, G_, D, KS_>), dim3((NB * KS_ + 3) / 4), dim3(256),   \
+                       lds, st, wq, sc, (const h2*)a.x, a.xexp, a.bias, a.y, a.ldy, (int)a.V,      \
                        (int)a.K, NB, NC, NG, SPG, a.scale_bf16)
 #define LMH_GEMV_KS(G_) \
     if (KS == 4) LMH_GEMV(G_, 4); else if (KS == 2) LMH_GEMV(G_, 2); else LMH_GEMV(G_, 1)

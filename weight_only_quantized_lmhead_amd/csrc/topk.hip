@@ -23,52 +23,40 @@
 // takes a threshold that at least T entries reach, keeps the few entries at or
 // above it, and places each kept entry by its rank among them.
 //
-// Pass 1 (grid: blocks of 2048 entries x rows, 256 threads, 8 entries each):
+// Pass 1 (grid: blocks of 256*kPer entries x rows, 256 threads, kPer = 8, 16
+//   or 32 entries each, so that a row has at most 256 blocks):
 //   thread maxima -> each wave's T-th largest thread maximum (rank among the
 //   wave's 64) -> threshold = the largest of those (T <= 64; for T = 65 the
 //   T-th largest of all 256 thread maxima) -> entries >= threshold into LDS
 //   -> rank among them -> the block's top T, sorted, into the workspace.
-// Pass 2 (grid: rows, 256 threads): the T-th largest list head is the
-//   threshold; only the T lists whose heads reach it can hold a top-T entry;
-//   their entries >= threshold are ranked as in pass 1.  Then the exact fp32
-//   dot products of the selected rows (all rows at once), the scatter into y,
-//   idx/val and the top-1.
+// Pass 2 (grid: rows, 256 threads, one list per thread): the T-th largest
+//   list head is the threshold; the entries at or above it of the T lists
+//   that reach it are ranked as in pass 1.  Then the exact fp32 dot products
+//   of the selected rows (all rows at once), the scatter into y, idx/val and
+//   the top-1.
 #include "lmh_internal.h"
 
-#include <limits.h>
 #include <math.h>
 
 namespace lmh {
 namespace {
 
-typedef unsigned long long u64;
-
-constexpr int kPer = 8;                // entries per thread in pass 1
-constexpr int kBlockN = 256 * kPer;    // entries per pass-1 block (2048)
 constexpr int kMaxT = 65;              // topk <= 64, plus the top-1 candidate
-constexpr int kMaxLists = 1024;        // pass-2 lists per row: V <= 2^21
+constexpr int kMaxLists = 256;         // pass-2 lists per row (one per pass-1 block)
+
+// Entries per thread in pass 1 (a block takes 256 times as many): the
+// smallest of 8, 16, 32 that keeps the row to at most kMaxLists blocks.
+inline int pass1_per(int64_t V) { return V <= 2048 * kMaxLists ? 8 : V <= 4096 * kMaxLists ? 16 : 32; }
 constexpr int kPass2Cand = kMaxT * kMaxT;
 
-__device__ __forceinline__ u64 make_code(float v, int idx) {
-    const float f = v == 0.0f ? 0.0f : v;  // -0 -> +0
-    const int b = __float_as_int(f);
-    const int key = (f != f) ? INT_MIN : (b >= 0 ? b : b ^ 0x7FFFFFFF);
-    return ((u64)((uint32_t)key ^ 0x80000000u) << 32) | (uint32_t)(0x7FFFFFFF - idx);
-}
-
-__device__ __forceinline__ int code_idx(u64 c) { return 0x7FFFFFFF - (int)(uint32_t)c; }
-
-__device__ __forceinline__ float code_val(u64 c) {
-    const int key = (int)((uint32_t)(c >> 32) ^ 0x80000000u);
-    return __int_as_float(key >= 0 ? key : key ^ 0x7FFFFFFF);
-}
-
 // Pass 1.  A position past the end of the row gets a code below every real
-// entry (high word 0, low word < 2048, distinct within the block), so a block
-// with fewer than T real entries still yields T distinct codes; they never
-// reach the final top T because T <= V.
+// entry (high word 0, low word in [1, 256*kPer], distinct within the block; 0
+// means "no list" in pass 2), so a block with fewer than T real entries still
+// yields T distinct codes; they never reach the final top T because T <= V.
+template <int kPer>
 __global__ __launch_bounds__(256) void topk_block_kernel(const float* __restrict__ y, int64_t ldy,
                                                          int64_t V, int T, u64* __restrict__ out) {
+    constexpr int kBlockN = 256 * kPer;
     __shared__ u64 tmax[256];
     __shared__ u64 wthr[4];
     __shared__ u64 cs[kBlockN];
@@ -84,7 +72,7 @@ __global__ __launch_bounds__(256) void topk_block_kernel(const float* __restrict
         const int64_t e = base + loc;
         const bool in = e < V;
         const float val = y[m * ldy + (in ? e : V - 1)];  // unconditional load, clamped
-        c[i] = in ? make_code(val, (int)e) : (u64)(kBlockN - 1 - loc);
+        c[i] = in ? topk_code(val, (int)e) : (u64)(kBlockN - loc);
         best = c[i] > best ? c[i] : best;
     }
     tmax[tid] = best;
@@ -127,34 +115,38 @@ __global__ __launch_bounds__(256) void topk_block_kernel(const float* __restrict
     for (int k = tid; k < S; k += 256) {
         const u64 me = cs[k];
         int r = 0;
+#pragma unroll 8
         for (int j = 0; j < S; ++j) r += cs[j] > me;
         if (r < T) o[r] = me;
     }
 }
 
-__device__ __forceinline__ float ld16(const uint16_t* p, int64_t i, int dt) {
+template <int DT>
+__device__ __forceinline__ float ld16(const uint16_t* p, int64_t i) {
     const uint16_t b = p[i];
-    return dt == BF16 ? __uint_as_float((uint32_t)b << 16) : (float)__builtin_bit_cast(_Float16, b);
+    return DT == BF16 ? __uint_as_float((uint32_t)b << 16) : (float)__builtin_bit_cast(_Float16, b);
 }
 
-__device__ __forceinline__ void to_f32x8(uint4 q, int dt, float* f) {
+template <int DT>
+__device__ __forceinline__ void to_f32x8(uint4 q, float* f) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const uint32_t u = j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w;
-        f[2 * j] = dt == BF16 ? __uint_as_float(u << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)u);
-        f[2 * j + 1] = dt == BF16 ? __uint_as_float(u & 0xFFFF0000u)
+        f[2 * j] = DT == BF16 ? __uint_as_float(u << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)u);
+        f[2 * j + 1] = DT == BF16 ? __uint_as_float(u & 0xFFFF0000u)
                                   : (float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16));
     }
 }
 
-__device__ __forceinline__ void load_w8(const void* w, int w_dtype, int64_t off, float* f) {
-    if (w_dtype == F32) {
+template <int WD>
+__device__ __forceinline__ void load_w8(const void* __restrict__ w, int64_t off, float* f) {
+    if constexpr (WD == F32) {
         const float4 a = *(const float4*)((const float*)w + off);
         const float4 b = *(const float4*)((const float*)w + off + 4);
         f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
         f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
     } else {
-        to_f32x8(*(const uint4*)((const uint16_t*)w + off), w_dtype, f);
+        to_f32x8<WD>(*(const uint4*)((const uint16_t*)w + off), f);
     }
 }
 
@@ -166,10 +158,12 @@ __device__ __forceinline__ void load_w8(const void* w, int w_dtype, int64_t off,
 // aligned rows), else one column at a time, strided by the group; its partial
 // sum is sequential and the group's partials meet in a fixed xor-shuffle tree,
 // so the result does not depend on timing.  An index outside [0, V) is never
-// dereferenced.
-__device__ void rescore_rows(const int* idx, int topk, int64_t m, int64_t V, const void* __restrict__ x,
-                             int x_dtype, const void* __restrict__ w, int w_dtype, int64_t K, int vec,
-                             float* rv) {
+// dereferenced.  XD / WD are the dtypes of x and of the reference weight.
+template <int XD, int WD>
+__device__ __forceinline__ void rescore_rows_t(const int* idx, int topk, int64_t m, int64_t V,
+                                               const void* __restrict__ x,
+                                               const void* __restrict__ w, int64_t K, int vec,
+                                               float* rv) {
     int P = 4;
     while (P < topk) P *= 2;
     const int G = 256 / P;  // 64, 32, 16, 8 or 4
@@ -183,17 +177,16 @@ __device__ void rescore_rows(const int* idx, int topk, int64_t m, int64_t V, con
 #pragma unroll 4
         for (int64_t k = 8 * sub; k < kend; k += 8 * G) {
             float xf[8], wf[8];
-            to_f32x8(*(const uint4*)((const uint16_t*)x + m * K + k), x_dtype, xf);
-            load_w8(w, w_dtype, v * K + k, wf);
+            to_f32x8<XD>(*(const uint4*)((const uint16_t*)x + m * K + k), xf);
+            load_w8<WD>(w, v * K + k, wf);
 #pragma unroll
             for (int q = 0; q < 8; ++q) acc = fmaf(xf[q], wf[q], acc);
         }
     } else {
 #pragma unroll 4
         for (int64_t k = sub; k < kend; k += G) {
-            const float xv = ld16((const uint16_t*)x, m * K + k, x_dtype);
-            const float wv = w_dtype == F32 ? ((const float*)w)[v * K + k]
-                                            : ld16((const uint16_t*)w, v * K + k, w_dtype);
+            const float xv = ld16<XD>((const uint16_t*)x, m * K + k);
+            const float wv = WD == F32 ? ((const float*)w)[v * K + k] : ld16<WD>((const uint16_t*)w, v * K + k);
             acc = fmaf(xv, wv, acc);
         }
     }
@@ -201,95 +194,165 @@ __device__ void rescore_rows(const int* idx, int topk, int64_t m, int64_t V, con
     if (t < topk && sub == 0) rv[t] = on ? acc : NAN;
 }
 
-// Pass 2: one workgroup per row over the C sorted lists of T codes that
-// pass 1 wrote; then rescoring, scatter, idx/val and top-1.
-__global__ __launch_bounds__(256) void topk_select_rescore_kernel(
-    const u64* __restrict__ lists, int C, int T, int topk, const void* __restrict__ x, int x_dtype,
-    const void* __restrict__ w, int w_dtype, int64_t V, int64_t K, int vec, float* __restrict__ y,
-    int64_t ldy, int32_t* __restrict__ idx_out, float* __restrict__ val_out,
-    int32_t* __restrict__ top1_out) {
-    __shared__ u64 heads[kMaxLists];
-    __shared__ u64 cs[kPass2Cand];
-    __shared__ int qual[kMaxT];
-    __shared__ u64 sel[kMaxT];
-    __shared__ int ti[kMaxT];
-    __shared__ float rv[64];
-    __shared__ u64 thr_s;
-    __shared__ int nq, cnt;
-    const int tid = threadIdx.x;
-    const int64_t m = blockIdx.x;
-    const u64* L = lists + m * (int64_t)C * T;
-    for (int l = tid; l < C; l += 256) heads[l] = L[(int64_t)l * T];
-    if (tid == 0) {
-        nq = 0;
-        cnt = 0;
-        thr_s = 0;  // C < T: every entry of every list
+__device__ __forceinline__ void rescore_rows(const int* idx, int topk, int64_t m, int64_t V,
+                                             const void* __restrict__ x, int x_dtype,
+                                             const void* __restrict__ w, int w_dtype, int64_t K,
+                                             int vec, float* rv) {
+    if (x_dtype == BF16) {
+        if (w_dtype == BF16) rescore_rows_t<BF16, BF16>(idx, topk, m, V, x, w, K, vec, rv);
+        else if (w_dtype == F32) rescore_rows_t<BF16, F32>(idx, topk, m, V, x, w, K, vec, rv);
+        else rescore_rows_t<BF16, F16>(idx, topk, m, V, x, w, K, vec, rv);
+    } else {
+        if (w_dtype == BF16) rescore_rows_t<F16, BF16>(idx, topk, m, V, x, w, K, vec, rv);
+        else if (w_dtype == F32) rescore_rows_t<F16, F32>(idx, topk, m, V, x, w, K, vec, rv);
+        else rescore_rows_t<F16, F16>(idx, topk, m, V, x, w, K, vec, rv);
     }
-    __syncthreads();
-    // threshold: the T-th largest head (then exactly T lists reach it)
-    if (C >= T) {
-        for (int l = tid; l < C; l += 256) {
-            const u64 h = heads[l];
-            int r = 0;
-            for (int j = 0; j < C; ++j) r += heads[j] > h;
-            if (r == T - 1) thr_s = h;
+}
+
+// Workgroup barrier for kernels whose threads share data only through LDS:
+// waits for this thread's LDS operations, not for its global loads (a
+// __syncthreads() fence would also wait for global loads still in flight).
+// The empty asm statements keep the compiler from moving memory accesses
+// across it.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+struct SelectShared {
+    u64 heads[256];
+    int qual[kMaxT];
+    u64 cs[kPass2Cand];
+    u64 sel[kMaxT];
+    int ti[kMaxT];
+    float rv[64];
+    u64 thr;
+    int nq, cnt;
+};
+
+// The top T of C <= 256 sorted lists of T codes (code 0: none) into sh.sel,
+// sorted: the T-th largest head is the threshold (then exactly T lists reach
+// it; all lists when C < T), and the entries of those lists at or above it
+// (at most T*T) are placed by rank.  Thread i owns list i; with T <= 16 it
+// loads the whole list at once, so the candidates come from its registers
+// (one round trip to memory instead of two).  Ends with a barrier.
+__device__ __forceinline__ void select_lists(const u64* __restrict__ L, int C, int T,
+                                             SelectShared& sh) {
+    constexpr int kRegT = 16;
+    const int tid = threadIdx.x;
+    const bool own = tid < C;
+    const int64_t lb = (int64_t)(own ? tid : C - 1) * T;  // clamped: loads are unconditional
+    u64 e[kRegT];
+    const bool inreg = T <= kRegT;
+    if (inreg) {
+#pragma unroll
+        for (int i = 0; i < kRegT; ++i) e[i] = L[lb + (i < T ? i : 0)];
+    } else {
+        e[0] = L[lb];
+    }
+    const u64 h = e[0];
+    sh.heads[tid] = own ? h : 0;
+    if (tid == 0) {
+        sh.nq = sh.cnt = 0;
+        sh.thr = 0;
+    }
+    lds_barrier();
+    if (own && C >= T) {
+        int r = 0;
+#pragma unroll 8
+        for (int j = 0; j < C; ++j) r += sh.heads[j] > h;
+        if (r == T - 1) sh.thr = h;
+    }
+    lds_barrier();
+    const u64 thr = sh.thr;
+    if (inreg) {
+        if (own && h >= thr) {
+#pragma unroll
+            for (int i = 0; i < kRegT; ++i)
+                if (i < T && e[i] != 0 && e[i] >= thr) sh.cs[atomicAdd(&sh.cnt, 1)] = e[i];
+        }
+    } else {
+        if (own && h >= thr) sh.qual[atomicAdd(&sh.nq, 1)] = tid;
+        lds_barrier();
+        const int ne = sh.nq * T;  // at most T*T entries
+        for (int q = tid; q < ne; q += 256) {
+            const int l = sh.qual[q / T];
+            const u64 c = L[(int64_t)l * T + q % T];
+            if (c != 0 && c >= thr) sh.cs[atomicAdd(&sh.cnt, 1)] = c;
         }
     }
-    __syncthreads();
-    const u64 thr = thr_s;
-    for (int l = tid; l < C; l += 256)
-        if (heads[l] >= thr) qual[atomicAdd(&nq, 1)] = l;
-    __syncthreads();
-    // entries >= thr of the qualifying lists (at most T*T)
-    const int ne = nq * T;
-    for (int e = tid; e < ne; e += 256) {
-        const int l = qual[e / T];
-        const u64 c = L[(int64_t)l * T + e % T];
-        if (c >= thr) cs[atomicAdd(&cnt, 1)] = c;
-    }
-    __syncthreads();
-    const int S = cnt;  // T <= S <= T*T
+    lds_barrier();
+    const int S = sh.cnt;  // T <= S <= T*T
     for (int k = tid; k < S; k += 256) {
-        const u64 me = cs[k];
+        const u64 me = sh.cs[k];
         int r = 0;
-        for (int j = 0; j < S; ++j) r += cs[j] > me;
-        if (r < T) sel[r] = me;
+#pragma unroll 8
+        for (int j = 0; j < S; ++j) r += sh.cs[j] > me;
+        if (r < T) sh.sel[r] = me;
     }
-    __syncthreads();
-    if (tid < T) ti[tid] = code_idx(sel[tid]);
-    __syncthreads();
-    rescore_rows(ti, topk, m, V, x, x_dtype, w, w_dtype, K, vec, rv);
-    __syncthreads();
+    lds_barrier();
+}
+
+// Rescore the selected rows, scatter into y (if given), write idx/val and
+// the top-1: the first maximum among the rescored values and the (K+1)-th
+// candidate, compared as floats (value descending, then index ascending).
+__device__ __forceinline__ void finish_row(SelectShared& sh, int T, int topk, int64_t m, int64_t V,
+                                           const void* __restrict__ x, int x_dtype,
+                                           const void* __restrict__ w, int w_dtype, int64_t K,
+                                           int vec, float* __restrict__ y, int64_t ldy,
+                                           int32_t* __restrict__ idx_out,
+                                           float* __restrict__ val_out,
+                                           int32_t* __restrict__ top1_out) {
+    const int tid = threadIdx.x;
+    if (tid < T) sh.ti[tid] = topk_code_idx(sh.sel[tid]);
+    lds_barrier();
+    rescore_rows(sh.ti, topk, m, V, x, x_dtype, w, w_dtype, K, vec, sh.rv);
+    lds_barrier();
     if (tid < topk) {
-        if (ti[tid] >= 0 && ti[tid] < V) y[m * ldy + ti[tid]] = rv[tid];
-        if (idx_out) idx_out[m * topk + tid] = ti[tid];
-        if (val_out) val_out[m * topk + tid] = rv[tid];
+        const int v = sh.ti[tid];
+        if (y && v >= 0 && v < V) y[m * ldy + v] = sh.rv[tid];
+        if (idx_out) idx_out[m * topk + tid] = v;
+        if (val_out) val_out[m * topk + tid] = sh.rv[tid];
     }
     if (tid == 0 && top1_out) {
-        // first maximum among the rescored values and the (K+1)-th candidate,
-        // compared as floats (value descending, then index ascending)
-        float bv = rv[0];
-        int bi = ti[0];
+        float bv = sh.rv[0];
+        int bi = sh.ti[0];
         for (int t = 1; t < topk; ++t)
-            if ((rv[t] > bv) | ((rv[t] == bv) & (ti[t] < bi))) {
-                bv = rv[t];
-                bi = ti[t];
+            if ((sh.rv[t] > bv) | ((sh.rv[t] == bv) & (sh.ti[t] < bi))) {
+                bv = sh.rv[t];
+                bi = sh.ti[t];
             }
         if (T > topk) {
-            const float cv = code_val(sel[topk]);
-            const int ci = ti[topk];
+            const float cv = topk_code_val(sh.sel[topk]);
+            const int ci = sh.ti[topk];
             if ((cv > bv) | ((cv == bv) & (ci < bi))) bi = ci;
         }
         top1_out[m] = bi;
     }
 }
 
+// Pass 2: one workgroup per row over the C <= 256 lists of pass 1.
+__global__ __launch_bounds__(256) void topk_select_rescore_kernel(
+    const u64* __restrict__ lists, int C, int T, int topk, const void* __restrict__ x, int x_dtype,
+    const void* __restrict__ w, int w_dtype, int64_t V, int64_t K, int vec, float* __restrict__ y,
+    int64_t ldy, int32_t* __restrict__ idx_out, float* __restrict__ val_out,
+    int32_t* __restrict__ top1_out) {
+    __shared__ SelectShared sh;
+    const int64_t m = blockIdx.x;
+    select_lists(lists + m * (int64_t)C * T, C, T, sh);
+    finish_row(sh, T, topk, m, V, x, x_dtype, w, w_dtype, K, vec, y, ldy, idx_out, val_out,
+               top1_out);
+}
+
 }  // namespace
 
-int64_t topk_max_v() { return (int64_t)kBlockN * kMaxLists; }
+int64_t topk_max_v() { return (int64_t)256 * 32 * kMaxLists; }
 
 size_t topk_ws_bytes(int64_t M, int64_t V, int topk) {
-    const int64_t C = (V + kBlockN - 1) / kBlockN;
+    const int64_t bn = 256 * pass1_per(V);
+    const int64_t C = (V + bn - 1) / bn;
     const int64_t T = topk + 1;
     return (size_t)(M * C * T * 8 + 256);
 }
@@ -298,10 +361,17 @@ hipError_t launch_topk_rescore(const void* x, int x_dtype, int M, const void* w,
                                int64_t V, int64_t K, float* y, int64_t ldy, int topk,
                                int32_t* idx, float* val, int32_t* top1, void* ws,
                                hipStream_t st) {
-    const int C = (int)((V + kBlockN - 1) / kBlockN);
+    const int per = pass1_per(V);
+    const int C = (int)((V + 256 * per - 1) / (256 * per));
+    if (C > kMaxLists) return hipErrorInvalidValue;  // V <= topk_max_v(), checked by the API
     const int T = (int)(topk + 1 <= V ? topk + 1 : V);
     u64* lists = (u64*)ws;
-    hipLaunchKernelGGL(topk_block_kernel, dim3(C, M), dim3(256), 0, st, y, ldy, V, T, lists);
+    if (per == 8)
+        hipLaunchKernelGGL(topk_block_kernel<8>, dim3(C, M), dim3(256), 0, st, y, ldy, V, T, lists);
+    else if (per == 16)
+        hipLaunchKernelGGL(topk_block_kernel<16>, dim3(C, M), dim3(256), 0, st, y, ldy, V, T, lists);
+    else
+        hipLaunchKernelGGL(topk_block_kernel<32>, dim3(C, M), dim3(256), 0, st, y, ldy, V, T, lists);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int esz = w_dtype == F32 ? 4 : 2;
