@@ -268,7 +268,7 @@ def main() -> int:
     def rescore():
         lmh.topk_rescore(xs[m_rs], Wref, outs[m_rs], args.topk, workspace=tws)
 
-    def fused(i):
+    def one_call(i):
         # logits (stored) and exact top-K rescoring in one call
         lmh.logits_topk(xs[m_rs], blobs[i % R], w.V, w.K, w.bits, w.group, sdt, Wref, args.topk,
                         out=outs[m_rs], workspace=fws, idx=t_idx, val=t_val, top1=t_top1)
@@ -276,7 +276,7 @@ def main() -> int:
     def step(i):
         # one pass of the per-call hot path at the headline M: logits, then
         # exact top-K rescoring (one call)
-        fused(i)
+        one_call(i)
 
     # ---- the timed region: K steps, synchronised on both sides ----
     for i in range(args.warmup):
@@ -319,7 +319,7 @@ def main() -> int:
         }
     rs_us = timed_loop(lambda i: rescore(), args.steps)
     per_call[f"top{args.topk}_rescore"] = {"us": round(rs_us, 3), "M": m_rs}
-    fu_us = timed_loop(fused, args.steps)
+    fu_us = timed_loop(one_call, args.steps)
     per_call[f"logits+top{args.topk}_one_call"] = {"us": round(fu_us, 3), "M": m_rs}
 
     m1 = per_call[f"M={Ms[0]}"]
