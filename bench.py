@@ -238,6 +238,18 @@ def main() -> int:
     torch.cuda.synchronize()
     quant_ms, pack_ms = e0.elapsed_time(e1), e1.elapsed_time(e2)
     del q, s
+    # the fused quantize + pack writes the same blob with no int8 copy of the codes
+    fused = lmh.quantize_pack(Wd, w.bits, w.group, sdt, w.clip)
+    torch.cuda.synchronize()
+    e0.record()
+    lmh.quantize_pack(Wd, w.bits, w.group, sdt, w.clip, out=fused)
+    e1.record()
+    torch.cuda.synchronize()
+    qp_ms = e0.elapsed_time(e1)
+    if not torch.equal(fused, blob):
+        print("bench.py: fused quantize+pack blob differs from pack(quantize(w))", file=sys.stderr)
+        return 1
+    del fused
 
     # unquantized 16-bit reference rows for rescoring
     if w.w_dtype == "f32":
@@ -369,6 +381,7 @@ def main() -> int:
                    "rotating_copies": R, "cache": "hot" if args.hot else "cold"},
         "per_call": per_call,
         "load_time": {"quantize_ms": round(quant_ms, 3), "pack_ms": round(pack_ms, 3),
+                      "quantize_pack_ms": round(qp_ms, 3),
                       "clip": w.clip},
         "roofline": roofline,
         "cpu_baseline": cpu,

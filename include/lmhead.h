@@ -134,6 +134,33 @@ int lmhead_pack(const int8_t* q, const void* s, int64_t V, int64_t K, int bits, 
                 void* packed_out, void* stream);
 
 /*
+ * lmhead_quantize_pack -- the quantizer and the packer fused: rows
+ *   [row0, row0 + rows) of a V x K head go straight from the unquantized
+ *   weight into their place in the packed blob, with no int8 copy of the
+ *   codes in between.  Page "radiance_lmhead_int4.py" quantizes the head in
+ *   row chunks at load time to bound the transient memory (module constant
+ *   CHUNK_ROWS; RadianceLMHeadInt4.process_weights_after_loading); the same
+ *   page's quantize_int4_rows defines the arithmetic, which is exactly that
+ *   of lmhead_quantize above.
+ *   Calling it over chunks that cover [0, V) in any order writes the same
+ *   bytes as lmhead_pack(lmhead_quantize(w)) for the whole head.
+ *   w          rows row0 .. row0+rows-1 of the head, row-major with row stride
+ *              ldw elements (ldw >= K, ldw % 8 == 0), w_dtype LMH_F32 /
+ *              LMH_F16 / LMH_BF16.  w[0] is row row0.
+ *   row0       multiple of 64; rows >= 0; row0 + rows <= V; rows is a
+ *              multiple of 64 unless row0 + rows == V (the last chunk, which
+ *              also writes the zero padding rows of the final block).
+ *   packed_out the whole blob of the V x K head (lmhead_packed_bytes); only
+ *              the blocks of this chunk are written, other bytes are left
+ *              as they are.
+ *   clip, scale_dtype, bits, group as for lmhead_quantize; layout rules as
+ *   for lmhead_pack.  rows == 0 is a valid empty call.  Deterministic.
+ */
+int lmhead_quantize_pack(const void* w, int w_dtype, int64_t ldw, int64_t V, int64_t K, int bits,
+                         int64_t group, int scale_dtype, int clip, int64_t row0, int64_t rows,
+                         void* packed_out, void* stream);
+
+/*
  * lmhead_logits_workspace_bytes -- device workspace that lmhead_logits needs
  *   for M rows of x: 0 for fp16 x; for bf16 x, room for x converted to fp16
  *   with a per-row power-of-two scale (M*K*2 and M*4 bytes, each rounded up

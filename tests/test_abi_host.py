@@ -123,6 +123,34 @@ def test_quantize_pack_validation():
     assert pk(P, P, 0, 128, 4, 64, P, None) == OK
 
 
+def test_fused_quantize_pack_validation():
+    L = lmh.lib()
+
+    def qp(w=P, wdt=F32, ldw=128, V=200, K=128, bits=4, G=64, sdt=F16, clip=0, row0=0, rows=200,
+           out=P):
+        return L.lmhead_quantize_pack(w, wdt, ldw, V, K, bits, G, sdt, clip, row0, rows, out, None)
+
+    assert qp(bits=5) == E_UNSUP
+    assert qp(K=100) == E_SHAPE
+    assert qp(G=48) == E_SHAPE
+    assert qp(wdt=7) == E_DTYPE
+    assert qp(sdt=F32) == E_DTYPE
+    assert qp(clip=2) == E_UNSUP
+    assert qp(row0=32, rows=64) == E_SHAPE            # chunks start on a 64-row block
+    assert qp(row0=64, rows=100) == E_SHAPE           # a chunk that is not last: whole blocks
+    assert qp(row0=128, rows=100) == E_SHAPE          # past V
+    assert qp(row0=-64, rows=64) == E_SHAPE
+    assert qp(rows=-1) == E_SHAPE
+    assert qp(ldw=120) == E_SHAPE                     # ldw < K
+    assert qp(ldw=132) == E_SHAPE                     # rows must stay 16-byte aligned
+    assert qp(w=None) == E_NULL
+    assert qp(out=None) == E_NULL
+    assert qp(w=P + 8) == E_ALIGN
+    assert qp(out=P + 4) == E_ALIGN
+    assert qp(w=None, rows=0, row0=64) == OK          # empty chunk: nothing launched
+    assert qp(V=0, rows=0) == OK
+
+
 def test_dense_and_topk_validation():
     L = lmh.lib()
     d = L.lmhead_dense_logits

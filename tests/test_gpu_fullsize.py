@@ -76,6 +76,21 @@ def test_fullsize_quantize_and_pack_sampled(built):
         assert np.array_equal(sc, ob[owreg:]), f"block {b} scales"
 
 
+def test_fullsize_fused_quantize_pack(built):
+    """The fused quantize + pack kernel writes exactly the two-step blob at full
+    size, in one call and in 8192-row chunks (the blob the sampled rows above
+    pin to the oracle)."""
+    w, W, Wd, q, s, blob = built
+    fused = lmh.quantize_pack(Wd, w.bits, w.group, TD[w.scale_dtype], w.clip)
+    assert torch.equal(fused, blob), "fused blob differs from pack(quantize(w))"
+    fused.fill_(0x5A)
+    for r0 in range(0, w.V, 8192):
+        lmh.quantize_pack(Wd[r0:r0 + 8192], w.bits, w.group, TD[w.scale_dtype], w.clip, V=w.V,
+                          row0=r0, out=fused)
+    assert torch.equal(fused, blob), "chunked fused blob differs"
+    del fused
+
+
 def test_fullsize_logits_sampled(built):
     w, W, Wd, q, s, blob = built
     rows = _sample_rows(w, 256, seed=w.wid + 1)

@@ -7,8 +7,7 @@ memory and the current stream.  There is no CPU fallback: if the library is
 missing or fails to load, importing the binding's functions raises.
 
     import weight_only_quantized_lmhead_amd as lmh
-    q, s = lmh.quantize(w, bits=4, group=64, scale_dtype=torch.float16, clip="rtn")
-    packed = lmh.pack(q, s, bits=4, group=64)
+    packed = lmh.quantize_pack(w, bits=4, group=64, scale_dtype=torch.float16, clip="rtn")
     y = lmh.logits(x, packed, V, K, bits=4, group=64, scale_dtype=torch.float16)
     idx, val, top1 = lmh.topk_rescore(x, w_ref, y, topk=8)
 """
@@ -52,6 +51,8 @@ def lib() -> ctypes.CDLL:
             "lmhead_packed_bytes": (sz, [i64, i64, i32, i64]),
             "lmhead_quantize": (i32, [vp, i32, i64, i64, i32, i64, i32, i32, vp, vp, vp]),
             "lmhead_pack": (i32, [vp, vp, i64, i64, i32, i64, vp, vp]),
+            "lmhead_quantize_pack": (i32, [vp, i32, i64, i64, i64, i32, i64, i32, i32, i64, i64,
+                                           vp, vp]),
             "lmhead_logits_workspace_bytes": (sz, [i64, i64, i32]),
             "lmhead_logits": (i32, [vp, i32, i64, vp, i64, i64, i32, i64, i32, vp, vp, i64, vp,
                                     sz, vp]),
@@ -121,6 +122,53 @@ def pack(q: torch.Tensor, s: torch.Tensor, bits: int, group: int) -> torch.Tenso
     out = torch.empty(packed_bytes(V, K, bits, group), dtype=torch.uint8, device=q.device)
     _check("lmhead_pack", lib().lmhead_pack(_ptr(q), _ptr(s), V, K, bits, group, _ptr(out),
                                             _stream(q)))
+    return out
+
+
+def quantize_pack(w: torch.Tensor, bits: int, group: int,
+                  scale_dtype: torch.dtype = torch.float16, clip: str = "rtn", *,
+                  V: Optional[int] = None, row0: int = 0,
+                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Packed blob straight from the unquantized weight -- lmhead_quantize_pack.
+
+    ``w`` holds rows ``[row0, row0 + w.shape[0])`` of a ``V``-row head (``V``
+    defaults to ``row0 + w.shape[0]``); its rows may be strided (unit column
+    stride).  ``out`` is the whole head's blob, allocated when None; only this
+    chunk's 64-row blocks are written."""
+    if not w.is_cuda or w.dim() != 2 or w.stride(1) != 1:
+        raise ValueError("w must be a 2-D GPU tensor with unit column stride")
+    rows, K = w.shape
+    V = row0 + rows if V is None else V
+    n = packed_bytes(V, K, bits, group)
+    if out is None:
+        out = torch.empty(n, dtype=torch.uint8, device=w.device)
+    elif not out.is_cuda or not out.is_contiguous() or out.numel() * out.element_size() < n:
+        raise ValueError(f"out must be a contiguous GPU buffer of at least {n} bytes")
+    _check("lmhead_quantize_pack", lib().lmhead_quantize_pack(
+        _ptr(w), _DT[w.dtype], w.stride(0), V, K, bits, group, _DT[scale_dtype], _CLIP[clip], row0,
+        rows, _ptr(out), _stream(w)))
+    return out
+
+
+def quantize_pack_host(w: torch.Tensor, bits: int, group: int,
+                       scale_dtype: torch.dtype = torch.float16, clip: str = "rtn", *,
+                       chunk_rows: int = 8192, device="cuda") -> torch.Tensor:
+    """Quantize a head held in host memory chunk by chunk into a device blob.
+
+    Each chunk of ``chunk_rows`` rows (a multiple of 64) is copied into one
+    device staging buffer and handed to lmhead_quantize_pack, so the device
+    holds the blob plus one chunk, never the whole unquantized head."""
+    if w.is_cuda or w.dim() != 2:
+        raise ValueError("w must be a 2-D host tensor")
+    if chunk_rows <= 0 or chunk_rows % 64 != 0:
+        raise ValueError("chunk_rows must be a positive multiple of 64")
+    V, K = w.shape
+    out = torch.empty(packed_bytes(V, K, bits, group), dtype=torch.uint8, device=device)
+    stage = torch.empty((min(chunk_rows, max(V, 1)), K), dtype=w.dtype, device=device)
+    for r0 in range(0, V, chunk_rows):
+        n = min(chunk_rows, V - r0)
+        stage[:n].copy_(w[r0:r0 + n])  # same stream as the kernel: ordered
+        quantize_pack(stage[:n], bits, group, scale_dtype, clip, V=V, row0=r0, out=out)
     return out
 
 
@@ -224,8 +272,7 @@ class QuantizedHead:
                  scale_dtype: torch.dtype = torch.float16, clip: str = "rtn"):
         self.V, self.K = w.shape
         self.bits, self.group, self.scale_dtype = bits, group, scale_dtype
-        q, s = quantize(w, bits, group, scale_dtype, clip)
-        self.packed = pack(q, s, bits, group)
+        self.packed = quantize_pack(w, bits, group, scale_dtype, clip)
 
     def __call__(self, x: torch.Tensor, bias: Optional[torch.Tensor] = None,
                  out: Optional[torch.Tensor] = None) -> torch.Tensor:

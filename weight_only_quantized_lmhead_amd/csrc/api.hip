@@ -75,6 +75,28 @@ int lmhead_quantize(const void* w, int w_dtype, int64_t V, int64_t K, int bits, 
                                          (hipStream_t)stream));
 }
 
+int lmhead_quantize_pack(const void* w, int w_dtype, int64_t ldw, int64_t V, int64_t K, int bits,
+                         int64_t group, int scale_dtype, int clip, int64_t row0, int64_t rows,
+                         void* packed_out, void* stream) {
+    const int rc = check_layout(V, K, bits, group);
+    if (rc != LMH_OK) return rc;
+    if (w_dtype != F32 && w_dtype != F16 && w_dtype != BF16) return LMH_E_DTYPE;
+    if (scale_dtype != F16 && scale_dtype != BF16) return LMH_E_DTYPE;
+    if (clip != LMH_CLIP_RTN && clip != LMH_CLIP_MSE) return LMH_E_UNSUPPORTED;
+    if (row0 < 0 || rows < 0 || row0 > V || rows > V - row0 || row0 % 64 != 0) return LMH_E_SHAPE;
+    if (rows % 64 != 0 && row0 + rows != V) return LMH_E_SHAPE;
+    if (ldw < K || ldw % 8 != 0) return LMH_E_SHAPE;
+    if (rows == 0) return LMH_OK;
+    if (!w || !packed_out) return LMH_E_NULL;
+    if (!aligned16(w) || !aligned16(packed_out)) return LMH_E_ALIGN;
+    // one wavefront per (64-row block, superchunk or group), four per workgroup
+    const int64_t units = (rows + 63) / 64 * (K / std::max<int64_t>(group, lmh::span_of(bits)));
+    if ((units + 3) / 4 >= (int64_t(1) << 31)) return LMH_E_UNSUPPORTED;
+    return from_hip(lmh::launch_quantize_pack(w, w_dtype, ldw, V, K, bits, group, scale_dtype,
+                                              clip == LMH_CLIP_MSE ? 5 : 1, row0, rows,
+                                              (uint8_t*)packed_out, (hipStream_t)stream));
+}
+
 int lmhead_pack(const int8_t* q, const void* s, int64_t V, int64_t K, int bits, int64_t group,
                 void* packed_out, void* stream) {
     const int rc = check_layout(V, K, bits, group);

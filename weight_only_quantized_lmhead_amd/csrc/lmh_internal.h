@@ -41,6 +41,11 @@ constexpr int span_of(int bits) { return bits == 4 ? 128 : 64; }
 // launch; arguments are already validated by the API layer.
 hipError_t launch_quantize(const void* w, int w_dtype, int64_t V, int64_t K, int bits, int64_t G,
                            int scale_dtype, int nratios, int8_t* q, uint16_t* s, hipStream_t st);
+// Fused quantize + pack of rows [row0, row0 + rows) (w points at row row0,
+// row stride ldw elements) straight into the blob of a V-row head.
+hipError_t launch_quantize_pack(const void* w, int w_dtype, int64_t ldw, int64_t V, int64_t K,
+                                int bits, int64_t G, int scale_dtype, int nratios, int64_t row0,
+                                int64_t rows, uint8_t* blob, hipStream_t st);
 hipError_t launch_pack(const int8_t* q, const uint16_t* s, int64_t V, int64_t K, int bits,
                        int64_t G, uint8_t* out, hipStream_t st);
 

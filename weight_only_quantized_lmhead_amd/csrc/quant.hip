@@ -2,17 +2,36 @@
 //
 // Quantizer: page "radiance_lmhead_int4.py" (docstring "How" paragraph,
 // module constants CLIP_RATIOS / QMAX / ZP_BIAS, quantize_int4_rows): per group
-// of G columns one 16-bit scale, symmetric codes, scale rounded to the 16-bit
-// type before the codes are chosen, optional least-squared-error search over
-// the clip ratios 1.0 .. 0.8.  The results are bit-exact with a plain CPU
-// implementation: IEEE-rounded fp32 division, ties-to-even everywhere, and the
-// squared error summed in fp64 in ascending column order with one fused
-// multiply-add per element.
+// of G columns one 16-bit scale, symmetric codes, the scale rounded to the
+// 16-bit type before the codes are chosen, and an optional least-squared-error
+// search over the clip ratios 1.0 .. 0.8.  Results are bit-exact with a plain
+// CPU implementation: IEEE-rounded fp32 quotients, ties-to-even everywhere,
+// and the squared error summed in fp64 in ascending column order with one
+// fused multiply-add per element.
 //
-// Packer: writes the blob layout documented in include/lmhead.h.
+// Work mapping.  One wavefront owns one 64-row block of the head and one unit
+// of columns; lane r owns row 64b + r.  A group of up to 128 columns stays in
+// the lane's registers for every pass (amax, each clip ratio, the final
+// codes); a longer group is streamed from memory once per pass.  Two outputs:
+//   * codes mode: q int8 [V, K] and s [V, K/G] row-major (lmhead_quantize);
+//   * packed mode: the blob itself (lmhead_quantize_pack).  The unit is one
+//     superchunk of the packed layout (or one group, when a group is longer),
+//     so a lane assembles its row's four 16-byte slots in registers and the 64
+//     lanes store each slot as one contiguous 1 KiB run; no int8 copy of the
+//     codes ever reaches memory.  A launch may cover any run of whole 64-row
+//     blocks, which is what lets a caller quantize a head chunk by chunk.
 //
-// Both kernels are load-time work (run once per head), VALU-bound rather than
-// HBM-bound; they favour simple, obviously-exact code over speed.
+// Quotient rounding.  q = rint(fl32(w / s)) needs the correctly rounded
+// quotient only next to a half-integer.  With rinv = fl32(1 / s) (correctly
+// rounded, once per group and ratio) and t = fl32(w * rinv), t and fl32(w / s)
+// differ by at most 3 * 2^-24 * |w / s| (three roundings of relative size
+// 2^-24, all results normal).  |w / s| <= qmax / 0.8 * (1 + 2^-8) (the
+// smallest clip ratio, and the scale's own 16-bit rounding), so the gap is
+// below 1.6e-6 for int4 and 2.9e-5 for int8.  When t is farther than 2^-17
+// (int4) or 2^-14 (int8) from every half-integer, t and the exact quotient lie
+// strictly between the same two half-integers and round to the same integer;
+// only the remaining elements (about 1e-5 resp. 1e-4 of them) take the IEEE
+// division.
 #include "lmh_internal.h"
 
 #include <math.h>
@@ -35,69 +54,400 @@ __device__ __forceinline__ float f16_to_f32(uint16_t b) {
     return (float)__builtin_bit_cast(_Float16, b);
 }
 
-template <int WDT>
-__device__ __forceinline__ float load_w(const void* w, int64_t i) {
-    if constexpr (WDT == F32) return ((const float*)w)[i];
-    else if constexpr (WDT == F16) return f16_to_f32(((const uint16_t*)w)[i]);
-    else return bf16_to_f32(((const uint16_t*)w)[i]);
-}
-
-struct QuantConsts {
-    float c[5];  // fl32(r / qmax) for each clip ratio, rounded on the host from doubles
+struct QCfg {
+    float c[5];     // fl32(ratio / qmax) per clip ratio, rounded on the host from doubles
+    float floor_s;  // smallest scale before rounding: 1e-8 (bf16 scales) or 2^-24 (fp16)
+    int nratios;    // 1 (round-to-nearest) or 5 (clip search)
+    int sbf16;      // scale type: 1 bf16, 0 fp16
 };
 
-// One thread per (row, group); the flat group f covers w[f*G, f*G + G).
+struct QuantArgs {
+    const void* w;       // row `row0` of the head
+    int64_t ldw;         // row stride of w in elements
+    int64_t row0, rows;  // rows present in w: [row0, row0 + rows)
+    int64_t blk0;        // first 64-row block of the launch
+    int64_t nunits;      // wavefronts with work: blocks * upb
+    int upb;             // units per 64-row block
+    int K, G, NG, NC;
+    QCfg cf;
+    uint8_t* wout;   // packed mode: weight region of the blob
+    uint16_t* sout;  //              scale region of the blob
+    int8_t* q;       // codes mode: q [V, K]
+    uint16_t* s;     //             s [V, NG]
+};
+
+template <int BITS>
+struct QRange {
+    static constexpr float lo = BITS == 4 ? -8.0f : -128.0f;
+    static constexpr float hi = BITS == 4 ? 7.0f : 127.0f;
+    // |t - rint(t)| above this: t is within the rounding gap of a half-integer
+    static constexpr float edge = BITS == 4 ? 0.5f - 0x1p-17f : 0.5f - 0x1p-14f;
+};
+
+// Eight consecutive weights of one row, widened exactly to fp32.
 template <int WDT>
-__global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ w, int64_t ngroups,
-                                                       int G, int qmin, int qmax, int sbf16,
-                                                       int nratios, QuantConsts cs,
-                                                       int8_t* __restrict__ q,
-                                                       uint16_t* __restrict__ s) {
-#pragma clang fp contract(off)
-    const int64_t f = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (f >= ngroups) return;
-    const int64_t base = f * (int64_t)G;
+__device__ __forceinline__ void load8(const char* row, int col, float* o) {
+    if constexpr (WDT == F32) {
+        const float4 x0 = *(const float4*)(row + (size_t)col * 4);
+        const float4 x1 = *(const float4*)(row + (size_t)col * 4 + 16);
+        o[0] = x0.x, o[1] = x0.y, o[2] = x0.z, o[3] = x0.w;
+        o[4] = x1.x, o[5] = x1.y, o[6] = x1.z, o[7] = x1.w;
+    } else {
+        const uint4 u = *(const uint4*)(row + (size_t)col * 2);
+        const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if constexpr (WDT == BF16) {
+                o[2 * j] = __uint_as_float(wd[j] << 16);
+                o[2 * j + 1] = __uint_as_float(wd[j] & 0xFFFF0000u);
+            } else {
+                o[2 * j] = f16_to_f32((uint16_t)wd[j]);
+                o[2 * j + 1] = f16_to_f32((uint16_t)(wd[j] >> 16));
+            }
+        }
+    }
+}
+
+// A lane's row; rows outside the launch's input (the padding rows of the last
+// block) read as zeros.
+template <int WDT>
+struct RowSrc {
+    const char* row;
+    bool valid;
+    __device__ __forceinline__ void get8(int col, float* o) const {
+        if (valid) {
+            load8<WDT>(row, col, o);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o[i] = 0.0f;
+        }
+    }
+};
+
+__device__ __forceinline__ float round_scale(float s32, int sbf16) {
+    return sbf16 ? bf16_to_f32(f32_to_bf16_rne(s32)) : f16_to_f32(f32_to_f16_rne(s32));
+}
+
+// The candidate scale of one clip ratio: round16(max(fl32(amax * c), floor)).
+__device__ __forceinline__ float ratio_scale(float amax, float c, const QCfg& cf) {
+    float s32 = amax * c;
+    s32 = s32 < cf.floor_s ? cf.floor_s : s32;
+    return round_scale(s32, cf.sbf16);
+}
+
+// q = clamp(rint(fl32(w / sv)), lo, hi) for eight weights (see the header).
+template <int BITS>
+__device__ __forceinline__ void codes8(const float* w, float sv, float rinv, float* q) {
+    float dev = 0.0f;  // largest distance of a quotient from its nearest integer
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float t = w[i] * rinv;
+        q[i] = rintf(t);
+        dev = fmaxf(dev, fabsf(t - q[i]));
+    }
+    if (__builtin_expect(dev > QRange<BITS>::edge, 0)) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float t = w[i] * rinv;
+            if (fabsf(t - rintf(t)) > QRange<BITS>::edge) q[i] = rintf(__fdiv_rn(w[i], sv));
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        q[i] = __builtin_amdgcn_fmed3f(q[i], QRange<BITS>::lo, QRange<BITS>::hi);
+}
+
+// err += sum_i (q_i * s - w_i)^2, i ascending, one fp64 fma each.  d = q*s - w
+// is exact in fp32: q*s has at most 8 + 11 significant bits, and for q != 0 it
+// lies within a factor of two of w (|w/s - q| <= 1/2 + 2^-20, or the clamp,
+// which leaves w/s within 1.25 q), so the difference is representable
+// (Sterbenz) and the single rounding of fmaf returns it unchanged.
+__device__ __forceinline__ double err8(const float* w, const float* q, float sv, double err) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const double d = (double)__builtin_fmaf(q[i], sv, -w[i]);
+        err = __builtin_fma(d, d, err);
+    }
+    return err;
+}
+
+// Chosen scale of a group held in registers; zero = the group is all zeros
+// (its stored scale is then 0 and every code 0).
+template <int BITS, int NE>
+__device__ __forceinline__ float pick_scale_held(const float* w, const QCfg& cf, bool& zero) {
     float amax = 0.0f;
-    for (int k = 0; k < G; ++k) amax = fmaxf(amax, fabsf(load_w<WDT>(w, base + k)));
-    int8_t* qd = q + base;
-    if (amax == 0.0f) {
-        for (int k = 0; k < G; ++k) qd[k] = 0;
-        s[f] = 0;
-        return;
-    }
-    const float floor_s = sbf16 ? 1e-8f : 5.9604644775390625e-8f;  // 2^-24
-    const float fqmin = (float)qmin, fqmax = (float)qmax;
-    float best_s = 0.0f;
-    double best_err = 0.0;
-    for (int i = 0; i < nratios; ++i) {
-        float s32 = amax * cs.c[i];
-        s32 = s32 < floor_s ? floor_s : s32;
-        const float sv = sbf16 ? bf16_to_f32(f32_to_bf16_rne(s32)) : f16_to_f32(f32_to_f16_rne(s32));
-        if (nratios == 1) {
-            best_s = sv;
-            break;
-        }
-        double err = 0.0;
-        const double sd = (double)sv;
-        for (int k = 0; k < G; ++k) {
-            const float wk = load_w<WDT>(w, base + k);
-            float r = rintf(__fdiv_rn(wk, sv));
-            r = fminf(fmaxf(r, fqmin), fqmax);
-            const double d = (double)r * sd - (double)wk;  // exact: product and difference fit in 53 bits
-            err = __builtin_fma(d, d, err);
-        }
-        if (i == 0 || err < best_err) {
-            best_err = err;
-            best_s = sv;
+#pragma unroll
+    for (int k = 0; k < NE; ++k) amax = fmaxf(amax, fabsf(w[k]));
+    zero = amax == 0.0f;
+    float best = ratio_scale(amax, cf.c[0], cf);
+    if (cf.nratios > 1) {
+        double best_err = 0.0;
+#pragma unroll 1
+        for (int i = 0; i < cf.nratios; ++i) {
+            const float sv = ratio_scale(amax, cf.c[i], cf);
+            const float rinv = __fdiv_rn(1.0f, sv);
+            double err = 0.0;
+#pragma unroll
+            for (int k = 0; k < NE; k += 8) {
+                float q[8];
+                codes8<BITS>(w + k, sv, rinv, q);
+                err = err8(w + k, q, sv, err);
+            }
+            if (i == 0 || err < best_err) {
+                best_err = err;
+                best = sv;
+            }
         }
     }
-    for (int k = 0; k < G; ++k) {
-        const float wk = load_w<WDT>(w, base + k);
-        float r = rintf(__fdiv_rn(wk, best_s));
-        r = fminf(fmaxf(r, fqmin), fqmax);
-        qd[k] = (int8_t)(int)r;
+    return best;
+}
+
+// The same for a group streamed from memory once per pass.
+template <int WDT, int BITS>
+__device__ __forceinline__ float pick_scale_stream(const RowSrc<WDT>& src, int col0, int G,
+                                                   const QCfg& cf, bool& zero) {
+    float amax = 0.0f;
+#pragma unroll 2
+    for (int k = 0; k < G; k += 8) {
+        float w[8];
+        src.get8(col0 + k, w);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(w[i]));
     }
-    s[f] = sbf16 ? f32_to_bf16_rne(best_s) : f32_to_f16_rne(best_s);
+    zero = amax == 0.0f;
+    float best = ratio_scale(amax, cf.c[0], cf);
+    if (cf.nratios > 1) {
+        double best_err = 0.0;
+#pragma unroll 1
+        for (int i = 0; i < cf.nratios; ++i) {
+            const float sv = ratio_scale(amax, cf.c[i], cf);
+            const float rinv = __fdiv_rn(1.0f, sv);
+            double err = 0.0;
+#pragma unroll 2
+            for (int k = 0; k < G; k += 8) {
+                float w[8], q[8];
+                src.get8(col0 + k, w);
+                codes8<BITS>(w, sv, rinv, q);
+                err = err8(w, q, sv, err);
+            }
+            if (i == 0 || err < best_err) {
+                best_err = err;
+                best = sv;
+            }
+        }
+    }
+    return best;
+}
+
+__device__ __forceinline__ uint16_t scale_bits(float sv, bool zero, int sbf16) {
+    if (zero) return 0;
+    return sbf16 ? f32_to_bf16_rne(sv) : f32_to_f16_rne(sv);
+}
+
+// Packed-layout words of one 32-column chunk (codes q[0..31], already
+// clamped) into slot words sw[t][j]: int4 chunk jj fills word j = jj of the
+// four slots (nibble q + 8; even columns in the low half-word, odd columns in
+// the high one); int8 chunk jj fills words 2jj and 2jj + 1 (byte q + 128).
+template <int BITS>
+__device__ __forceinline__ void put_chunk(const float* q, int jj, uint32_t (&sw)[4][4]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const float* q8 = q + 8 * t;
+        if constexpr (BITS == 4) {
+            uint32_t lo = 0, hi = 0;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                lo |= (uint32_t)(int)(q8[2 * p] + 8.0f) << (4 * p);
+                hi |= (uint32_t)(int)(q8[2 * p + 1] + 8.0f) << (4 * p);
+            }
+            sw[t][jj] = lo | (hi << 16);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                uint32_t wd = 0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) wd |= (uint32_t)(int)(q8[4 * e + i] + 128.0f) << (8 * i);
+                sw[t][2 * jj + e] = wd;
+            }
+        }
+    }
+}
+
+// The four slots of superchunk c of a lane's row: 64 lanes store 1 KiB runs.
+__device__ __forceinline__ void store_slots(uint8_t* wout, int64_t b, int NC, int c, int r,
+                                            const uint32_t (&sw)[4][4]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+        *(uint4*)(wout + ((((b * NC + c) * 4 + t) * 64 + r) * 16)) =
+            make_uint4(sw[t][0], sw[t][1], sw[t][2], sw[t][3]);
+}
+
+// 32 codes of a row in codes mode: int8 two's complement, row-major.
+__device__ __forceinline__ void store_codes32(int8_t* dst, const float* q) {
+    uint32_t wd[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        uint32_t x = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x |= ((uint32_t)(int)q[4 * m + i] & 0xFFu) << (8 * i);
+        wd[m] = x;
+    }
+    *(uint4*)dst = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+    *(uint4*)(dst + 16) = make_uint4(wd[4], wd[5], wd[6], wd[7]);
+}
+
+template <int WDT>
+__device__ __forceinline__ RowSrc<WDT> lane_row(const QuantArgs& a, int64_t v) {
+    constexpr int esz = WDT == F32 ? 4 : 2;
+    const int64_t lr = v - a.row0;
+    const bool valid = lr < a.rows;
+    return RowSrc<WDT>{(const char*)a.w + (valid ? lr : 0) * a.ldw * esz, valid};
+}
+
+// Groups of GT <= 128 columns, held in registers.  Unit: one superchunk (or
+// one group when GT exceeds the span) in packed mode, one group in codes mode.
+template <int WDT, int BITS, int GT, bool PACKED>
+__global__ __launch_bounds__(256, GT == 128 ? 2 : (GT == 64 ? 3 : 4)) void quant_held_kernel(
+    const QuantArgs a) {
+#pragma clang fp contract(off)
+    const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (unit >= a.nunits) return;
+    const int r = threadIdx.x & 63;
+    const int64_t b = a.blk0 + unit / a.upb;
+    const int u = (int)(unit % a.upb);
+    const int64_t v = b * 64 + r;
+    const RowSrc<WDT> src = lane_row<WDT>(a, v);
+    constexpr int span = span_of(BITS);
+    constexpr int UC = PACKED ? (GT > span ? GT : span) : GT;  // unit columns
+    constexpr int CPS = span / 32;                             // chunks per superchunk
+    const int col_u = u * UC;
+    uint32_t sw[4][4];
+#pragma unroll
+    for (int gi = 0; gi < UC / GT; ++gi) {
+        const int col0 = col_u + gi * GT;
+        float w[GT];
+#pragma unroll
+        for (int k = 0; k < GT; k += 8) src.get8(col0 + k, w + k);
+        bool zero;
+        const float sv = pick_scale_held<BITS, GT>(w, a.cf, zero);
+        const uint16_t sb = scale_bits(sv, zero, a.cf.sbf16);
+        const float rinv = __fdiv_rn(1.0f, sv);
+        if constexpr (PACKED) {
+            a.sout[(b * a.NG + col0 / GT) * 64 + r] = sb;
+#pragma unroll
+            for (int ch = 0; ch < GT / 32; ++ch) {
+                float q[32];
+#pragma unroll
+                for (int k = 0; k < 32; k += 8) codes8<BITS>(w + 32 * ch + k, sv, rinv, q + k);
+                const int cu = gi * (GT / 32) + ch;  // chunk index within the unit
+                put_chunk<BITS>(q, cu % CPS, sw);
+                if (cu % CPS == CPS - 1) store_slots(a.wout, b, a.NC, (col_u + 32 * cu) / span, r, sw);
+            }
+        } else if (src.valid) {
+            a.s[v * a.NG + col0 / GT] = sb;
+#pragma unroll
+            for (int ch = 0; ch < GT / 32; ++ch) {
+                float q[32];
+#pragma unroll
+                for (int k = 0; k < 32; k += 8) codes8<BITS>(w + 32 * ch + k, sv, rinv, q + k);
+                store_codes32(a.q + v * a.K + col0 + 32 * ch, q);
+            }
+        }
+    }
+}
+
+// Longer groups, streamed once per pass.  Unit: one group.
+template <int WDT, int BITS, bool PACKED>
+__global__ __launch_bounds__(256, 3) void quant_stream_kernel(const QuantArgs a) {
+#pragma clang fp contract(off)
+    const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (unit >= a.nunits) return;
+    const int r = threadIdx.x & 63;
+    const int64_t b = a.blk0 + unit / a.upb;
+    const int g = (int)(unit % a.upb);
+    const int64_t v = b * 64 + r;
+    const RowSrc<WDT> src = lane_row<WDT>(a, v);
+    const int col0 = g * a.G;
+    bool zero;
+    const float sv = pick_scale_stream<WDT, BITS>(src, col0, a.G, a.cf, zero);
+    const uint16_t sb = scale_bits(sv, zero, a.cf.sbf16);
+    const float rinv = __fdiv_rn(1.0f, sv);
+    if constexpr (PACKED) {
+        constexpr int span = span_of(BITS);
+        a.sout[(b * a.NG + g) * 64 + r] = sb;
+#pragma unroll 1
+        for (int c = col0 / span; c < (col0 + a.G) / span; ++c) {
+            uint32_t sw[4][4];
+#pragma unroll
+            for (int ch = 0; ch < span / 32; ++ch) {
+                float w[32], q[32];
+#pragma unroll
+                for (int k = 0; k < 32; k += 8) {
+                    src.get8(c * span + 32 * ch + k, w + k);
+                    codes8<BITS>(w + k, sv, rinv, q + k);
+                }
+                put_chunk<BITS>(q, ch, sw);
+            }
+            store_slots(a.wout, b, a.NC, c, r, sw);
+        }
+    } else if (src.valid) {
+        a.s[v * a.NG + g] = sb;
+#pragma unroll 1
+        for (int col = col0; col < col0 + a.G; col += 32) {
+            float w[32], q[32];
+#pragma unroll
+            for (int k = 0; k < 32; k += 8) {
+                src.get8(col + k, w + k);
+                codes8<BITS>(w + k, sv, rinv, q + k);
+            }
+            store_codes32(a.q + v * a.K + col, q);
+        }
+    }
+}
+
+template <int WDT, int BITS, bool PACKED>
+void launch_q3(const QuantArgs& a, dim3 grid, hipStream_t st) {
+    switch (a.G) {
+    case 32:
+        hipLaunchKernelGGL((quant_held_kernel<WDT, BITS, 32, PACKED>), grid, dim3(256), 0, st, a);
+        break;
+    case 64:
+        hipLaunchKernelGGL((quant_held_kernel<WDT, BITS, 64, PACKED>), grid, dim3(256), 0, st, a);
+        break;
+    case 128:
+        hipLaunchKernelGGL((quant_held_kernel<WDT, BITS, 128, PACKED>), grid, dim3(256), 0, st, a);
+        break;
+    default:
+        hipLaunchKernelGGL((quant_stream_kernel<WDT, BITS, PACKED>), grid, dim3(256), 0, st, a);
+        break;
+    }
+}
+
+template <bool PACKED>
+hipError_t launch_q(const QuantArgs& a, int w_dtype, int bits, hipStream_t st) {
+    if (a.nunits <= 0) return hipSuccess;
+    const dim3 grid((unsigned)((a.nunits + 3) / 4));
+#define LMH_Q_CASE(WDT)                                                \
+    if (bits == 4) launch_q3<WDT, 4, PACKED>(a, grid, st);             \
+    else launch_q3<WDT, 8, PACKED>(a, grid, st);
+    switch (w_dtype) {
+    case F32: LMH_Q_CASE(F32) break;
+    case F16: LMH_Q_CASE(F16) break;
+    default: LMH_Q_CASE(BF16) break;
+    }
+#undef LMH_Q_CASE
+    return hipGetLastError();
+}
+
+QCfg make_cfg(int bits, int scale_dtype, int nratios) {
+    static const double kRatios[5] = {1.0, 0.95, 0.9, 0.85, 0.8};
+    const int qmax = bits == 4 ? 7 : 127;
+    QCfg cf;
+    for (int i = 0; i < 5; ++i) cf.c[i] = (float)(kRatios[i] / (double)qmax);
+    cf.sbf16 = scale_dtype == BF16;
+    cf.floor_s = cf.sbf16 ? 1e-8f : 5.9604644775390625e-8f;  // 2^-24
+    cf.nratios = nratios;
+    return cf;
 }
 
 // One thread per 16-byte weight slot of the blob.
@@ -159,29 +509,46 @@ inline unsigned grid_for(int64_t n, int block) { return (unsigned)((n + block - 
 
 hipError_t launch_quantize(const void* w, int w_dtype, int64_t V, int64_t K, int bits, int64_t G,
                            int scale_dtype, int nratios, int8_t* q, uint16_t* s, hipStream_t st) {
-    static const double kRatios[5] = {1.0, 0.95, 0.9, 0.85, 0.8};
-    const int qmax = bits == 4 ? 7 : 127;
-    const int qmin = bits == 4 ? -8 : -128;
-    QuantConsts cs;
-    for (int i = 0; i < 5; ++i) cs.c[i] = (float)(kRatios[i] / (double)qmax);
-    const int64_t ngroups = V * (K / G);
-    const dim3 grid(grid_for(ngroups, 256)), block(256);
-    const int sbf = scale_dtype == BF16;
-    switch (w_dtype) {
-    case F32:
-        hipLaunchKernelGGL(quantize_kernel<F32>, grid, block, 0, st, w, ngroups, (int)G, qmin, qmax,
-                           sbf, nratios, cs, q, s);
-        break;
-    case F16:
-        hipLaunchKernelGGL(quantize_kernel<F16>, grid, block, 0, st, w, ngroups, (int)G, qmin, qmax,
-                           sbf, nratios, cs, q, s);
-        break;
-    default:
-        hipLaunchKernelGGL(quantize_kernel<BF16>, grid, block, 0, st, w, ngroups, (int)G, qmin,
-                           qmax, sbf, nratios, cs, q, s);
-        break;
-    }
-    return hipGetLastError();
+    QuantArgs a{};
+    a.w = w;
+    a.ldw = K;
+    a.row0 = 0;
+    a.rows = V;
+    a.blk0 = 0;
+    a.K = (int)K;
+    a.G = (int)G;
+    a.NG = (int)(K / G);
+    a.NC = 0;
+    a.upb = a.NG;  // codes mode: one unit per group
+    a.nunits = (V + 63) / 64 * a.upb;
+    a.cf = make_cfg(bits, scale_dtype, nratios);
+    a.q = q;
+    a.s = s;
+    return launch_q<false>(a, w_dtype, bits, st);
+}
+
+hipError_t launch_quantize_pack(const void* w, int w_dtype, int64_t ldw, int64_t V, int64_t K,
+                                int bits, int64_t G, int scale_dtype, int nratios, int64_t row0,
+                                int64_t rows, uint8_t* blob, hipStream_t st) {
+    const int span = span_of(bits);
+    const int64_t vpad = (V + 63) / 64 * 64;
+    QuantArgs a{};
+    a.w = w;
+    a.ldw = ldw;
+    a.row0 = row0;
+    a.rows = rows;
+    a.blk0 = row0 / 64;
+    a.K = (int)K;
+    a.G = (int)G;
+    a.NG = (int)(K / G);
+    a.NC = (int)(K / span);
+    // unit: a superchunk, or a whole group when the group is longer
+    a.upb = (int)(K / (G > span ? G : span));
+    a.nunits = (rows + 63) / 64 * a.upb;
+    a.cf = make_cfg(bits, scale_dtype, nratios);
+    a.wout = blob;
+    a.sout = (uint16_t*)(blob + vpad * K * bits / 8);
+    return launch_q<true>(a, w_dtype, bits, st);
 }
 
 hipError_t launch_pack(const int8_t* q, const uint16_t* s, int64_t V, int64_t K, int bits,
