@@ -21,17 +21,18 @@
 //     codes ever reaches memory.  A launch may cover any run of whole 64-row
 //     blocks, which is what lets a caller quantize a head chunk by chunk.
 //
-// Quotient rounding.  q = rint(fl32(w / s)) needs the correctly rounded
-// quotient only next to a half-integer.  With rinv = fl32(1 / s) (correctly
-// rounded, once per group and ratio) and t = fl32(w * rinv), t and fl32(w / s)
-// differ by at most 3 * 2^-24 * |w / s| (three roundings of relative size
-// 2^-24, all results normal).  |w / s| <= qmax / 0.8 * (1 + 2^-8) (the
-// smallest clip ratio, and the scale's own 16-bit rounding), so the gap is
-// below 1.6e-6 for int4 and 2.9e-5 for int8.  When t is farther than 2^-17
-// (int4) or 2^-14 (int8) from every half-integer, t and the exact quotient lie
-// strictly between the same two half-integers and round to the same integer;
-// only the remaining elements (about 1e-5 resp. 1e-4 of them) take the IEEE
-// division.
+// Quotient rounding.  q = rint(fl32(w / s)) is computed without a division
+// and without any data-dependent branch: fl32(w / s) == RN32(RN64(w * r))
+// with r = RN64(1 / s) (once per group and ratio).  Proof sketch: write the
+// scale's odd significand as S < 2^11 (fp16; < 2^8 for bf16) and the weight's
+// significand as W < 2^24.  An fp32 rounding midpoint is m = (2M + 1) 2^g with
+// 2^24 <= 2M + 1 < 2^25; w / s = m would need W 2^j = S (2M + 1), an odd
+// number of at least 2^24, so w / s is never a midpoint, and when nonzero its
+// distance to one is at least 2^g / S, i.e. a relative 1 / (S (2M + 1)) >
+// 2^-36.  The fp64 product is within 2^-52 (relative) of w / s, so it lies on
+// the same side of every fp32 midpoint and rounds to the same fp32 value;
+// exactly representable quotients (half-integers included) come back
+// unchanged, so ties still go to even.
 #include "lmh_internal.h"
 
 #include <math.h>
@@ -80,8 +81,6 @@ template <int BITS>
 struct QRange {
     static constexpr float lo = BITS == 4 ? -8.0f : -128.0f;
     static constexpr float hi = BITS == 4 ? 7.0f : 127.0f;
-    // |t - rint(t)| above this: t is within the rounding gap of a half-integer
-    static constexpr float edge = BITS == 4 ? 0.5f - 0x1p-17f : 0.5f - 0x1p-14f;
 };
 
 // Eight consecutive weights of one row, widened exactly to fp32.
@@ -130,110 +129,147 @@ __device__ __forceinline__ float round_scale(float s32, int sbf16) {
 
 // The candidate scale of one clip ratio: round16(max(fl32(amax * c), floor)).
 __device__ __forceinline__ float ratio_scale(float amax, float c, const QCfg& cf) {
+#pragma clang fp contract(off)
     float s32 = amax * c;
     s32 = s32 < cf.floor_s ? cf.floor_s : s32;
     return round_scale(s32, cf.sbf16);
 }
 
-// q = clamp(rint(fl32(w / sv)), lo, hi) for eight weights (see the header).
-template <int BITS>
-__device__ __forceinline__ void codes8(const float* w, float sv, float rinv, float* q) {
-    float dev = 0.0f;  // largest distance of a quotient from its nearest integer
+// q = clamp(rint(fl32(w / s)), lo, hi) for N weights, r = RN64(1 / s) (see
+// the header).
+template <int BITS, int N>
+__device__ __forceinline__ void codes(const float* w, double r, float* q) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float t = w[i] * rinv;
-        q[i] = rintf(t);
-        dev = fmaxf(dev, fabsf(t - q[i]));
+    for (int i = 0; i < N; ++i) {
+        const float x = (float)((double)w[i] * r);
+        q[i] = __builtin_amdgcn_fmed3f(rintf(x), QRange<BITS>::lo, QRange<BITS>::hi);
     }
-    if (__builtin_expect(dev > QRange<BITS>::edge, 0)) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float t = w[i] * rinv;
-            if (fabsf(t - rintf(t)) > QRange<BITS>::edge) q[i] = rintf(__fdiv_rn(w[i], sv));
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        q[i] = __builtin_amdgcn_fmed3f(q[i], QRange<BITS>::lo, QRange<BITS>::hi);
 }
 
 // err += sum_i (q_i * s - w_i)^2, i ascending, one fp64 fma each.  d = q*s - w
 // is exact in fp32: q*s has at most 8 + 11 significant bits, and for q != 0 it
-// lies within a factor of two of w (|w/s - q| <= 1/2 + 2^-20, or the clamp,
+// lies within a factor of two of w (|w/s - q| <= 1/2 + 2^-16, or the clamp,
 // which leaves w/s within 1.25 q), so the difference is representable
 // (Sterbenz) and the single rounding of fmaf returns it unchanged.
-__device__ __forceinline__ double err8(const float* w, const float* q, float sv, double err) {
+template <int N>
+__device__ __forceinline__ double errN(const float* w, const float* q, float sv, double err) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < N; ++i) {
         const double d = (double)__builtin_fmaf(q[i], sv, -w[i]);
         err = __builtin_fma(d, d, err);
     }
     return err;
 }
 
-// Chosen scale of a group held in registers; zero = the group is all zeros
-// (its stored scale is then 0 and every code 0).
-template <int BITS, int NE>
-__device__ __forceinline__ float pick_scale_held(const float* w, const QCfg& cf, bool& zero) {
-    float amax = 0.0f;
+// A group of NE <= 128 weights of one row held in registers: fp32 as is,
+// 16-bit weights as their raw bit patterns two to a register (widened on use).
+template <int WDT, int NE>
+struct Held {
+    static constexpr int kWords = WDT == F32 ? NE : NE / 2;
+    uint32_t v[kWords];
+    __device__ __forceinline__ void load(const RowSrc<WDT>& src, int col0) {
+        constexpr int per16 = WDT == F32 ? 4 : 8;  // elements per 16-byte load
 #pragma unroll
-    for (int k = 0; k < NE; ++k) amax = fmaxf(amax, fabsf(w[k]));
-    zero = amax == 0.0f;
-    float best = ratio_scale(amax, cf.c[0], cf);
-    if (cf.nratios > 1) {
-        double best_err = 0.0;
-#pragma unroll 1
-        for (int i = 0; i < cf.nratios; ++i) {
-            const float sv = ratio_scale(amax, cf.c[i], cf);
-            const float rinv = __fdiv_rn(1.0f, sv);
-            double err = 0.0;
+        for (int k = 0; k < NE; k += per16) {
+            uint4 u = make_uint4(0, 0, 0, 0);
+            if (src.valid)
+                u = *(const uint4*)(src.row + (size_t)(col0 + k) * (WDT == F32 ? 4 : 2));
+            const int o = WDT == F32 ? k : k / 2;
+            v[o] = u.x, v[o + 1] = u.y, v[o + 2] = u.z, v[o + 3] = u.w;
+        }
+    }
+    // N weights starting at element k (a multiple of N), as fp32
+    template <int N>
+    __device__ __forceinline__ void get(int k, float* o) const {
 #pragma unroll
-            for (int k = 0; k < NE; k += 8) {
-                float q[8];
-                codes8<BITS>(w + k, sv, rinv, q);
-                err = err8(w + k, q, sv, err);
-            }
-            if (i == 0 || err < best_err) {
-                best_err = err;
-                best = sv;
+        for (int i = 0; i < N; ++i) {
+            if constexpr (WDT == F32) {
+                o[i] = __uint_as_float(v[k + i]);
+            } else {
+                const uint32_t x = v[(k + i) / 2];
+                if constexpr (WDT == BF16)
+                    o[i] = __uint_as_float((i & 1) ? (x & 0xFFFF0000u) : (x << 16));
+                else
+                    o[i] = f16_to_f32((uint16_t)((i & 1) ? (x >> 16) : x));
             }
         }
     }
-    return best;
+};
+
+// Streamed weights of one row: N from column col, read from memory.
+template <int WDT, int N>
+__device__ __forceinline__ void get_stream(const RowSrc<WDT>& src, int col, float* w) {
+#pragma unroll
+    for (int k = 0; k < N; k += 8) src.get8(col + k, w + k);
 }
 
-// The same for a group streamed from memory once per pass.
-template <int WDT, int BITS>
-__device__ __forceinline__ float pick_scale_stream(const RowSrc<WDT>& src, int col0, int G,
-                                                   const QCfg& cf, bool& zero) {
+template <int WDT, int NE>
+struct HeldGet {
+    const Held<WDT, NE>& h;
+    template <int N>
+    __device__ __forceinline__ void operator()(int k, float* o) const {
+        h.template get<N>(k, o);
+    }
+};
+
+template <int WDT>
+struct StreamGet {
+    const RowSrc<WDT>& src;
+    int col0;
+    template <int N>
+    __device__ __forceinline__ void operator()(int k, float* o) const {
+        get_stream<WDT, N>(src, col0 + k, o);
+    }
+};
+
+constexpr int kRatios = 5;  // the clip search's ratios: 1.0, 0.95, 0.9, 0.85, 0.8
+constexpr int kSearchN = 16;  // columns per step of the search
+
+// Chosen scale of a group; zero = the group is all zeros (its stored scale is
+// then 0 and every code 0).  `get(k, w)` yields the group's columns
+// [k, k + N) as fp32 for any multiple k of N.  The clip search walks the group
+// once with the five candidate scales side by side: each ratio's error is
+// still summed in ascending column order, but the five independent fp64
+// chains interleave instead of running one after another.
+template <int BITS, bool UNROLL, class Get>
+__device__ __forceinline__ float pick_scale(const Get& get, int G, const QCfg& cf, bool& zero) {
     float amax = 0.0f;
-#pragma unroll 2
-    for (int k = 0; k < G; k += 8) {
-        float w[8];
-        src.get8(col0 + k, w);
+#pragma unroll(UNROLL ? 16 : 1)
+    for (int k = 0; k < G; k += 32) {
+        float w[32];
+        get.template operator()<32>(k, w);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(w[i]));
+        for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(w[i]));
     }
     zero = amax == 0.0f;
-    float best = ratio_scale(amax, cf.c[0], cf);
-    if (cf.nratios > 1) {
-        double best_err = 0.0;
-#pragma unroll 1
-        for (int i = 0; i < cf.nratios; ++i) {
-            const float sv = ratio_scale(amax, cf.c[i], cf);
-            const float rinv = __fdiv_rn(1.0f, sv);
-            double err = 0.0;
-#pragma unroll 2
-            for (int k = 0; k < G; k += 8) {
-                float w[8], q[8];
-                src.get8(col0 + k, w);
-                codes8<BITS>(w, sv, rinv, q);
-                err = err8(w, q, sv, err);
-            }
-            if (i == 0 || err < best_err) {
-                best_err = err;
-                best = sv;
-            }
+    if (cf.nratios == 1) return ratio_scale(amax, cf.c[0], cf);
+    float sv[kRatios];
+    double rr[kRatios], err[kRatios];
+#pragma unroll
+    for (int i = 0; i < kRatios; ++i) {
+        sv[i] = ratio_scale(amax, cf.c[i], cf);
+        rr[i] = 1.0 / (double)sv[i];
+        err[i] = 0.0;
+    }
+#pragma unroll(UNROLL ? 16 : 1)
+    for (int k = 0; k < G; k += kSearchN) {
+        float w[kSearchN];
+        get.template operator()<kSearchN>(k, w);
+#pragma unroll
+        for (int i = 0; i < kRatios; ++i) {
+            float q[kSearchN];
+            codes<BITS, kSearchN>(w, rr[i], q);
+            err[i] = errN<kSearchN>(w, q, sv[i], err[i]);
+        }
+    }
+    // the first ratio whose error is strictly below every earlier one
+    float best = sv[0];
+    double best_err = err[0];
+#pragma unroll
+    for (int i = 1; i < kRatios; ++i) {
+        if (err[i] < best_err) {
+            best_err = err[i];
+            best = sv[i];
         }
     }
     return best;
@@ -307,7 +343,8 @@ __device__ __forceinline__ RowSrc<WDT> lane_row(const QuantArgs& a, int64_t v) {
 // Groups of GT <= 128 columns, held in registers.  Unit: one superchunk (or
 // one group when GT exceeds the span) in packed mode, one group in codes mode.
 template <int WDT, int BITS, int GT, bool PACKED>
-__global__ __launch_bounds__(256, GT == 128 ? 2 : (GT == 64 ? 3 : 4)) void quant_held_kernel(
+__global__ __launch_bounds__(256, 2) void
+quant_held_kernel(
     const QuantArgs a) {
 #pragma clang fp contract(off)
     const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -325,32 +362,33 @@ __global__ __launch_bounds__(256, GT == 128 ? 2 : (GT == 64 ? 3 : 4)) void quant
 #pragma unroll
     for (int gi = 0; gi < UC / GT; ++gi) {
         const int col0 = col_u + gi * GT;
-        float w[GT];
-#pragma unroll
-        for (int k = 0; k < GT; k += 8) src.get8(col0 + k, w + k);
+        Held<WDT, GT> h;
+        h.load(src, col0);
         bool zero;
-        const float sv = pick_scale_held<BITS, GT>(w, a.cf, zero);
+        const float sv = pick_scale<BITS, true>(HeldGet<WDT, GT>{h}, GT, a.cf, zero);
         const uint16_t sb = scale_bits(sv, zero, a.cf.sbf16);
-        const float rinv = __fdiv_rn(1.0f, sv);
+        const double rr = 1.0 / (double)sv;
         if constexpr (PACKED) {
             a.sout[(b * a.NG + col0 / GT) * 64 + r] = sb;
 #pragma unroll
             for (int ch = 0; ch < GT / 32; ++ch) {
-                float q[32];
-#pragma unroll
-                for (int k = 0; k < 32; k += 8) codes8<BITS>(w + 32 * ch + k, sv, rinv, q + k);
+                float w[32], q[32];
+                h.template get<32>(32 * ch, w);
+                codes<BITS, 32>(w, rr, q);
                 const int cu = gi * (GT / 32) + ch;  // chunk index within the unit
                 put_chunk<BITS>(q, cu % CPS, sw);
                 if (cu % CPS == CPS - 1) store_slots(a.wout, b, a.NC, (col_u + 32 * cu) / span, r, sw);
+                __builtin_amdgcn_sched_barrier(0);
             }
         } else if (src.valid) {
             a.s[v * a.NG + col0 / GT] = sb;
 #pragma unroll
             for (int ch = 0; ch < GT / 32; ++ch) {
-                float q[32];
-#pragma unroll
-                for (int k = 0; k < 32; k += 8) codes8<BITS>(w + 32 * ch + k, sv, rinv, q + k);
+                float w[32], q[32];
+                h.template get<32>(32 * ch, w);
+                codes<BITS, 32>(w, rr, q);
                 store_codes32(a.q + v * a.K + col0 + 32 * ch, q);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     }
@@ -358,7 +396,7 @@ __global__ __launch_bounds__(256, GT == 128 ? 2 : (GT == 64 ? 3 : 4)) void quant
 
 // Longer groups, streamed once per pass.  Unit: one group.
 template <int WDT, int BITS, bool PACKED>
-__global__ __launch_bounds__(256, 3) void quant_stream_kernel(const QuantArgs a) {
+__global__ __launch_bounds__(256, 2) void quant_stream_kernel(const QuantArgs a) {
 #pragma clang fp contract(off)
     const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (unit >= a.nunits) return;
@@ -369,9 +407,9 @@ __global__ __launch_bounds__(256, 3) void quant_stream_kernel(const QuantArgs a)
     const RowSrc<WDT> src = lane_row<WDT>(a, v);
     const int col0 = g * a.G;
     bool zero;
-    const float sv = pick_scale_stream<WDT, BITS>(src, col0, a.G, a.cf, zero);
+    const float sv = pick_scale<BITS, false>(StreamGet<WDT>{src, col0}, a.G, a.cf, zero);
     const uint16_t sb = scale_bits(sv, zero, a.cf.sbf16);
-    const float rinv = __fdiv_rn(1.0f, sv);
+    const double rr = 1.0 / (double)sv;
     if constexpr (PACKED) {
         constexpr int span = span_of(BITS);
         a.sout[(b * a.NG + g) * 64 + r] = sb;
@@ -381,11 +419,8 @@ __global__ __launch_bounds__(256, 3) void quant_stream_kernel(const QuantArgs a)
 #pragma unroll
             for (int ch = 0; ch < span / 32; ++ch) {
                 float w[32], q[32];
-#pragma unroll
-                for (int k = 0; k < 32; k += 8) {
-                    src.get8(c * span + 32 * ch + k, w + k);
-                    codes8<BITS>(w + k, sv, rinv, q + k);
-                }
+                get_stream<WDT, 32>(src, c * span + 32 * ch, w);
+                codes<BITS, 32>(w, rr, q);
                 put_chunk<BITS>(q, ch, sw);
             }
             store_slots(a.wout, b, a.NC, c, r, sw);
@@ -395,11 +430,8 @@ __global__ __launch_bounds__(256, 3) void quant_stream_kernel(const QuantArgs a)
 #pragma unroll 1
         for (int col = col0; col < col0 + a.G; col += 32) {
             float w[32], q[32];
-#pragma unroll
-            for (int k = 0; k < 32; k += 8) {
-                src.get8(col + k, w + k);
-                codes8<BITS>(w + k, sv, rinv, q + k);
-            }
+            get_stream<WDT, 32>(src, col, w);
+            codes<BITS, 32>(w, rr, q);
             store_codes32(a.q + v * a.K + col, q);
         }
     }
