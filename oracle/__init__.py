@@ -84,6 +84,8 @@ def _load() -> ctypes.CDLL:
         lib.orc_unpack.argtypes = [vp, i64, i64, i32, i64, vp, vp]
         lib.orc_logits.restype = i32
         lib.orc_logits.argtypes = [vp, i32, i64, vp, vp, i32, i64, i64, i64, vp, vp, i64, vp]
+        lib.orc_embed.restype = i32
+        lib.orc_embed.argtypes = [vp, vp, i32, i64, i64, i64, vp, i64, i32, vp]
         lib.orc_dense_logits.restype = i32
         lib.orc_dense_logits.argtypes = [vp, i32, i64, vp, i32, i64, i64, vp, i64, vp]
         lib.orc_topk.restype = i32
@@ -225,6 +227,23 @@ def logits(x: np.ndarray, q: np.ndarray, s: np.ndarray, scale_dtype: int, group:
                             V, K, group, bp or None, rp or None, n, _ptr(y))
     _check(rc, "logits")
     return y
+
+
+def embed(q: np.ndarray, s: np.ndarray, scale_dtype: int, group: int, ids,
+          out_dtype: int = F32) -> np.ndarray:
+    """Embedding rows out[t, k] = q[id,k] * s[id, k/G] rounded once to out_dtype
+    (float32 array, or uint16 bit patterns for F16/BF16); ids outside [0, V)
+    give zero rows."""
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    s = np.ascontiguousarray(s, dtype=np.uint16)
+    ids = np.ascontiguousarray(np.asarray(ids, dtype=np.int32).ravel())
+    V, K = q.shape
+    out = np.empty((len(ids), K), dtype=np.float32 if out_dtype == F32 else np.uint16)
+    rc = _load().orc_embed(_ptr(q), _ptr(s), scale_dtype, V, K, group, _ptr(ids) if len(ids) else None,
+                           len(ids), out_dtype, _ptr(out) if out.size else None)
+    if len(ids):
+        _check(rc, "embed")
+    return out
 
 
 def dense_logits(x: np.ndarray, w: np.ndarray, rows=None, x_dtype: Optional[int] = None,

@@ -19,6 +19,9 @@
  *     products, fp64 sums (vLLM PR #48870 "Fused WNA16 GEMM for tied quantized
  *     lm_head logits", Purpose: the fused dequant-GEMM computes the same logits
  *     as dequantize-then-F.linear);
+ *   - embedding rows q[v,k] * s[v,k/G] gathered by token id from the same
+ *     quantized table (same page, Purpose: the tied embedding's table serves
+ *     both the input lookup and the lm_head);
  *   - dense logits x * W_ref^T in fp64 (the unquantized control, same page,
  *     review comment point 1);
  *   - top-K selection and exact rescoring of the K rows from the unquantized
@@ -356,6 +359,40 @@ int orc_logits(const void* x, int x_dtype, int64_t M, const int8_t* q, const uin
             }
             if (bias) acc += (double)bias[v];
             y[m * nrows + j] = acc;
+        }
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Embedding rows from the canonical quantized form:                          */
+/*   out[t, k] = q[v,k] * s[v, k/G],  v = ids[t],                             */
+/* the product exact (at most 8 + 11 significant bits), then rounded once to  */
+/* out_dtype (fp32: unchanged; fp16/bf16: nearest, ties to even).  An id      */
+/* outside [0, V) gives a row of zeros.  The packed table of a tied head is    */
+/* also the input-embedding table, so the lookup dequantizes its rows (vLLM   */
+/* PR #48870, Purpose: the quantized embedding serves the input lookup and     */
+/* is reused as the tied lm_head).                                            */
+/* ------------------------------------------------------------------------ */
+int orc_embed(const int8_t* q, const uint16_t* s, int scale_dtype, int64_t V, int64_t K,
+              int64_t G, const int32_t* ids, int64_t T, int out_dtype, void* out) {
+    if (!q || !s || !ids || !out || G <= 0 || K % G != 0 || T < 0) return ORC_EARG;
+    if (scale_dtype != ORC_F16 && scale_dtype != ORC_BF16) return ORC_EARG;
+    if (out_dtype != ORC_F32 && out_dtype != ORC_F16 && out_dtype != ORC_BF16) return ORC_EARG;
+    const int64_t NG = K / G;
+    const int sb = (scale_dtype == ORC_F16) ? 10 : 7, sbias = (scale_dtype == ORC_F16) ? 15 : 127;
+    for (int64_t t = 0; t < T; ++t) {
+        const int64_t v = ids[t];
+        for (int64_t k = 0; k < K; ++k) {
+            double p = 0.0;
+            if (v >= 0 && v < V) p = (double)q[v * K + k] * dec16(s[v * NG + k / G], sb, sbias);
+            const float f = (float)p; /* exact: the product fits in fp32 */
+            if (out_dtype == ORC_F32)
+                ((float*)out)[t * K + k] = f;
+            else if (out_dtype == ORC_F16)
+                ((uint16_t*)out)[t * K + k] = enc16(f, 10, 15);
+            else
+                ((uint16_t*)out)[t * K + k] = enc16(f, 7, 127);
         }
     }
     return ORC_OK;
