@@ -325,7 +325,8 @@ def main() -> int:
         tfl = F / (t_us * 1e-6) / 1e12
         per_call[f"M={M}"] = {
             "us": round(t_us, 3),
-            "kernel": {1: "gemv", 2: "mfma"}.get(args.path, "gemv" if M == 1 and w.K <= 32768 else "mfma"),
+            "kernel": {1: "gemv", 2: "mfma", 3: "mfma_lds"}.get(
+                args.path, "gemv" if M == 1 and w.K <= 32768 else ("mfma" if M <= 16 else "mfma_lds")),
             "algorithmic_bytes": B, "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
             "TFLOP/s": round(tfl, 2), "frac_mfma_f16_peak": round(tfl / MFMA_F16_PEAK_TFLOPS, 4),
         }
@@ -333,6 +334,17 @@ def main() -> int:
     per_call[f"top{args.topk}_rescore"] = {"us": round(rs_us, 3), "M": m_rs}
     fu_us = timed_loop(one_call, args.steps)
     per_call[f"logits+top{args.topk}_one_call"] = {"us": round(fu_us, 3), "M": m_rs}
+    # input-embedding gather from the same packed blob: one decode token and a
+    # 4096-token prefill, rows in the activation dtype
+    gen = torch.Generator(device="cpu").manual_seed(w.wid)
+    for T in (1, 4096):
+        ids = torch.randint(0, w.V, (T,), generator=gen, dtype=torch.int32).to(dev)
+        eo = torch.empty((T, w.K), dtype=TD[w.x_dtype], device=dev)
+        e_us = timed_loop(lambda i, ids=ids, eo=eo: lmh.embed(
+            ids, blobs[i % R], w.V, w.K, w.bits, w.group, sdt, out=eo), args.steps)
+        eb = T * (w.K * w.bits // 8 + (w.K // w.group) * 2 + w.K * 2 + 4)
+        per_call[f"embed_T={T}"] = {"us": round(e_us, 3), "algorithmic_bytes": eb,
+                                     "GB/s": round(eb / (e_us * 1e-6) / 1e9, 1)}
 
     m1 = per_call[f"M={Ms[0]}"]
     value = m1["us"]

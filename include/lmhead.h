@@ -161,6 +161,28 @@ int lmhead_quantize_pack(const void* w, int w_dtype, int64_t ldw, int64_t V, int
                          void* packed_out, void* stream);
 
 /*
+ * lmhead_embed -- the input-embedding lookup of a tied head, read from the
+ *   same packed blob the logits use:
+ *       out[t, k] = q[id, k] * s[id, k / G],   id = ids[t],
+ *   the product exact, rounded once to out_dtype (LMH_F32: exact; LMH_F16 /
+ *   LMH_BF16: nearest, ties to even; an fp16 result beyond its range becomes
+ *   +-inf).  vLLM PR #48870, Purpose: the quantized embedding table that
+ *   serves the input lookup is the one reused as the tied lm_head (that PR
+ *   keeps a second, gather-format copy; this layout serves both).
+ *   ids     [T] int32 token ids, device memory, 4-byte aligned.  An id outside
+ *           [0, V) yields a row of zeros (never an out-of-bounds read).
+ *   packed  blob of lmhead_pack / lmhead_quantize_pack for this (V, K, bits,
+ *           group); scale_dtype as it was quantized with.
+ *   out     [T, ldo] row-major, out_dtype LMH_F32 / LMH_F16 / LMH_BF16;
+ *           ldo >= K and each row 16-byte aligned (ldo % 4 == 0 for fp32,
+ *           % 8 for 16-bit).  Columns K..ldo-1 are not written.
+ *   T == 0 is a valid empty call.  Deterministic.
+ */
+int lmhead_embed(const int32_t* ids, int64_t T, const void* packed, int64_t V, int64_t K, int bits,
+                 int64_t group, int scale_dtype, void* out, int out_dtype, int64_t ldo,
+                 void* stream);
+
+/*
  * lmhead_logits_workspace_bytes -- device workspace that lmhead_logits needs
  *   for M rows of x: 0 for fp16 x; for bf16 x, room for x converted to fp16
  *   with a per-row power-of-two scale (M*K*2 and M*4 bytes, each rounded up

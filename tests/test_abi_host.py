@@ -216,3 +216,23 @@ def test_logits_topk_validation():
     assert n1 >= 75 * 9 * 8 + 151936 * 4 and n1 % 256 == 0
     assert L.lmhead_logits_topk_workspace_bytes(1, 151936, 1024, F16, 65) == 0
     assert L.lmhead_logits_topk_workspace_bytes(1, 151936, 1024, F32, 8) == 0
+
+
+def test_embed_validation():
+    L = lmh.lib()
+
+    def em(ids=P, T=4, packed=P, V=200, K=128, bits=4, G=64, sdt=F16, out=P, odt=F16, ldo=128):
+        return L.lmhead_embed(ids, T, packed, V, K, bits, G, sdt, out, odt, ldo, None)
+
+    assert em(bits=5) == E_UNSUP
+    assert em(K=100) == E_SHAPE
+    assert em(sdt=F32) == E_DTYPE
+    assert em(odt=7) == E_DTYPE
+    assert em(T=-1) == E_SHAPE
+    assert em(ldo=120) == E_SHAPE
+    assert em(ids=None) == E_NULL
+    assert em(out=None) == E_NULL
+    assert em(ids=P + 2) == E_ALIGN
+    assert em(out=P + 8) == E_ALIGN
+    assert em(ldo=132) == E_ALIGN                 # 16-bit rows must stay 16-byte aligned
+    assert em(T=0, ids=None, out=None) == OK

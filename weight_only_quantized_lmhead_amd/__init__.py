@@ -53,6 +53,7 @@ def lib() -> ctypes.CDLL:
             "lmhead_pack": (i32, [vp, vp, i64, i64, i32, i64, vp, vp]),
             "lmhead_quantize_pack": (i32, [vp, i32, i64, i64, i64, i32, i64, i32, i32, i64, i64,
                                            vp, vp]),
+            "lmhead_embed": (i32, [vp, i64, vp, i64, i64, i32, i64, i32, vp, i32, i64, vp]),
             "lmhead_logits_workspace_bytes": (sz, [i64, i64, i32]),
             "lmhead_logits": (i32, [vp, i32, i64, vp, i64, i64, i32, i64, i32, vp, vp, i64, vp,
                                     sz, vp]),
@@ -172,6 +173,26 @@ def quantize_pack_host(w: torch.Tensor, bits: int, group: int,
     return out
 
 
+def embed(ids: torch.Tensor, packed: torch.Tensor, V: int, K: int, bits: int, group: int,
+          scale_dtype: torch.dtype = torch.float16, out_dtype: torch.dtype = torch.float16,
+          out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Dequantized embedding rows [T, K] for int32 token ids -- lmhead_embed.
+    Ids outside [0, V) give zero rows."""
+    _need_cuda(ids, packed)
+    if ids.dtype != torch.int32:
+        raise ValueError("ids must be int32")
+    ids = ids.reshape(-1)
+    T = ids.numel()
+    if out is None:
+        out = torch.empty((T, K), dtype=out_dtype, device=packed.device)
+    elif not out.is_cuda or out.dim() != 2 or out.shape[0] != T or out.stride(1) != 1:
+        raise ValueError("out must be a [T, >=K] GPU tensor with unit column stride")
+    _check("lmhead_embed", lib().lmhead_embed(
+        _ptr(ids), T, _ptr(packed), V, K, bits, group, _DT[scale_dtype], _ptr(out), _DT[out.dtype],
+        out.stride(0), _stream(packed)))
+    return out
+
+
 def logits_workspace(M: int, K: int, x_dtype: torch.dtype, device) -> Optional[torch.Tensor]:
     n = int(lib().lmhead_logits_workspace_bytes(M, K, _DT[x_dtype]))
     return torch.empty(n, dtype=torch.uint8, device=device) if n else None
@@ -273,6 +294,11 @@ class QuantizedHead:
         self.V, self.K = w.shape
         self.bits, self.group, self.scale_dtype = bits, group, scale_dtype
         self.packed = quantize_pack(w, bits, group, scale_dtype, clip)
+
+    def embed(self, ids: torch.Tensor, out_dtype: torch.dtype = torch.float16) -> torch.Tensor:
+        """Input-embedding rows of the same packed table (tied head)."""
+        return embed(ids, self.packed, self.V, self.K, self.bits, self.group, self.scale_dtype,
+                     out_dtype)
 
     def __call__(self, x: torch.Tensor, bias: Optional[torch.Tensor] = None,
                  out: Optional[torch.Tensor] = None) -> torch.Tensor:

@@ -109,6 +109,25 @@ int lmhead_pack(const int8_t* q, const void* s, int64_t V, int64_t K, int bits, 
                                      (hipStream_t)stream));
 }
 
+int lmhead_embed(const int32_t* ids, int64_t T, const void* packed, int64_t V, int64_t K, int bits,
+                 int64_t group, int scale_dtype, void* out, int out_dtype, int64_t ldo,
+                 void* stream) {
+    const int rc = check_layout(V, K, bits, group);
+    if (rc != LMH_OK) return rc;
+    if (scale_dtype != F16 && scale_dtype != BF16) return LMH_E_DTYPE;
+    if (out_dtype != F32 && out_dtype != F16 && out_dtype != BF16) return LMH_E_DTYPE;
+    if (T < 0 || ldo < K) return LMH_E_SHAPE;
+    if (T == 0) return LMH_OK;
+    if (!ids || !packed || !out) return LMH_E_NULL;
+    if (!aligned16(packed) || !aligned16(out) || ((uintptr_t)ids & 3u) != 0) return LMH_E_ALIGN;
+    if (ldo % (out_dtype == F32 ? 4 : 8) != 0) return LMH_E_ALIGN;  // rows stay 16-byte aligned
+    // one thread per (token, 16-byte slot), 256 per workgroup
+    const int64_t threads = T * (K / lmh::span_of(bits)) * 4;
+    if ((threads + 255) / 256 >= (int64_t(1) << 31)) return LMH_E_UNSUPPORTED;
+    return from_hip(lmh::launch_embed(ids, T, (const uint8_t*)packed, V, K, bits, group,
+                                      scale_dtype, out, out_dtype, ldo, (hipStream_t)stream));
+}
+
 size_t lmhead_logits_workspace_bytes(int64_t M, int64_t K, int x_dtype) {
     if (x_dtype != BF16 || M <= 0 || K <= 0) return 0;
     return (size_t)(((M * K * 2 + 255) / 256) * 256 + ((M * 4 + 255) / 256) * 256);

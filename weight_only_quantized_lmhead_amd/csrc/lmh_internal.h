@@ -46,6 +46,10 @@ hipError_t launch_quantize(const void* w, int w_dtype, int64_t V, int64_t K, int
 hipError_t launch_quantize_pack(const void* w, int w_dtype, int64_t ldw, int64_t V, int64_t K,
                                 int bits, int64_t G, int scale_dtype, int nratios, int64_t row0,
                                 int64_t rows, uint8_t* blob, hipStream_t st);
+// Embedding rows of ids[0..T) from the blob into out (row stride ldo elements).
+hipError_t launch_embed(const int32_t* ids, int64_t T, const uint8_t* blob, int64_t V, int64_t K,
+                        int bits, int64_t G, int scale_dtype, void* out, int out_dtype, int64_t ldo,
+                        hipStream_t st);
 hipError_t launch_pack(const int8_t* q, const uint16_t* s, int64_t V, int64_t K, int bits,
                        int64_t G, uint8_t* out, hipStream_t st);
 

@@ -233,8 +233,9 @@ constexpr int kSearchN = 16;  // columns per step of the search
 // chains interleave instead of running one after another.
 template <int BITS, bool UNROLL, class Get>
 __device__ __forceinline__ float pick_scale(const Get& get, int G, const QCfg& cf, bool& zero) {
+    constexpr int kU = UNROLL ? 16 : 1;  // held groups: fully unrolled; streamed: rolled
     float amax = 0.0f;
-#pragma unroll(UNROLL ? 16 : 1)
+#pragma unroll kU
     for (int k = 0; k < G; k += 32) {
         float w[32];
         get.template operator()<32>(k, w);
@@ -251,7 +252,7 @@ __device__ __forceinline__ float pick_scale(const Get& get, int G, const QCfg& c
         rr[i] = 1.0 / (double)sv[i];
         err[i] = 0.0;
     }
-#pragma unroll(UNROLL ? 16 : 1)
+#pragma unroll kU
     for (int k = 0; k < G; k += kSearchN) {
         float w[kSearchN];
         get.template operator()<kSearchN>(k, w);
