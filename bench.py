@@ -178,7 +178,7 @@ def main() -> int:
     ap.add_argument("--workload", default=None, help="synthetic workload name (default: the headline)")
     ap.add_argument("--ms", default=None, help="comma-separated M list (default: the workload's)")
     ap.add_argument("--topk", type=int, default=8)
-    ap.add_argument("--path", type=int, default=0, help="0 automatic, 1 force the GEMV, 2 force the MFMA kernel")
+    ap.add_argument("--path", type=int, default=0, help="0 automatic, 1 GEMV, 2 register-fed MFMA, 3 LDS-staged MFMA, 4 activation-resident MFMA")
     ap.add_argument("--hot", action="store_true", help="reuse one copy of the head (cache-hot; labelled)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -316,6 +316,16 @@ def main() -> int:
         torch.cuda.synchronize()
         return a_.elapsed_time(b_) / n * 1e3  # us per call
 
+    def auto_kernel(M):
+        # the library's automatic choice (lmhead_logits)
+        if M == 1 and w.K <= 32768:
+            return "gemv"
+        if M <= 16:
+            return "mfma"
+        if M > 32 and w.bits == 4 and w.group >= 64 and w.K <= 1024:
+            return "mfma_xres"
+        return "mfma_lds"
+
     per_call = {}
     for M in Ms:
         t_us = timed_loop(lambda i, M=M: call(M, i), args.steps)
@@ -325,8 +335,7 @@ def main() -> int:
         tfl = F / (t_us * 1e-6) / 1e12
         per_call[f"M={M}"] = {
             "us": round(t_us, 3),
-            "kernel": {1: "gemv", 2: "mfma", 3: "mfma_lds"}.get(
-                args.path, "gemv" if M == 1 and w.K <= 32768 else ("mfma" if M <= 16 else "mfma_lds")),
+            "kernel": {1: "gemv", 2: "mfma", 3: "mfma_lds", 4: "mfma_xres"}.get(args.path, auto_kernel(M)),
             "algorithmic_bytes": B, "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
             "TFLOP/s": round(tfl, 2), "frac_mfma_f16_peak": round(tfl / MFMA_F16_PEAK_TFLOPS, 4),
         }

@@ -207,11 +207,12 @@ size_t lmhead_logits_workspace_bytes(int64_t M, int64_t K, int x_dtype);
  *           (may be NULL/0 for fp16 x).
  *   M = 1 runs a GEMV with one lane per vocabulary row (all of K per wave);
  *   M >= 2 runs a 16x16x32 fp16 MFMA kernel (its code unpacking is shared by
- *   all activation rows): the register-fed one for M <= 16, the LDS-staged
- *   one from M = 17 on (see lmhead_logits_path).  Every kernel runs the same
- *   per-group MFMA chains and fp32 scale FMAs in the same order, so the two
- *   MFMA kernels give bit-identical results.  The result does not depend on
- *   the stream or on other calls.
+ *   all activation rows): the register-fed one for M <= 16, from M = 17 on
+ *   the LDS-staged one, and from M = 33 on, for int4 with G >= 64 and
+ *   K <= 1024, the activation-resident one (see lmhead_logits_path).  Every
+ *   MFMA kernel runs the same per-group MFMA chains and fp32 scale FMAs in
+ *   the same order, so they give bit-identical results.  The result does not
+ *   depend on the stream or on other calls.
  */
 int lmhead_logits(const void* x, int x_dtype, int64_t M, const void* packed, int64_t V, int64_t K,
                   int bits, int64_t group, int scale_dtype, const float* bias, float* y,
@@ -223,8 +224,11 @@ int lmhead_logits(const void* x, int x_dtype, int64_t M, const void* packed, int
  *   (M <= 4, else LMH_E_UNSUPPORTED), 2 = the MFMA kernel with B operands
  *   loaded straight into registers (any M), 3 = the MFMA kernel with every
  *   operand staged in LDS by direct global-to-LDS loads (any M; 32 or 64
- *   activation rows per workgroup).  All kernels compute the same function;
- *   this entry point exists to test and time each of them on the same shapes.
+ *   activation rows per workgroup), 4 = the activation-resident MFMA kernel
+ *   (a 64-row activation tile held in LDS for the workgroup's life, weights
+ *   streamed through registers; K <= 1024, else LMH_E_UNSUPPORTED).  All
+ *   kernels compute the same function; this entry point exists to test and
+ *   time each of them on the same shapes.
  */
 int lmhead_logits_path(const void* x, int x_dtype, int64_t M, const void* packed, int64_t V,
                        int64_t K, int bits, int64_t group, int scale_dtype, const float* bias,

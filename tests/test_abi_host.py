@@ -89,7 +89,7 @@ def test_logits_validation():
     assert _logits(xd=BF16) == E_WS           # bf16 x needs the conversion workspace
     assert _logits(xd=BF16, ws=P, wsn=16) == E_WS
     assert _logits(path=1, M=5) == E_UNSUP   # the GEMV serves M <= 4
-    assert _logits(path=4) == E_UNSUP
+    assert _logits(path=5) == E_UNSUP
     # empty requests are valid and launch nothing
     assert _logits(M=0) == OK
     assert _logits(V=0) == OK

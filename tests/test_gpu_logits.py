@@ -1,5 +1,5 @@
-"""GPU logits (GEMV and both MFMA kernels) against the fp64 oracle on small heads that
-still span several row blocks, several superchunks per wave and a ragged tail."""
+"""GPU logits (GEMV and the three MFMA kernels) against the fp64 oracle on small heads
+that still span several row blocks, several superchunks per wave and a ragged tail."""
 import numpy as np
 import pytest
 import torch
@@ -11,7 +11,7 @@ from gpu_common import DEV, OD, TD, abs_terms, bits16, check_logits, gpu, need_g
 
 pytestmark = gpu
 
-GEMV, MFMA, LDS = lmh.PATH_GEMV, lmh.PATH_MFMA, lmh.PATH_MFMA_LDS
+GEMV, MFMA, LDS, XRES = lmh.PATH_GEMV, lmh.PATH_MFMA, lmh.PATH_MFMA_LDS, lmh.PATH_MFMA_XRES
 
 
 def _head(V, K, bits, G, sdt, seed, zero_rows=()):
@@ -45,7 +45,7 @@ CASES = [  # bits, G, K
 @pytest.mark.parametrize("bits,G,K", CASES)
 @pytest.mark.parametrize("xdt,sdt", [("f16", "f16"), ("bf16", "bf16"), ("f16", "bf16")])
 @pytest.mark.parametrize("path,Ms", [(GEMV, (1, 2, 3, 4)), (MFMA, (1, 5, 16, 17, 40, 67)),
-                                     (LDS, (1, 5, 64, 65, 130))])
+                                     (LDS, (1, 5, 64, 65, 130)), (XRES, (1, 7, 64, 65, 130))])
 def test_logits_small_vs_oracle(bits, G, K, xdt, sdt, path, Ms):
     need_gpu()
     V = 64 * 5 + 37
@@ -60,7 +60,8 @@ def test_logits_small_vs_oracle(bits, G, K, xdt, sdt, path, Ms):
     print(f"bits={bits} G={G} K={K} x={xdt} s={sdt} path={path}: max row rel err {worst:.2e}")
 
 
-@pytest.mark.parametrize("path,M", [(GEMV, 1), (GEMV, 3), (MFMA, 8), (MFMA, 33), (LDS, 20), (LDS, 70)])
+@pytest.mark.parametrize("path,M", [(GEMV, 1), (GEMV, 3), (MFMA, 8), (MFMA, 33), (LDS, 20), (LDS, 70),
+                                    (XRES, 3), (XRES, 70)])
 def test_bias_and_row_stride(path, M):
     need_gpu()
     V, K, bits, G = 200, 512, 4, 64
@@ -74,7 +75,7 @@ def test_bias_and_row_stride(path, M):
 
 
 @pytest.mark.parametrize("bits,G", [(4, 64), (4, 128), (8, 128), (8, 32)])
-@pytest.mark.parametrize("path", [GEMV, MFMA, LDS])
+@pytest.mark.parametrize("path", [GEMV, MFMA, LDS, XRES])
 def test_one_hot_exposes_layout(bits, G, path):
     """x = e_k gives y[v] = q[v,k] * s[v, k/G] exactly (one exact product): any
     misplaced nibble, byte, slot or scale shows up bit for bit."""
@@ -94,7 +95,8 @@ def test_one_hot_exposes_layout(bits, G, path):
             assert np.array_equal(y[m].astype(np.float64), want), f"column {k}"
 
 
-@pytest.mark.parametrize("path,M", [(GEMV, 1), (GEMV, 4), (MFMA, 16), (MFMA, 64), (LDS, 64), (LDS, 128)])
+@pytest.mark.parametrize("path,M", [(GEMV, 1), (GEMV, 4), (MFMA, 16), (MFMA, 64), (LDS, 64), (LDS, 128),
+                                    (XRES, 64), (XRES, 200)])
 def test_invariants_zero_rows_scaling_determinism(path, M):
     need_gpu()
     V, K, bits, G = 320, 512, 4, 64
@@ -124,9 +126,10 @@ def test_gemv_and_mfma_agree():
 
 @pytest.mark.parametrize("bits,G", [(4, 32), (4, 64), (4, 256), (8, 64), (8, 128)])
 def test_mfma_kernels_bit_identical(bits, G):
-    """The register-fed and LDS-staged MFMA kernels run the same per-group
-    MFMA chains and the same fp32 scale FMAs in the same order: bit-identical,
-    across activation-tile boundaries and a ragged vocabulary tail."""
+    """The register-fed, LDS-staged and activation-resident MFMA kernels run
+    the same per-group MFMA chains and the same fp32 scale FMAs in the same
+    order: bit-identical, across activation-tile boundaries and a ragged
+    vocabulary tail."""
     need_gpu()
     V, K = 64 * 9 + 21, 512
     q, s, blob = _head(V, K, bits, G, "f16", seed=41 + G)
@@ -135,6 +138,8 @@ def test_mfma_kernels_bit_identical(bits, G):
         a = _run(x, "f16", blob, V, K, bits, G, "f16", MFMA)
         b = _run(x, "f16", blob, V, K, bits, G, "f16", LDS)
         assert np.array_equal(a, b), f"M={M}"
+        c = _run(x, "f16", blob, V, K, bits, G, "f16", XRES)
+        assert np.array_equal(a, c), f"M={M} (activation-resident)"
 
 
 def test_bf16_activations_large_and_small_rows():
@@ -148,7 +153,7 @@ def test_bf16_activations_large_and_small_rows():
     xf[1] *= 1e-6
     xf[2, 5] = 3e4
     x = synth.to_bf16_bits(xf)
-    for path in (GEMV, MFMA, LDS):
+    for path in (GEMV, MFMA, LDS, XRES):
         y = _run(x, "bf16", blob, V, K, bits, G, "bf16", path)
         y_or = oracle.logits(x, q, s, oracle.BF16, G, x_dtype=oracle.BF16)
         y_abs = abs_terms(x, "bf16", q, s, oracle.BF16, G)

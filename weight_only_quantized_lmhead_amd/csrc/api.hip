@@ -142,7 +142,7 @@ static int logits_impl(const void* x, int x_dtype, int64_t M, const void* packed
     if (x_dtype != F16 && x_dtype != BF16) return LMH_E_DTYPE;
     if (scale_dtype != F16 && scale_dtype != BF16) return LMH_E_DTYPE;
     if (M < 0 || M > 65535) return LMH_E_SHAPE;
-    if (path < 0 || path > 3) return LMH_E_UNSUPPORTED;
+    if (path < 0 || path > 4) return LMH_E_UNSUPPORTED;
     if (M == 0 || V == 0) return LMH_OK;
     if (ldy < V) return LMH_E_SHAPE;
     if (!x || !packed || !y) return LMH_E_NULL;
@@ -157,6 +157,7 @@ static int logits_impl(const void* x, int x_dtype, int64_t M, const void* packed
     if ((V + 255) / 256 * ((M + 15) / 16) >= (int64_t(1) << 30)) return LMH_E_UNSUPPORTED;
     const bool gemv_ok = M <= lmh::kGemvMaxM && M * K <= lmh::kGemvMaxMK;
     if (path == 1 && !gemv_ok) return LMH_E_UNSUPPORTED;
+    if (path == 4 && !lmh::xres_fits(K)) return LMH_E_UNSUPPORTED;
 
     hipStream_t st = (hipStream_t)stream;
     lmh::LogitsArgs a;
@@ -182,8 +183,14 @@ static int logits_impl(const void* x, int x_dtype, int64_t M, const void* packed
     a.scale_bf16 = scale_dtype == BF16;
     const bool use_gemv = path == 1 || (path == 0 && gemv_ok && M <= lmh::kGemvAutoMaxM);
     if (use_gemv) return from_hip(lmh::launch_gemv(a, st));
-    // automatic: the LDS-staged kernel where it measured fastest (from 17
-    // rows on, on the 151936 x 1024 int4 head), the register-fed one for 2..16
+    // automatic, from measurements on the 151936 x 1024 heads: the register-fed
+    // MFMA kernel for 2..16 rows; from 33 rows the activation-resident kernel
+    // for int4 with groups of 64 or more (M = 64..256: 5-19 % faster than the
+    // LDS-staged one; with 32-column groups it runs out of registers), else
+    // the LDS-staged kernel (int8: equal or faster)
+    const bool use_xres = path == 4 || (path == 0 && M > 32 && bits == 4 && group >= 64 &&
+                                        lmh::xres_fits(K));
+    if (use_xres) return from_hip(lmh::launch_mfma_xres(a, st));
     const bool use_lds = path == 3 || (path == 0 && M > 16);
     return from_hip(use_lds ? lmh::launch_mfma_lds(a, st) : lmh::launch_mfma(a, st));
 }

@@ -68,6 +68,9 @@ hipError_t launch_x_to_f16(const uint16_t* x_bf16, int M, int K, _Float16* xh, i
                            hipStream_t st);
 hipError_t launch_gemv(const LogitsArgs& a, hipStream_t st);
 hipError_t launch_mfma(const LogitsArgs& a, hipStream_t st);
+// Activation-resident MFMA kernel for large M; needs K <= xres max (xres_fits).
+bool xres_fits(int64_t K);
+hipError_t launch_mfma_xres(const LogitsArgs& a, hipStream_t st);
 hipError_t launch_mfma_lds(const LogitsArgs& a, hipStream_t st);
 hipError_t launch_dense(const void* x, int dtype, int M, const void* w, int64_t V, int64_t K,
                         float* y, int64_t ldy, hipStream_t st);

@@ -684,6 +684,175 @@ void mfma_lds_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Activation-resident MFMA kernel (large M, K <= kXresMaxK).  A workgroup of 8
+// waves loads one 64-row activation tile x[m0 .. m0+63, 0 .. K) into LDS once
+// (16-byte pieces swizzled as in mfma_lds_kernel) and then sweeps a
+// contiguous range of row blocks, one block per wave at a time, with no
+// further barrier: each wave streams its blocks' weight slots and scales
+// through a D-deep register ring (loads past its last step are clamped to
+// that step and their contribution dropped, so every load is unconditional
+// and the wait counts stay exact), reads its A operands from the resident
+// tile, and stores a block's 64 x 64 results as soon as its last superchunk
+// is done.  The workgroups of one XCD cover NMT activation tiles times VRX
+// vocabulary ranges with the NMT tiles of a range side by side, so a weight
+// slot comes from HBM once and from that XCD's L2 for the other tiles.
+constexpr int kXresMaxK = 1024;
+
+template <int BITS, int GPS, int D>
+__global__ __launch_bounds__(512, 1) void mfma_xres_kernel(
+    const uint4* __restrict__ wq, const uint16_t* __restrict__ sc, const _Float16* __restrict__ x,
+    const int* __restrict__ xexp, const float* __restrict__ bias, float* __restrict__ y,
+    int64_t ldy, int V, int K, int M, int NB, int NC, int NG, int SPG, int sbf16, int NMT,
+    int VRX) {
+    constexpr int MT = 4, NT = 4, ROWS = 64;
+    constexpr int SPAN = BITS == 4 ? 128 : 64;
+    constexpr int CPS = SPAN / 32;
+    constexpr int CPG = CPS / GPS;
+    constexpr int WPG = BITS == 4 ? CPG : 2 * CPG;  // 32-bit code words per group and slot
+    __shared__ uint4 xs[ROWS * kXresMaxK / 8];
+    __shared__ int xe_s[ROWS];  // power-of-two row exponents of the tile (bf16 x)
+
+    const int xcd = blockIdx.x & 7, l = blockIdx.x >> 3;
+    const int mtile = l % NMT, vr = xcd * VRX + l / NMT;
+    const int NV = 8 * VRX;
+    const int rb0 = (int)((int64_t)NB * vr / NV), rb1 = (int)((int64_t)NB * (vr + 1) / NV);
+    const int m0 = mtile * ROWS;
+    const int P = K / 8;                       // 16-byte pieces per row
+    const int msk = (P & 15) == 0 ? 15 : 7;    // piece p of row m sits at p ^ (m & msk)
+    for (int i = threadIdx.x; i < ROWS * P; i += 512) {
+        const int m = i / P, p = i - m * P;
+        const int mr = min(m0 + m, M - 1);     // rows past M: any valid row, never stored
+        xs[m * P + (p ^ (m & msk))] = *(const uint4*)(x + (int64_t)mr * K + p * 8);
+    }
+    if (xexp && threadIdx.x < ROWS) xe_s[threadIdx.x] = xexp[min(m0 + (int)threadIdx.x, M - 1)];
+    __syncthreads();
+
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int r = lane & 15, t = lane >> 4;
+    const int nblk = rb1 - rb0 > wv ? (rb1 - rb0 - wv + 7) / 8 : 0;
+    const int nsteps = nblk * NC;
+    if (nsteps == 0) return;
+
+    // ring stage: the 4 slots and their scales
+    uint4 wbuf[D][NT];
+    uint16_t sbuf[D][GPS][NT];
+    auto load = [&](int p, int s) {
+        const int sl = min(s, nsteps - 1);
+        const int i = sl / NC, c = sl - i * NC;
+        const int blk = rb0 + wv + 8 * i;
+        const uint4* wp = wq + ((int64_t)blk * NC + c) * 256 + t * 64 + r;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) wbuf[p][nt] = wp[16 * nt];
+        const int g0 = GPS > 1 ? c * GPS : c / SPG;
+        const uint16_t* sp = sc + ((int64_t)blk * NG + g0) * 64 + r;
+#pragma unroll
+        for (int g = 0; g < GPS; ++g)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) sbuf[p][g][nt] = sp[g * 64 + 16 * nt];
+    };
+
+    f4 acc[MT][NT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = (f4){0.f, 0.f, 0.f, 0.f};
+    const uint32_t magic = 0x64006400u;
+
+#pragma unroll
+    for (int p = 0; p < D; ++p) load(p, p);
+    int ci = 0, cc = 0;  // block index within the wave's list, superchunk of step s
+    for (int sb = 0; sb < nsteps; sb += D) {
+#pragma unroll
+        for (int p = 0; p < D; ++p) {
+            const int s = sb + p;
+            const bool real = s < nsteps;
+#pragma unroll
+            for (int g = 0; g < GPS; ++g) {
+                h8 bop[NT][CPG];
+                float sv[NT];
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+                    for (int jj = 0; jj < CPG; ++jj) {
+                        h2 p0, p1, p2, p3;
+                        if constexpr (BITS == 4) {
+                            unpack_i4(word_of(wbuf[p][nt], g * WPG + jj), magic, p0, p1, p2, p3);
+                        } else {
+                            unpack_i8(word_of(wbuf[p][nt], g * WPG + 2 * jj), p0, p1);
+                            unpack_i8(word_of(wbuf[p][nt], g * WPG + 2 * jj + 1), p2, p3);
+                        }
+                        bop[nt][jj] = (h8){p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+                    }
+                    sv[nt] = real ? scale_to_f32(sbuf[p][g][nt], sbf16) : 0.0f;
+                }
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const int m = 16 * mt + r;
+                    h8 a[CPG];
+#pragma unroll
+                    for (int jj = 0; jj < CPG; ++jj) {
+                        const int pc = cc * (SPAN / 8) + 4 * (g * CPG + jj) + t;
+                        a[jj] = __builtin_bit_cast(h8, xs[m * P + (pc ^ (m & msk))]);
+                    }
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) {
+                        f4 q = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[0], bop[nt][0],
+                                                                       (f4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+                        for (int jj = 1; jj < CPG; ++jj)
+                            q = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[jj], bop[nt][jj], q, 0, 0, 0);
+                        acc[mt][nt] += sv[nt] * q;
+                    }
+                    // one activation tile at a time: the scheduler would
+                    // otherwise read every tile's A operands up front and spill
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            load(p, s + D);
+            if (real && cc == NC - 1) {
+                // the block's results: y[m, v] = acc * 2^xexp[m] + bias[v] for
+                // rows m = m0 + 16 mt + 4 t + e and columns v = blk * 64 + 16 nt + r,
+                // through one row pointer that steps down the lane's rows
+                const int blk = rb0 + wv + 8 * ci;
+                const int vlim = V - blk * 64 - r;  // 16 nt < vlim: column inside V
+                int mlim = M - m0 - 4 * t;          // 16 mt + e < mlim: row inside M
+                // (kept opaque so the row tests stay here instead of being
+                // hoisted out of the loop, where they would pin 32 SGPRs)
+                asm volatile("" : "+v"(mlim));
+                float bv[NT];
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+                    bv[nt] = (bias && 16 * nt < vlim) ? bias[blk * 64 + 16 * nt + r] : 0.0f;
+                float* yrow = y + (int64_t)(m0 + 4 * t) * ldy + (int64_t)blk * 64 + r;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const bool rowok = 16 * mt + e < mlim;
+                        const int xe = xexp ? xe_s[16 * mt + 4 * t + e] : 0;
+#pragma unroll
+                        for (int nt = 0; nt < NT; ++nt) {
+                            if (rowok && 16 * nt < vlim) {
+                                float o = acc[mt][nt][e];
+                                if (xexp) o = ldexpf(o, xe);
+                                yrow[16 * nt] = o + bv[nt];
+                            }
+                            acc[mt][nt][e] = 0.0f;
+                        }
+                        yrow += ldy;
+                    }
+                    yrow += 12 * ldy;  // the lane's next rows are 16 further on
+                }
+            }
+            if (++cc == NC) {
+                cc = 0;
+                ++ci;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Dense 16-bit control GEMV: a wave computes 4 rows at a time; lane l covers
 // columns 8l + 512i; partial sums meet in a fixed xor-shuffle tree.
 template <int DT, int MM>
@@ -855,6 +1024,31 @@ hipError_t mfma_lds_dispatch(const LogitsArgs& a, hipStream_t st) {
     return mfma_lds_dispatch_mt<BITS, 4, 2, 4>(a, st);
 }
 
+template <int BITS, int D>
+hipError_t mfma_xres_dispatch_d(const LogitsArgs& a, hipStream_t st) {
+    const int NB = (int)((a.V + 63) / 64);
+    const int NC = (int)(a.K / span_of(BITS));
+    const int NG = (int)(a.K / a.G);
+    const int gps = gps_of(BITS, a.G);
+    const int SPG = gps == 1 ? (int)(a.G / span_of(BITS)) : 1;
+    const uint4* wq = (const uint4*)a.packed;
+    const uint16_t* sc = (const uint16_t*)(a.packed + (int64_t)NB * 64 * a.K * BITS / 8);
+    const int NMT = (a.M + 63) / 64;
+    // one workgroup per CU: per XCD, NMT activation tiles x VRX vocabulary ranges
+    const int VRX = NMT >= 32 ? 1 : 32 / NMT;
+    const dim3 grid((unsigned)(8 * NMT * VRX));
+#define LMH_XRES(G_)                                                                              \
+    hipLaunchKernelGGL((mfma_xres_kernel<BITS, G_, D>), grid, dim3(512), 0, st, wq, sc,          \
+                       (const _Float16*)a.x, a.xexp, a.bias, a.y, a.ldy, (int)a.V, (int)a.K, a.M, \
+                       NB, NC, NG, SPG, a.scale_bf16, NMT, VRX)
+    if (gps == 1) LMH_XRES(1);
+    else if constexpr (BITS == 8) LMH_XRES(2);
+    else if (gps == 2) LMH_XRES(2);
+    else LMH_XRES(4);
+#undef LMH_XRES
+    return hipGetLastError();
+}
+
 template <int BITS>
 hipError_t mfma_dispatch(const LogitsArgs& a, hipStream_t st) {
     // one 16-row activation tile for M <= 16; two (32 rows) otherwise: the
@@ -882,6 +1076,16 @@ hipError_t launch_mfma(const LogitsArgs& a, hipStream_t st) {
 
 hipError_t launch_mfma_lds(const LogitsArgs& a, hipStream_t st) {
     return a.bits == 4 ? mfma_lds_dispatch<4>(a, st) : mfma_lds_dispatch<8>(a, st);
+}
+
+bool xres_fits(int64_t K) { return K <= kXresMaxK; }
+
+hipError_t launch_mfma_xres(const LogitsArgs& a, hipStream_t st) {
+#ifndef LMH_XRES_D
+#define LMH_XRES_D 3
+#endif
+    return a.bits == 4 ? mfma_xres_dispatch_d<4, LMH_XRES_D>(a, st)
+                       : mfma_xres_dispatch_d<8, LMH_XRES_D>(a, st);
 }
 
 hipError_t launch_dense(const void* x, int dtype, int M, const void* w, int64_t V, int64_t K,
