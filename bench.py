@@ -322,7 +322,7 @@ def main() -> int:
             return "gemv"
         if M <= 16:
             return "mfma"
-        if M > 32 and w.bits == 4 and w.group >= 64 and w.K <= 1024:
+        if M > 32 and w.K <= 1024 and (w.bits == 8 or w.group >= 64):
             return "mfma_xres"
         return "mfma_lds"
 

@@ -184,12 +184,12 @@ static int logits_impl(const void* x, int x_dtype, int64_t M, const void* packed
     const bool use_gemv = path == 1 || (path == 0 && gemv_ok && M <= lmh::kGemvAutoMaxM);
     if (use_gemv) return from_hip(lmh::launch_gemv(a, st));
     // automatic, from measurements on the 151936 x 1024 heads: the register-fed
-    // MFMA kernel for 2..16 rows; from 33 rows the activation-resident kernel
-    // for int4 with groups of 64 or more (M = 64..256: 5-19 % faster than the
-    // LDS-staged one; with 32-column groups it runs out of registers), else
-    // the LDS-staged kernel (int8: equal or faster)
-    const bool use_xres = path == 4 || (path == 0 && M > 32 && bits == 4 && group >= 64 &&
-                                        lmh::xres_fits(K));
+    // MFMA kernel for 2..16 rows, the LDS-staged one for 17..32, and from 33
+    // rows the activation-resident kernel (M = 64..256: 6-18 % faster than the
+    // LDS-staged one for int4 g64 and int8 g128) unless K > 1024 or an int4
+    // head has 32-column groups (it runs out of registers there)
+    const bool use_xres = path == 4 || (path == 0 && M > 32 && lmh::xres_fits(K) &&
+                                        (bits == 8 || group >= 64));
     if (use_xres) return from_hip(lmh::launch_mfma_xres(a, st));
     const bool use_lds = path == 3 || (path == 0 && M > 16);
     return from_hip(use_lds ? lmh::launch_mfma_lds(a, st) : lmh::launch_mfma(a, st));

@@ -27,6 +27,8 @@
 //                review comment, point 1).
 #include "lmh_internal.h"
 
+#include <type_traits>
+
 #include <math.h>
 
 namespace lmh {
@@ -698,7 +700,7 @@ void mfma_lds_kernel(
 // slot comes from HBM once and from that XCD's L2 for the other tiles.
 constexpr int kXresMaxK = 1024;
 
-template <int BITS, int GPS, int D>
+template <int BITS, int GPS, int D, bool TR>
 __global__ __launch_bounds__(512, 1) void mfma_xres_kernel(
     const uint4* __restrict__ wq, const uint16_t* __restrict__ sc, const _Float16* __restrict__ x,
     const int* __restrict__ xexp, const float* __restrict__ bias, float* __restrict__ y,
@@ -729,13 +731,18 @@ __global__ __launch_bounds__(512, 1) void mfma_xres_kernel(
 
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int r = lane & 15, t = lane >> 4;
+    // 16-byte output stores need 16-byte aligned rows
+    const bool vec16 = ((uintptr_t)y & 15) == 0 && (ldy & 3) == 0;
     const int nblk = rb1 - rb0 > wv ? (rb1 - rb0 - wv + 7) / 8 : 0;
     const int nsteps = nblk * NC;
     if (nsteps == 0) return;
 
-    // ring stage: the 4 slots and their scales
+    // ring stage: the 4 slots, and per group and column tile the scales of the
+    // lane's vocabulary rows: row 16 nt + r (one 2-byte load), or with TR the
+    // 4 rows 16 nt + 4 t .. + 3 (one 8-byte load)
+    using SW = typename std::conditional<TR, uint2, uint16_t>::type;
     uint4 wbuf[D][NT];
-    uint16_t sbuf[D][GPS][NT];
+    SW sbuf[D][GPS][NT];
     auto load = [&](int p, int s) {
         const int sl = min(s, nsteps - 1);
         const int i = sl / NC, c = sl - i * NC;
@@ -744,11 +751,11 @@ __global__ __launch_bounds__(512, 1) void mfma_xres_kernel(
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) wbuf[p][nt] = wp[16 * nt];
         const int g0 = GPS > 1 ? c * GPS : c / SPG;
-        const uint16_t* sp = sc + ((int64_t)blk * NG + g0) * 64 + r;
+        const uint16_t* sp = sc + ((int64_t)blk * NG + g0) * 64 + (TR ? 4 * t : r);
 #pragma unroll
         for (int g = 0; g < GPS; ++g)
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) sbuf[p][g][nt] = sp[g * 64 + 16 * nt];
+            for (int nt = 0; nt < NT; ++nt) sbuf[p][g][nt] = *(const SW*)(sp + g * 64 + 16 * nt);
     };
 
     f4 acc[MT][NT];
@@ -769,7 +776,7 @@ __global__ __launch_bounds__(512, 1) void mfma_xres_kernel(
 #pragma unroll
             for (int g = 0; g < GPS; ++g) {
                 h8 bop[NT][CPG];
-                float sv[NT];
+                f4 sv[NT];  // the scale of each of the lane's 4 result elements
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
@@ -783,33 +790,104 @@ __global__ __launch_bounds__(512, 1) void mfma_xres_kernel(
                         }
                         bop[nt][jj] = (h8){p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
                     }
-                    sv[nt] = real ? scale_to_f32(sbuf[p][g][nt], sbf16) : 0.0f;
+                    if constexpr (TR) {
+                        const uint2 sw = sbuf[p][g][nt];
+                        sv[nt] = real ? (f4){scale_to_f32((uint16_t)sw.x, sbf16),
+                                             scale_to_f32((uint16_t)(sw.x >> 16), sbf16),
+                                             scale_to_f32((uint16_t)sw.y, sbf16),
+                                             scale_to_f32((uint16_t)(sw.y >> 16), sbf16)}
+                                      : (f4){0.f, 0.f, 0.f, 0.f};
+                    } else {
+                        const float v1 = real ? scale_to_f32(sbuf[p][g][nt], sbf16) : 0.0f;
+                        sv[nt] = (f4){v1, v1, v1, v1};
+                    }
                 }
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
+                // activation tiles in a software pipeline: the MFMA chains of
+                // tile mt are issued before the scale FMAs of tile mt - 1 read
+                // their results, so the chains' latency is hidden
+                auto read_a = [&](int mt, h8 (&a)[CPG]) {
                     const int m = 16 * mt + r;
-                    h8 a[CPG];
 #pragma unroll
                     for (int jj = 0; jj < CPG; ++jj) {
                         const int pc = cc * (SPAN / 8) + 4 * (g * CPG + jj) + t;
                         a[jj] = __builtin_bit_cast(h8, xs[m * P + (pc ^ (m & msk))]);
                     }
+                };
+                f4 pq[2][NT];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    h8 a[CPG];
+                    read_a(mt, a);
 #pragma unroll
                     for (int nt = 0; nt < NT; ++nt) {
-                        f4 q = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[0], bop[nt][0],
-                                                                       (f4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                        // D[4t + e][r] holds activation row 16 mt + 4 t + e and
+                        // vocabulary row 16 nt + r; with TR (weights as the A
+                        // operand) vocabulary row 16 nt + 4 t + e and activation
+                        // row 16 mt + r.  Same products, same sums, either way.
+                        f4 q = TR ? __builtin_amdgcn_mfma_f32_16x16x32_f16(bop[nt][0], a[0],
+                                                                            (f4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0)
+                                  : __builtin_amdgcn_mfma_f32_16x16x32_f16(a[0], bop[nt][0],
+                                                                            (f4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
                         for (int jj = 1; jj < CPG; ++jj)
-                            q = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[jj], bop[nt][jj], q, 0, 0, 0);
-                        acc[mt][nt] += sv[nt] * q;
+                            q = TR ? __builtin_amdgcn_mfma_f32_16x16x32_f16(bop[nt][jj], a[jj], q, 0, 0, 0)
+                                   : __builtin_amdgcn_mfma_f32_16x16x32_f16(a[jj], bop[nt][jj], q, 0, 0, 0);
+                        pq[mt & 1][nt] = q;
                     }
-                    // one activation tile at a time: the scheduler would
-                    // otherwise read every tile's A operands up front and spill
-                    __builtin_amdgcn_sched_barrier(0);
+                    if (mt > 0) {
+#pragma unroll
+                        for (int nt = 0; nt < NT; ++nt) acc[mt - 1][nt] += sv[nt] * pq[(mt - 1) & 1][nt];
+                    }
                 }
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) acc[MT - 1][nt] += sv[nt] * pq[(MT - 1) & 1][nt];
             }
             load(p, s + D);
             if (real && cc == NC - 1) {
+                if constexpr (TR) {
+                // the block's results: y[m, v] = acc * 2^xexp[m] + bias[v] for
+                // row m = m0 + 16 mt + r and the 4 columns v = blk*64 + 16 nt +
+                // 4 t + e, e = 0..3, contiguous: one 16-byte store each (when
+                // y's rows are 16-byte aligned and all 4 columns exist)
+                const int blk = rb0 + wv + 8 * ci;
+                const int vlim = V - blk * 64 - 4 * t;  // 16 nt + e < vlim: column inside V
+                int mlim = M - m0 - r;                  // 16 mt < mlim: row inside M
+                // (kept opaque so the row tests stay here instead of being
+                // hoisted out of the loop)
+                asm volatile("" : "+v"(mlim));
+                f4 bv[NT];
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        bv[nt][e] = (bias && 16 * nt + e < vlim) ? bias[blk * 64 + 16 * nt + 4 * t + e] : 0.0f;
+                float* yrow = y + (int64_t)(m0 + r) * ldy + (int64_t)blk * 64 + 4 * t;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    if (16 * mt < mlim) {
+                        const int xe = xexp ? xe_s[16 * mt + r] : 0;
+#pragma unroll
+                        for (int nt = 0; nt < NT; ++nt) {
+                            f4 o = acc[mt][nt];
+                            if (xexp) {
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) o[e] = ldexpf(o[e], xe);
+                            }
+                            o = o + bv[nt];
+                            if (vec16 && 16 * nt + 3 < vlim) {
+                                *(f4*)(yrow + 16 * nt) = o;
+                            } else {
+#pragma unroll
+                                for (int e = 0; e < 4; ++e)
+                                    if (16 * nt + e < vlim) yrow[16 * nt + e] = o[e];
+                            }
+                        }
+                    }
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = (f4){0.f, 0.f, 0.f, 0.f};
+                    yrow += 16 * ldy;
+                }
+                } else {
                 // the block's results: y[m, v] = acc * 2^xexp[m] + bias[v] for
                 // rows m = m0 + 16 mt + 4 t + e and columns v = blk * 64 + 16 nt + r,
                 // through one row pointer that steps down the lane's rows
@@ -842,6 +920,7 @@ __global__ __launch_bounds__(512, 1) void mfma_xres_kernel(
                         yrow += ldy;
                     }
                     yrow += 12 * ldy;  // the lane's next rows are 16 further on
+                }
                 }
             }
             if (++cc == NC) {
@@ -1024,7 +1103,7 @@ hipError_t mfma_lds_dispatch(const LogitsArgs& a, hipStream_t st) {
     return mfma_lds_dispatch_mt<BITS, 4, 2, 4>(a, st);
 }
 
-template <int BITS, int D>
+template <int BITS, int D, bool TR>
 hipError_t mfma_xres_dispatch_d(const LogitsArgs& a, hipStream_t st) {
     const int NB = (int)((a.V + 63) / 64);
     const int NC = (int)(a.K / span_of(BITS));
@@ -1038,7 +1117,7 @@ hipError_t mfma_xres_dispatch_d(const LogitsArgs& a, hipStream_t st) {
     const int VRX = NMT >= 32 ? 1 : 32 / NMT;
     const dim3 grid((unsigned)(8 * NMT * VRX));
 #define LMH_XRES(G_)                                                                              \
-    hipLaunchKernelGGL((mfma_xres_kernel<BITS, G_, D>), grid, dim3(512), 0, st, wq, sc,          \
+    hipLaunchKernelGGL((mfma_xres_kernel<BITS, G_, D, TR>), grid, dim3(512), 0, st, wq, sc,      \
                        (const _Float16*)a.x, a.xexp, a.bias, a.y, a.ldy, (int)a.V, (int)a.K, a.M, \
                        NB, NC, NG, SPG, a.scale_bf16, NMT, VRX)
     if (gps == 1) LMH_XRES(1);
@@ -1081,11 +1160,12 @@ hipError_t launch_mfma_lds(const LogitsArgs& a, hipStream_t st) {
 bool xres_fits(int64_t K) { return K <= kXresMaxK; }
 
 hipError_t launch_mfma_xres(const LogitsArgs& a, hipStream_t st) {
-#ifndef LMH_XRES_D
-#define LMH_XRES_D 3
-#endif
-    return a.bits == 4 ? mfma_xres_dispatch_d<4, LMH_XRES_D>(a, st)
-                       : mfma_xres_dispatch_d<8, LMH_XRES_D>(a, st);
+    // int4: results as activation rows x single vocabulary columns, a 3-deep
+    // ring; int8: transposed results (4 contiguous vocabulary columns per lane,
+    // 16-byte stores) with a 2-deep ring -- the fastest of the variants that fit
+    // in 256 VGPRs on the 151936 x 1024 heads
+    return a.bits == 4 ? mfma_xres_dispatch_d<4, 3, false>(a, st)
+                       : mfma_xres_dispatch_d<8, 2, true>(a, st);
 }
 
 hipError_t launch_dense(const void* x, int dtype, int M, const void* w, int64_t V, int64_t K,
