@@ -107,7 +107,7 @@ def summarize(args) -> int:
 
     w = synth.WORKLOADS[args.workload or synth.HEADLINE]
     out = []
-    out.append(f"# Logits hot path on {w.name} ({w.V} x {w.K}, int{w.bits}, G={w.group}), one MI355X\n")
+    out.append(f"# Hot path on {w.name} ({w.V} x {w.K}, int{w.bits}, G={w.group}, {w.clip}), one MI355X\n")
     out.append("Commands (from the repository root; `cd /tmp && export TMPDIR=/tmp` first):\n")
     out.append("```")
     out.extend(args.cmd)
@@ -149,7 +149,7 @@ def summarize(args) -> int:
              "|---|---|---|---|---|---|---|"]
         recs = []
         for k in sorted(fv):
-            if not (k.startswith("gemv_kernel") or k.startswith("mfma") or k.startswith("topk")):
+            if not k.startswith(("gemv_kernel", "mfma", "topk", "quant_", "embed_")):
                 continue
             f_ = statistics.mean(fv[k])
             w_ = statistics.mean(wv.get(k, [0.0]))
