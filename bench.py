@@ -339,6 +339,19 @@ def main() -> int:
             "algorithmic_bytes": B, "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
             "TFLOP/s": round(tfl, 2), "frac_mfma_f16_peak": round(tfl / MFMA_F16_PEAK_TFLOPS, 4),
         }
+    # 16-bit logits (fp16 output: half the output bytes) at every M > 1
+    for M in Ms:
+        if M == 1:
+            continue
+        o16 = torch.empty((M, w.V), dtype=torch.float16, device=dev)
+        t_us = timed_loop(lambda i, M=M, o16=o16: lmh.logits(
+            xs[M], blobs[i % R], w.V, w.K, w.bits, w.group, sdt, out=o16, workspace=wss[M],
+            path=args.path), args.steps)
+        B = algorithmic_bytes(M, w.V, w.K, w.bits, w.group) - M * w.V * 2
+        per_call[f"M={M} y=f16"] = {"us": round(t_us, 3), "algorithmic_bytes": B,
+                                     "GB/s": round(B / (t_us * 1e-6) / 1e9, 1),
+                                     "TFLOP/s": round(2.0 * M * w.V * w.K / (t_us * 1e-6) / 1e12, 2)}
+        del o16
     rs_us = timed_loop(lambda i: rescore(), args.steps)
     per_call[f"top{args.topk}_rescore"] = {"us": round(rs_us, 3), "M": m_rs}
     fu_us = timed_loop(one_call, args.steps)

@@ -236,6 +236,22 @@ int lmhead_logits_path(const void* x, int x_dtype, int64_t M, const void* packed
                        void* stream);
 
 /*
+ * lmhead_logits_typed -- lmhead_logits_path with the output type chosen by
+ *   the caller: y_dtype LMH_F32 (exactly lmhead_logits_path), LMH_F16 or
+ *   LMH_BF16.  The arithmetic is unchanged; the final fp32 value (after the
+ *   bias and the bf16 row exponent) is rounded once to the 16-bit type,
+ *   nearest even; an fp16 value beyond its range becomes +-inf.  16-bit
+ *   logits halve the output bytes (M * V * 2), which at large M are the
+ *   largest single cost of the call; the rounding adds up to 2^-11 (fp16) or
+ *   2^-8 (bf16) of |y| to the error (vLLM's logits leave the head in the
+ *   activation dtype).  y needs 2-byte alignment for 16-bit types.
+ */
+int lmhead_logits_typed(const void* x, int x_dtype, int64_t M, const void* packed, int64_t V,
+                        int64_t K, int bits, int64_t group, int scale_dtype, const float* bias,
+                        void* y, int y_dtype, int64_t ldy, void* workspace, size_t ws_bytes,
+                        int path, void* stream);
+
+/*
  * lmhead_dense_logits -- y[m, v] = sum_k x[m,k] * W[v,k] with an unquantized
  *   16-bit weight: the bandwidth control of the fp16 logits GEMV (vLLM PR
  *   #48870, review comment, point 1).  fp32 accumulation.

@@ -236,3 +236,21 @@ def test_embed_validation():
     assert em(out=P + 8) == E_ALIGN
     assert em(ldo=132) == E_ALIGN                 # 16-bit rows must stay 16-byte aligned
     assert em(T=0, ids=None, out=None) == OK
+
+
+def test_logits_typed_validation():
+    L = lmh.lib()
+
+    def lt(ydt=F16, y=P, path=0, **kw):
+        a = dict(x=P, xdt=F16, M=2, packed=P, V=200, K=128, bits=4, G=64, sdt=F16, bias=None,
+                 ldy=200, ws=None, wsn=0)
+        a.update(kw)
+        return L.lmhead_logits_typed(a["x"], a["xdt"], a["M"], a["packed"], a["V"], a["K"], a["bits"],
+                                     a["G"], a["sdt"], a["bias"], y, ydt, a["ldy"], a["ws"], a["wsn"],
+                                     path, None)
+
+    assert lt(ydt=7) == E_DTYPE
+    assert lt(ydt=F16, y=P + 1) == E_ALIGN
+    assert lt(ydt=F32, y=P + 2) == E_ALIGN
+    assert lt(ydt=BF16, ldy=100) == E_SHAPE
+    assert lt(ydt=F16, M=0) == OK

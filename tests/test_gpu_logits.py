@@ -166,3 +166,56 @@ def test_empty_calls_launch_nothing():
     blob = torch.zeros(lmh.packed_bytes(64, 128, 4, 64), dtype=torch.uint8, device=DEV)
     y = lmh.logits(x, blob, 64, 128, 4, 64, torch.float16)
     assert y.shape == (0, 64)
+
+
+def _ulp16(y: np.ndarray, odt: str) -> np.ndarray:
+    """Spacing of the 16-bit format at |y| (normal range)."""
+    e = np.floor(np.log2(np.maximum(np.abs(y), 1e-30)))
+    return np.exp2(e - (10 if odt == "f16" else 7))
+
+
+@pytest.mark.parametrize("odt", ["f16", "bf16"])
+@pytest.mark.parametrize("path,M", [(GEMV, 1), (GEMV, 3), (MFMA, 5), (MFMA, 17), (LDS, 20), (LDS, 70),
+                                    (XRES, 40), (XRES, 130)])
+@pytest.mark.parametrize("bits,G", [(4, 64), (8, 128)])
+def test_16bit_logits_output(odt, path, M, bits, G):
+    """16-bit logits are the fp32 result rounded once to nearest even (bit-exact
+    against converting the same kernel's fp32 output), so they stay within the
+    fp32 bound plus half a 16-bit ulp of the oracle; bias and strided rows too."""
+    need_gpu()
+    V, K = 64 * 5 + 13, 512
+    q, s, blob = _head(V, K, bits, G, "f16", seed=bits + G + M)
+    x = synth.random_x(M, K, seed=60 + M)
+    bias = synth.random_weight((1, V), 0.5, 7)[0]
+    y32 = _run(x, "f16", blob, V, K, bits, G, "f16", path, bias=bias)
+    ldy = V + 24
+    out = torch.full((M, ldy), 7.0, dtype=TD[odt], device=DEV)
+    lmh.logits(to_dev(x, "f16"), blob, V, K, bits, G, torch.float16,
+               bias=torch.from_numpy(bias).to(DEV), out=out[:, :V], path=path)
+    torch.cuda.synchronize()
+    assert (out[:, V:] == 7.0).all(), "columns past V were written"
+    got = out[:, :V].float().cpu().numpy()
+    want = torch.from_numpy(y32).to(TD[odt]).float().numpy()
+    assert np.array_equal(got, want), f"not the rounded fp32 result at {np.argwhere(got != want)[:4]}"
+    y_or = oracle.logits(x, q, s, oracle.F16, G, bias=bias, x_dtype=oracle.F16)
+    y_abs = abs_terms(x, "f16", q, s, oracle.F16, G)
+    slack = (K + K // G + 16) * 2.0**-24 * y_abs + np.abs(bias)[None, :] * 2.0**-23
+    assert (np.abs(got - y_or) <= slack + 0.5 * _ulp16(y_or, odt) * (1 + 2.0**-10) + 1e-30).all()
+
+
+def test_16bit_output_overflow_to_inf():
+    """fp16 logits beyond 65504 round to +-inf, as the conversion of the fp32 value does."""
+    need_gpu()
+    V, K, bits, G = 200, 256, 4, 64
+    q, s, blob = _head(V, K, bits, G, "f16", seed=3)
+    x = synth.random_x(2, K, seed=5)
+    bias = np.zeros(V, dtype=np.float32)
+    bias[::3] = 7.0e4                      # past the fp16 range
+    bias[1::7] = -6.6e4
+    y32 = _run(x, "f16", blob, V, K, bits, G, "f16", GEMV, bias=bias)
+    y16 = lmh.logits(to_dev(x, "f16"), blob, V, K, bits, G, torch.float16, path=GEMV,
+                     bias=torch.from_numpy(bias).to(DEV), out_dtype=torch.float16)
+    torch.cuda.synchronize()
+    want = torch.from_numpy(y32).half()
+    assert torch.isinf(want).any(), "test input did not reach the fp16 range limit"
+    assert torch.equal(y16.cpu(), want)

@@ -59,6 +59,8 @@ def lib() -> ctypes.CDLL:
                                     sz, vp]),
             "lmhead_logits_path": (i32, [vp, i32, i64, vp, i64, i64, i32, i64, i32, vp, vp, i64,
                                          vp, sz, i32, vp]),
+            "lmhead_logits_typed": (i32, [vp, i32, i64, vp, i64, i64, i32, i64, i32, vp, vp, i32, i64,
+                                          vp, sz, i32, vp]),
             "lmhead_dense_logits": (i32, [vp, i32, i64, vp, i32, i64, i64, vp, i64, vp]),
             "lmhead_topk_workspace_bytes": (sz, [i64, i64, i32]),
             "lmhead_topk_rescore": (i32, [vp, i32, i64, vp, i32, i64, i64, vp, i64, i32, vp, vp,
@@ -201,19 +203,22 @@ def logits_workspace(M: int, K: int, x_dtype: torch.dtype, device) -> Optional[t
 def logits(x: torch.Tensor, packed: torch.Tensor, V: int, K: int, bits: int, group: int,
            scale_dtype: torch.dtype, bias: Optional[torch.Tensor] = None,
            out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-           path: int = PATH_AUTO) -> torch.Tensor:
-    """fp32 logits [M, V] (or into ``out`` [M, ldy]) -- lmhead_logits / lmhead_logits_path."""
+           path: int = PATH_AUTO, out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """Logits [M, V] (or into ``out`` [M, ldy]) in ``out_dtype`` (fp32, or fp16 / bf16
+    rounded once from the fp32 result) -- lmhead_logits_typed."""
     _need_cuda(x, packed, bias)
     M = x.shape[0]
     if out is None:
-        out = torch.empty((M, V), dtype=torch.float32, device=x.device)
+        out = torch.empty((M, V), dtype=out_dtype, device=x.device)
+    elif out.stride(-1) != 1:
+        raise ValueError("out must have unit column stride")
     ldy = out.stride(0) if out.dim() == 2 else V
     if workspace is None:
         workspace = logits_workspace(M, K, x.dtype, x.device)
     ws_n = 0 if workspace is None else workspace.numel()
-    _check("lmhead_logits", lib().lmhead_logits_path(
+    _check("lmhead_logits", lib().lmhead_logits_typed(
         _ptr(x), _DT[x.dtype], M, _ptr(packed), V, K, bits, group, _DT[scale_dtype], _ptr(bias),
-        _ptr(out), ldy, _ptr(workspace), ws_n, path, _stream(x)))
+        _ptr(out), _DT[out.dtype], ldy, _ptr(workspace), ws_n, path, _stream(x)))
     return out
 
 

@@ -135,8 +135,8 @@ size_t lmhead_logits_workspace_bytes(int64_t M, int64_t K, int x_dtype) {
 
 static int logits_impl(const void* x, int x_dtype, int64_t M, const void* packed, int64_t V,
                        int64_t K, int bits, int64_t group, int scale_dtype, const float* bias,
-                       float* y, int64_t ldy, void* workspace, size_t ws_bytes, void* stream,
-                       int path) {
+                       void* y, int y_dtype, int64_t ldy, void* workspace, size_t ws_bytes,
+                       void* stream, int path) {
     int rc = check_layout(V, K, bits, group);
     if (rc != LMH_OK) return rc;
     if (x_dtype != F16 && x_dtype != BF16) return LMH_E_DTYPE;
@@ -147,7 +147,9 @@ static int logits_impl(const void* x, int x_dtype, int64_t M, const void* packed
     if (ldy < V) return LMH_E_SHAPE;
     if (!x || !packed || !y) return LMH_E_NULL;
     if (!aligned16(x) || !aligned16(packed)) return LMH_E_ALIGN;
-    if (((uintptr_t)y & 3u) != 0 || (bias && ((uintptr_t)bias & 3u) != 0)) return LMH_E_ALIGN;
+    if (y_dtype != F32 && y_dtype != F16 && y_dtype != BF16) return LMH_E_DTYPE;
+    if (((uintptr_t)y & (y_dtype == F32 ? 3u : 1u)) != 0) return LMH_E_ALIGN;
+    if (bias && ((uintptr_t)bias & 3u) != 0) return LMH_E_ALIGN;
     const size_t need = lmhead_logits_workspace_bytes(M, K, x_dtype);
     if (need > 0) {
         if (!workspace || ws_bytes < need) return LMH_E_WORKSPACE;
@@ -174,6 +176,7 @@ static int logits_impl(const void* x, int x_dtype, int64_t M, const void* packed
     a.packed = (const uint8_t*)packed;
     a.bias = bias;
     a.y = y;
+    a.y_dtype = y_dtype;
     a.ldy = ldy;
     a.V = V;
     a.K = K;
@@ -198,7 +201,7 @@ static int logits_impl(const void* x, int x_dtype, int64_t M, const void* packed
 int lmhead_logits(const void* x, int x_dtype, int64_t M, const void* packed, int64_t V, int64_t K,
                   int bits, int64_t group, int scale_dtype, const float* bias, float* y,
                   int64_t ldy, void* workspace, size_t ws_bytes, void* stream) {
-    return logits_impl(x, x_dtype, M, packed, V, K, bits, group, scale_dtype, bias, y, ldy,
+    return logits_impl(x, x_dtype, M, packed, V, K, bits, group, scale_dtype, bias, y, F32, ldy,
                        workspace, ws_bytes, stream, 0);
 }
 
@@ -206,8 +209,16 @@ int lmhead_logits_path(const void* x, int x_dtype, int64_t M, const void* packed
                        int64_t K, int bits, int64_t group, int scale_dtype, const float* bias,
                        float* y, int64_t ldy, void* workspace, size_t ws_bytes, int path,
                        void* stream) {
-    return logits_impl(x, x_dtype, M, packed, V, K, bits, group, scale_dtype, bias, y, ldy,
+    return logits_impl(x, x_dtype, M, packed, V, K, bits, group, scale_dtype, bias, y, F32, ldy,
                        workspace, ws_bytes, stream, path);
+}
+
+int lmhead_logits_typed(const void* x, int x_dtype, int64_t M, const void* packed, int64_t V,
+                        int64_t K, int bits, int64_t group, int scale_dtype, const float* bias,
+                        void* y, int y_dtype, int64_t ldy, void* workspace, size_t ws_bytes,
+                        int path, void* stream) {
+    return logits_impl(x, x_dtype, M, packed, V, K, bits, group, scale_dtype, bias, y, y_dtype,
+                       ldy, workspace, ws_bytes, stream, path);
 }
 
 int lmhead_dense_logits(const void* x, int x_dtype, int64_t M, const void* w, int w_dtype,
@@ -293,7 +304,7 @@ int lmhead_logits_topk(const void* x, int x_dtype, int64_t M, const void* packed
     float* yy = y ? y : (float*)(ws + xws + tws);
     const int64_t ly = y ? ldy : V;
     // the logits (automatic kernel), then the two top-K passes over them
-    rc = logits_impl(x, x_dtype, M, packed, V, K, bits, group, scale_dtype, bias, yy, ly, ws,
+    rc = logits_impl(x, x_dtype, M, packed, V, K, bits, group, scale_dtype, bias, yy, F32, ly, ws,
                      (size_t)xws, stream, 0);
     if (rc != LMH_OK) return rc;
     return from_hip(lmh::launch_topk_rescore(x, x_dtype, (int)M, w_ref, w_dtype, V, K, yy, ly, topk,

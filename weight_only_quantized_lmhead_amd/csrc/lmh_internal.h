@@ -58,7 +58,8 @@ struct LogitsArgs {
     const int* xexp;       // [M] power-of-two row exponents, or nullptr
     const uint8_t* packed; // blob
     const float* bias;     // [V] or nullptr
-    float* y;
+    void* y;               // [M, ldy] in y_dtype (F32, F16 or BF16)
+    int y_dtype;
     int64_t ldy;
     int64_t V, K, G;
     int M, bits, scale_bf16;

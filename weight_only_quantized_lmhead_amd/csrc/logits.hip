@@ -75,6 +75,43 @@ __device__ __forceinline__ uint32_t word_of(const uint4& u, int j) {
     return j == 0 ? u.x : j == 1 ? u.y : j == 2 ? u.z : u.w;
 }
 
+// Logits storage type: fp32, or the 16-bit pattern of fp16 / bf16.
+template <int OUT>
+using YT = typename std::conditional<OUT == F32, float, uint16_t>::type;
+
+// fp32 -> the output type, rounded to nearest even once, from the final fp32
+// value (bias and row exponent already applied).  The value passes through an
+// empty asm first: otherwise the backend may fold the last fp32 add into a
+// mixed-precision fma that rounds only once, which differs from rounding the
+// fp32 result.
+template <int OUT>
+__device__ __forceinline__ YT<OUT> to_out(float v) {
+    if constexpr (OUT == F32) {
+        return v;
+    } else {
+        asm("" : "+v"(v));
+        if constexpr (OUT == F16) {
+            return __builtin_bit_cast(uint16_t, (_Float16)v);
+        } else {
+            uint32_t u = __float_as_uint(v);
+            u += 0x7FFFu + ((u >> 16) & 1u);  // nearest even (finite values)
+            return (uint16_t)(u >> 16);
+        }
+    }
+}
+
+// Four consecutive logits at p (aligned to four elements).
+template <int OUT>
+__device__ __forceinline__ void store4(YT<OUT>* p, f4 v) {
+    if constexpr (OUT == F32) {
+        *(f4*)p = v;
+    } else {
+        const uint32_t lo = (uint32_t)to_out<OUT>(v[0]) | ((uint32_t)to_out<OUT>(v[1]) << 16);
+        const uint32_t hi = (uint32_t)to_out<OUT>(v[2]) | ((uint32_t)to_out<OUT>(v[3]) << 16);
+        *(uint2*)p = make_uint2(lo, hi);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // bf16 x -> fp16 x * 2^-e, one workgroup per row.
 __global__ __launch_bounds__(256) void x_to_f16_kernel(const uint16_t* __restrict__ xb, int K,
@@ -113,13 +150,13 @@ __global__ __launch_bounds__(256) void x_to_f16_kernel(const uint16_t* __restric
 // keep exact vmcnt accounting (no drain at the loop head).  GPS = groups per
 // superchunk (G <= span); GPS == 1 covers G >= span, the scale of superchunk c
 // then being that of group c / SPG.
-template <int BITS, int MM, int GPS, int D, int KS>
+template <int BITS, int MM, int GPS, int D, int KS, int OUT>
 __global__ __launch_bounds__(256) void gemv_kernel(const uint4* __restrict__ wq,
                                                    const uint16_t* __restrict__ sc,
                                                    const h2* __restrict__ xg,
                                                    const int* __restrict__ xexp,
                                                    const float* __restrict__ bias,
-                                                   float* __restrict__ y, int64_t ldy, int V, int K,
+                                                   void* __restrict__ y, int64_t ldy, int V, int K,
                                                    int NB, int NC, int NG, int SPG, int sbf16) {
     constexpr int SPAN = BITS == 4 ? 128 : 64;
     constexpr int CPS = SPAN / 32;    // 32-column chunks per superchunk
@@ -250,7 +287,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint4* __restrict__ wq,
         for (int m = 0; m < MM; ++m) {
             float r = acc[m];
             if (xexp) r = ldexpf(r, xexp[m]);
-            y[(int64_t)m * ldy + v] = r + b;
+            ((YT<OUT>*)y)[(int64_t)m * ldy + v] = to_out<OUT>(r + b);
         }
     }
 }
@@ -269,10 +306,10 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint4* __restrict__ wq,
 // vocabulary row r.  Per scale group: the B operands of the 4 column tiles are
 // unpacked once, then per row tile a CPG-long MFMA chain is started from zero
 // and folded into the fp32 accumulator with the group scale of the lane's row.
-template <int BITS, int MT, int GPS>
+template <int BITS, int MT, int GPS, int OUT>
 __global__ __launch_bounds__(256, MT >= 4 ? 1 : 2) void mfma_kernel(
     const uint4* __restrict__ wq, const uint16_t* __restrict__ sc, const _Float16* __restrict__ x,
-    const int* __restrict__ xexp, const float* __restrict__ bias, float* __restrict__ y,
+    const int* __restrict__ xexp, const float* __restrict__ bias, void* __restrict__ y,
     int64_t ldy, int V, int K, int M, int NB, int NC, int NG, int SPG, int sbf16) {
     // grid (row groups, activation tiles): all row groups of one activation
     // tile run before the next tile's; the last-level cache serves the
@@ -425,7 +462,7 @@ __global__ __launch_bounds__(256, MT >= 4 ? 1 : 2) void mfma_kernel(
                 if (m < M) {
                     float o = acc[mt][nt][e];
                     if (xexp) o = ldexpf(o, xexp[m]);
-                    y[(int64_t)m * ldy + v] = o + b;
+                    ((YT<OUT>*)y)[(int64_t)m * ldy + v] = to_out<OUT>(o + b);
                 }
             }
     }
@@ -470,11 +507,11 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
 // workgroups, so the activation tiles of one row group run at the same time
 // on one XCD and read its weights through that XCD's L2 once.  With WPB = 8
 // the 8 waves (two per SIMD) share one activation tile.
-template <int BITS, int MT, int GPS, int STAGES, int WPB>
+template <int BITS, int MT, int GPS, int STAGES, int WPB, int OUT>
 __global__ __launch_bounds__(64 * WPB, WPB == 8 ? 1 : (MT <= 2 ? 3 : (MT <= 4 ? 2 : 1)))
 void mfma_lds_kernel(
     const uint4* __restrict__ wq, const uint16_t* __restrict__ sc, const _Float16* __restrict__ x,
-    const int* __restrict__ xexp, const float* __restrict__ bias, float* __restrict__ y,
+    const int* __restrict__ xexp, const float* __restrict__ bias, void* __restrict__ y,
     int64_t ldy, int V, int K, int M, int NB, int NC, int NG, int SPG, int sbf16, int NMT,
     int total) {
     constexpr int NT = 4;
@@ -646,7 +683,7 @@ void mfma_lds_kernel(
                         if (m < M && v < V) {
                             float o = acc[mt][nt][e];
                             if (xexp) o = ldexpf(o, xexp[m]);
-                            y[(int64_t)m * ldy + v] = o + b;
+                            ((YT<OUT>*)y)[(int64_t)m * ldy + v] = to_out<OUT>(o + b);
                         }
                     }
             }
@@ -700,10 +737,10 @@ void mfma_lds_kernel(
 // slot comes from HBM once and from that XCD's L2 for the other tiles.
 constexpr int kXresMaxK = 1024;
 
-template <int BITS, int GPS, int D, bool TR>
+template <int BITS, int GPS, int D, bool TR, int OUT>
 __global__ __launch_bounds__(512, 1) void mfma_xres_kernel(
     const uint4* __restrict__ wq, const uint16_t* __restrict__ sc, const _Float16* __restrict__ x,
-    const int* __restrict__ xexp, const float* __restrict__ bias, float* __restrict__ y,
+    const int* __restrict__ xexp, const float* __restrict__ bias, void* __restrict__ y,
     int64_t ldy, int V, int K, int M, int NB, int NC, int NG, int SPG, int sbf16, int NMT,
     int VRX) {
     constexpr int MT = 4, NT = 4, ROWS = 64;
@@ -731,8 +768,9 @@ __global__ __launch_bounds__(512, 1) void mfma_xres_kernel(
 
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int r = lane & 15, t = lane >> 4;
-    // 16-byte output stores need 16-byte aligned rows
-    const bool vec16 = ((uintptr_t)y & 15) == 0 && (ldy & 3) == 0;
+    // 4-element output stores need rows aligned to 4 elements
+    constexpr int OSZ = OUT == F32 ? 4 : 2;
+    const bool vec16 = ((uintptr_t)y & (4 * OSZ - 1)) == 0 && (ldy & 3) == 0;
     const int nblk = rb1 - rb0 > wv ? (rb1 - rb0 - wv + 7) / 8 : 0;
     const int nsteps = nblk * NC;
     if (nsteps == 0) return;
@@ -861,7 +899,7 @@ __global__ __launch_bounds__(512, 1) void mfma_xres_kernel(
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         bv[nt][e] = (bias && 16 * nt + e < vlim) ? bias[blk * 64 + 16 * nt + 4 * t + e] : 0.0f;
-                float* yrow = y + (int64_t)(m0 + r) * ldy + (int64_t)blk * 64 + 4 * t;
+                YT<OUT>* yrow = (YT<OUT>*)y + (int64_t)(m0 + r) * ldy + (int64_t)blk * 64 + 4 * t;
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
                     if (16 * mt < mlim) {
@@ -875,11 +913,11 @@ __global__ __launch_bounds__(512, 1) void mfma_xres_kernel(
                             }
                             o = o + bv[nt];
                             if (vec16 && 16 * nt + 3 < vlim) {
-                                *(f4*)(yrow + 16 * nt) = o;
+                                store4<OUT>(yrow + 16 * nt, o);
                             } else {
 #pragma unroll
                                 for (int e = 0; e < 4; ++e)
-                                    if (16 * nt + e < vlim) yrow[16 * nt + e] = o[e];
+                                    if (16 * nt + e < vlim) yrow[16 * nt + e] = to_out<OUT>(o[e]);
                             }
                         }
                     }
@@ -901,7 +939,7 @@ __global__ __launch_bounds__(512, 1) void mfma_xres_kernel(
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt)
                     bv[nt] = (bias && 16 * nt < vlim) ? bias[blk * 64 + 16 * nt + r] : 0.0f;
-                float* yrow = y + (int64_t)(m0 + 4 * t) * ldy + (int64_t)blk * 64 + r;
+                YT<OUT>* yrow = (YT<OUT>*)y + (int64_t)(m0 + 4 * t) * ldy + (int64_t)blk * 64 + r;
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
@@ -913,7 +951,7 @@ __global__ __launch_bounds__(512, 1) void mfma_xres_kernel(
                             if (rowok && 16 * nt < vlim) {
                                 float o = acc[mt][nt][e];
                                 if (xexp) o = ldexpf(o, xe);
-                                yrow[16 * nt] = o + bv[nt];
+                                yrow[16 * nt] = to_out<OUT>(o + bv[nt]);
                             }
                             acc[mt][nt][e] = 0.0f;
                         }
@@ -1002,7 +1040,7 @@ inline int gps_of(int bits, int64_t G) {
     return G >= span ? 1 : span / (int)G;
 }
 
-template <int BITS, int MM>
+template <int BITS, int MM, int OUT>
 hipError_t gemv_dispatch_gps(const LogitsArgs& a, int gps, hipStream_t st) {
     constexpr int D = 1;
     const int NB = (int)((a.V + 63) / 64);
@@ -1017,7 +1055,7 @@ hipError_t gemv_dispatch_gps(const LogitsArgs& a, int gps, hipStream_t st) {
     auto splits = [&](int ks) { return NC % (2 * ks) == 0 && (NC / ks) % SPG == 0; };
     const int KS = splits(4) ? 4 : splits(2) ? 2 : 1;
 #define LMH_GEMV(G_, KS_)                                                                          \
-    hipLaunchKernelGGL((gemv_kernel<BITS, MM, G_, D, KS_>), dim3((NB * KS_ + 3) / 4), dim3(256),   \
+    hipLaunchKernelGGL((gemv_kernel<BITS, MM, G_, D, KS_, OUT>), dim3((NB * KS_ + 3) / 4), dim3(256), \
                        lds, st, wq, sc, (const h2*)a.x, a.xexp, a.bias, a.y, a.ldy, (int)a.V,      \
                        (int)a.K, NB, NC, NG, SPG, a.scale_bf16)
 #define LMH_GEMV_KS(G_) \
@@ -1031,18 +1069,18 @@ hipError_t gemv_dispatch_gps(const LogitsArgs& a, int gps, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int BITS>
+template <int BITS, int OUT>
 hipError_t gemv_dispatch(const LogitsArgs& a, hipStream_t st) {
     const int gps = gps_of(BITS, a.G);
     switch (a.M) {
-    case 1: return gemv_dispatch_gps<BITS, 1>(a, gps, st);
-    case 2: return gemv_dispatch_gps<BITS, 2>(a, gps, st);
-    case 3: return gemv_dispatch_gps<BITS, 3>(a, gps, st);
-    default: return gemv_dispatch_gps<BITS, 4>(a, gps, st);
+    case 1: return gemv_dispatch_gps<BITS, 1, OUT>(a, gps, st);
+    case 2: return gemv_dispatch_gps<BITS, 2, OUT>(a, gps, st);
+    case 3: return gemv_dispatch_gps<BITS, 3, OUT>(a, gps, st);
+    default: return gemv_dispatch_gps<BITS, 4, OUT>(a, gps, st);
     }
 }
 
-template <int BITS, int MT>
+template <int BITS, int MT, int OUT>
 hipError_t mfma_dispatch_mt(const LogitsArgs& a, hipStream_t st) {
     const int NB = (int)((a.V + 63) / 64);
     const int NC = (int)(a.K / span_of(BITS));
@@ -1053,7 +1091,7 @@ hipError_t mfma_dispatch_mt(const LogitsArgs& a, hipStream_t st) {
     const uint16_t* sc = (const uint16_t*)(a.packed + (int64_t)NB * 64 * a.K * BITS / 8);
     const dim3 grid((NB + 3) / 4, (a.M + MT * 16 - 1) / (MT * 16));
 #define LMH_MFMA(G_)                                                                               \
-    hipLaunchKernelGGL((mfma_kernel<BITS, MT, G_>), grid, dim3(256), 0, st, wq, sc,               \
+    hipLaunchKernelGGL((mfma_kernel<BITS, MT, G_, OUT>), grid, dim3(256), 0, st, wq, sc,          \
                        (const _Float16*)a.x, a.xexp, a.bias, a.y, a.ldy, (int)a.V, (int)a.K, a.M, \
                        NB, NC, NG, SPG, a.scale_bf16)
     if (gps == 1) LMH_MFMA(1);
@@ -1064,7 +1102,7 @@ hipError_t mfma_dispatch_mt(const LogitsArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int BITS, int MT, int STAGES, int WPB>
+template <int BITS, int MT, int STAGES, int WPB, int OUT>
 hipError_t mfma_lds_dispatch_mt(const LogitsArgs& a, hipStream_t st) {
     const int NB = (int)((a.V + 63) / 64);
     const int NC = (int)(a.K / span_of(BITS));
@@ -1080,7 +1118,8 @@ hipError_t mfma_lds_dispatch_mt(const LogitsArgs& a, hipStream_t st) {
     // the 151936 x 1024 head, whose output stores then stall the next tile)
     const dim3 grid((unsigned)((total + 7) / 8 * 8));
 #define LMH_MFMA_LDS(G_)                                                                           \
-    hipLaunchKernelGGL((mfma_lds_kernel<BITS, MT, G_, STAGES, WPB>), grid, dim3(64 * WPB), 0, st,  \
+    hipLaunchKernelGGL((mfma_lds_kernel<BITS, MT, G_, STAGES, WPB, OUT>), grid, dim3(64 * WPB), 0, \
+                       st,                                                                        \
                        wq, sc,                                                                    \
                        (const _Float16*)a.x, a.xexp, a.bias, a.y, a.ldy, (int)a.V, (int)a.K, a.M, \
                        NB, NC, NG, SPG, a.scale_bf16, NMT, total)
@@ -1092,18 +1131,18 @@ hipError_t mfma_lds_dispatch_mt(const LogitsArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int BITS>
+template <int BITS, int OUT>
 hipError_t mfma_lds_dispatch(const LogitsArgs& a, hipStream_t st) {
     // 32-row tiles for M <= 32 (3 workgroups of 4 waves per CU), else 64-row
     // tiles (2 per CU).  Measured on the 151936 x 1024 int4 head, M = 128 and
     // 256: 128-row tiles, with one workgroup of 4 or 8 waves per CU, lose more
     // to the waves meeting at one barrier than they gain from sharing each
     // unpacked operand among more MFMAs.
-    if (a.M <= 32) return mfma_lds_dispatch_mt<BITS, 2, 2, 4>(a, st);
-    return mfma_lds_dispatch_mt<BITS, 4, 2, 4>(a, st);
+    if (a.M <= 32) return mfma_lds_dispatch_mt<BITS, 2, 2, 4, OUT>(a, st);
+    return mfma_lds_dispatch_mt<BITS, 4, 2, 4, OUT>(a, st);
 }
 
-template <int BITS, int D, bool TR>
+template <int BITS, int D, bool TR, int OUT>
 hipError_t mfma_xres_dispatch_d(const LogitsArgs& a, hipStream_t st) {
     const int NB = (int)((a.V + 63) / 64);
     const int NC = (int)(a.K / span_of(BITS));
@@ -1117,7 +1156,7 @@ hipError_t mfma_xres_dispatch_d(const LogitsArgs& a, hipStream_t st) {
     const int VRX = NMT >= 32 ? 1 : 32 / NMT;
     const dim3 grid((unsigned)(8 * NMT * VRX));
 #define LMH_XRES(G_)                                                                              \
-    hipLaunchKernelGGL((mfma_xres_kernel<BITS, G_, D, TR>), grid, dim3(512), 0, st, wq, sc,      \
+    hipLaunchKernelGGL((mfma_xres_kernel<BITS, G_, D, TR, OUT>), grid, dim3(512), 0, st, wq, sc, \
                        (const _Float16*)a.x, a.xexp, a.bias, a.y, a.ldy, (int)a.V, (int)a.K, a.M, \
                        NB, NC, NG, SPG, a.scale_bf16, NMT, VRX)
     if (gps == 1) LMH_XRES(1);
@@ -1128,13 +1167,13 @@ hipError_t mfma_xres_dispatch_d(const LogitsArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int BITS>
+template <int BITS, int OUT>
 hipError_t mfma_dispatch(const LogitsArgs& a, hipStream_t st) {
     // one 16-row activation tile for M <= 16; two (32 rows) otherwise: the
     // 64-row tile needs one wave per SIMD and loses more to latency than it
     // saves in unpacking (measured on the 151936 x 1024 head, M = 64..256)
-    if (a.M <= 16) return mfma_dispatch_mt<BITS, 1>(a, st);
-    return mfma_dispatch_mt<BITS, 2>(a, st);
+    if (a.M <= 16) return mfma_dispatch_mt<BITS, 1, OUT>(a, st);
+    return mfma_dispatch_mt<BITS, 2, OUT>(a, st);
 }
 
 }  // namespace
@@ -1145,28 +1184,37 @@ hipError_t launch_x_to_f16(const uint16_t* x_bf16, int M, int K, _Float16* xh, i
     return hipGetLastError();
 }
 
-hipError_t launch_gemv(const LogitsArgs& a, hipStream_t st) {
-    return a.bits == 4 ? gemv_dispatch<4>(a, st) : gemv_dispatch<8>(a, st);
-}
+// Instantiate a dispatcher for the head's code width and the output type.
+#define LMH_BY_BITS_OUT(FN)                                                                       \
+    switch (a.y_dtype) {                                                                          \
+    case F32: return a.bits == 4 ? FN<4, F32>(a, st) : FN<8, F32>(a, st);                         \
+    case F16: return a.bits == 4 ? FN<4, F16>(a, st) : FN<8, F16>(a, st);                         \
+    default: return a.bits == 4 ? FN<4, BF16>(a, st) : FN<8, BF16>(a, st);                        \
+    }
 
-hipError_t launch_mfma(const LogitsArgs& a, hipStream_t st) {
-    return a.bits == 4 ? mfma_dispatch<4>(a, st) : mfma_dispatch<8>(a, st);
-}
+hipError_t launch_gemv(const LogitsArgs& a, hipStream_t st) { LMH_BY_BITS_OUT(gemv_dispatch) }
+
+hipError_t launch_mfma(const LogitsArgs& a, hipStream_t st) { LMH_BY_BITS_OUT(mfma_dispatch) }
 
 hipError_t launch_mfma_lds(const LogitsArgs& a, hipStream_t st) {
-    return a.bits == 4 ? mfma_lds_dispatch<4>(a, st) : mfma_lds_dispatch<8>(a, st);
+    LMH_BY_BITS_OUT(mfma_lds_dispatch)
 }
 
 bool xres_fits(int64_t K) { return K <= kXresMaxK; }
 
-hipError_t launch_mfma_xres(const LogitsArgs& a, hipStream_t st) {
-    // int4: results as activation rows x single vocabulary columns, a 3-deep
-    // ring; int8: transposed results (4 contiguous vocabulary columns per lane,
-    // 16-byte stores) with a 2-deep ring -- the fastest of the variants that fit
-    // in 256 VGPRs on the 151936 x 1024 heads
-    return a.bits == 4 ? mfma_xres_dispatch_d<4, 3, false>(a, st)
-                       : mfma_xres_dispatch_d<8, 2, true>(a, st);
+// int4: results as activation rows x single vocabulary columns, a 3-deep ring;
+// int8: transposed results (4 contiguous vocabulary columns per lane, one
+// 4-element store) with a 2-deep ring -- the fastest of the variants that fit
+// in 256 VGPRs on the 151936 x 1024 heads
+template <int BITS, int OUT>
+hipError_t xres_dispatch(const LogitsArgs& a, hipStream_t st) {
+    if constexpr (BITS == 4) return mfma_xres_dispatch_d<4, 3, false, OUT>(a, st);
+    else return mfma_xres_dispatch_d<8, 2, true, OUT>(a, st);
 }
+
+hipError_t launch_mfma_xres(const LogitsArgs& a, hipStream_t st) { LMH_BY_BITS_OUT(xres_dispatch) }
+
+#undef LMH_BY_BITS_OUT
 
 hipError_t launch_dense(const void* x, int dtype, int M, const void* w, int64_t V, int64_t K,
                         float* y, int64_t ldy, hipStream_t st) {
