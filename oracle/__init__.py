@@ -92,6 +92,18 @@ def _load() -> ctypes.CDLL:
         lib.orc_topk.argtypes = [vp, i64, i32, vp]
         lib.orc_topk_rescore.restype = i32
         lib.orc_topk_rescore.argtypes = [vp, i64, i64, i64, i32, vp, i32, vp, i32, i64, vp, vp, vp]
+        lib.orc_quantize_asym.restype = i32
+        lib.orc_quantize_asym.argtypes = [vp, i32, i64, i64, i32, i64, i32, vp, vp, vp]
+        lib.orc_packed_bytes_zp.restype = i64
+        lib.orc_packed_bytes_zp.argtypes = [i64, i64, i32, i64]
+        lib.orc_pack_zp.restype = i32
+        lib.orc_pack_zp.argtypes = [vp, vp, vp, i64, i64, i32, i64, vp]
+        lib.orc_unpack_zp.restype = i32
+        lib.orc_unpack_zp.argtypes = [vp, i64, i64, i32, i64, vp, vp, vp]
+        lib.orc_logits_zp.restype = i32
+        lib.orc_logits_zp.argtypes = [vp, i32, i64, vp, vp, vp, i32, i64, i64, i64, vp, vp, i64, vp]
+        lib.orc_embed_zp.restype = i32
+        lib.orc_embed_zp.argtypes = [vp, vp, vp, i32, i64, i64, i64, vp, i64, i32, vp]
         lib.orc_algorithmic_bytes.restype = i64
         lib.orc_algorithmic_bytes.argtypes = [i64, i64, i64, i32, i64]
         _lib = lib
@@ -259,6 +271,89 @@ def dense_logits(x: np.ndarray, w: np.ndarray, rows=None, x_dtype: Optional[int]
                                   _dtype_code(w, w_dtype), V, K, rp or None, n, _ptr(y))
     _check(rc, "dense_logits")
     return y
+
+
+# ---- asymmetric (zero-point) form ---------------------------------------------
+
+def quantize_asym(w: np.ndarray, bits: int, group: int, scale_dtype: int,
+                  w_dtype: Optional[int] = None):
+    """(n uint8 [V,K], s uint16 [V,K/G], z uint8 [V,K/G]) with w ~ (n - z) * s:
+    per-group min/max round to nearest with zero exactly representable (R21)."""
+    w = np.ascontiguousarray(w)
+    V, K = w.shape
+    n = np.empty((V, K), dtype=np.uint8)
+    s = np.empty((V, K // group), dtype=np.uint16)
+    z = np.empty((V, K // group), dtype=np.uint8)
+    rc = _load().orc_quantize_asym(_ptr(w), _dtype_code(w, w_dtype), V, K, bits, group,
+                                   scale_dtype, _ptr(n), _ptr(s), _ptr(z))
+    _check(rc, "quantize_asym")
+    return n, s, z
+
+
+def packed_bytes_zp(V: int, K: int, bits: int, group: int) -> int:
+    n = int(_load().orc_packed_bytes_zp(V, K, bits, group))
+    if n < 0:
+        raise ValueError("unsupported packed shape")
+    return n
+
+
+def pack_zp(n: np.ndarray, s: np.ndarray, z: np.ndarray, bits: int, group: int) -> np.ndarray:
+    n = np.ascontiguousarray(n, dtype=np.uint8)
+    s = np.ascontiguousarray(s, dtype=np.uint16)
+    z = np.ascontiguousarray(z, dtype=np.uint8)
+    V, K = n.shape
+    out = np.empty(packed_bytes_zp(V, K, bits, group), dtype=np.uint8)
+    _check(_load().orc_pack_zp(_ptr(n), _ptr(s), _ptr(z), V, K, bits, group, _ptr(out)), "pack_zp")
+    return out
+
+
+def unpack_zp(blob: np.ndarray, V: int, K: int, bits: int, group: int):
+    blob = np.ascontiguousarray(blob, dtype=np.uint8)
+    n = np.empty((V, K), dtype=np.uint8)
+    s = np.empty((V, K // group), dtype=np.uint16)
+    z = np.empty((V, K // group), dtype=np.uint8)
+    _check(_load().orc_unpack_zp(_ptr(blob), V, K, bits, group, _ptr(n), _ptr(s), _ptr(z)),
+           "unpack_zp")
+    return n, s, z
+
+
+def logits_zp(x: np.ndarray, n: np.ndarray, s: np.ndarray, z: np.ndarray, scale_dtype: int,
+              group: int, bias: Optional[np.ndarray] = None, rows=None,
+              x_dtype: Optional[int] = None) -> np.ndarray:
+    """fp64 y[M, rows] = x * ((n - z) * s)^T (+ bias), exact products, fp64 sums."""
+    x = np.ascontiguousarray(x)
+    n = np.ascontiguousarray(n, dtype=np.uint8)
+    s = np.ascontiguousarray(s, dtype=np.uint16)
+    z = np.ascontiguousarray(z, dtype=np.uint8)
+    M, K = x.shape
+    V = n.shape[0]
+    r, nr, rp = _rows_arg(rows, V)
+    y = np.empty((M, nr), dtype=np.float64)
+    bp = 0
+    if bias is not None:
+        bias = np.ascontiguousarray(bias, dtype=np.float32)
+        bp = _ptr(bias)
+    rc = _load().orc_logits_zp(_ptr(x), _dtype_code(x, x_dtype), M, _ptr(n), _ptr(s), _ptr(z),
+                               scale_dtype, V, K, group, bp or None, rp or None, nr, _ptr(y))
+    _check(rc, "logits_zp")
+    return y
+
+
+def embed_zp(n: np.ndarray, s: np.ndarray, z: np.ndarray, scale_dtype: int, group: int, ids,
+             out_dtype: int = F32) -> np.ndarray:
+    """Embedding rows (n[id,k] - z[id,g]) * s[id,g] rounded once to out_dtype;
+    ids outside [0, V) give zero rows."""
+    n = np.ascontiguousarray(n, dtype=np.uint8)
+    s = np.ascontiguousarray(s, dtype=np.uint16)
+    z = np.ascontiguousarray(z, dtype=np.uint8)
+    ids = np.ascontiguousarray(np.asarray(ids, dtype=np.int32).ravel())
+    V, K = n.shape
+    out = np.empty((len(ids), K), dtype=np.float32 if out_dtype == F32 else np.uint16)
+    if len(ids):
+        rc = _load().orc_embed_zp(_ptr(n), _ptr(s), _ptr(z), scale_dtype, V, K, group, _ptr(ids),
+                                  len(ids), out_dtype, _ptr(out))
+        _check(rc, "embed_zp")
+    return out
 
 
 # ---- top-K and rescoring -------------------------------------------------------

@@ -13,6 +13,9 @@
  *     with the least-squared-error clip-ratio search, the scale rounded to the
  *     16-bit scale type before q is chosen (page "radiance_lmhead_int4.py":
  *     docstring "How" paragraph, module constants, quantize_int4_rows);
+ *   - the asymmetric variant: unsigned codes with a per-group zero point
+ *     (reading R21: plain min/max round-to-nearest, zero kept exact), its
+ *     packed form (an extra zero-point region), logits and embedding rows;
  *   - the packed blob layout (our own gfx950 layout; the byte-level definition
  *     is in include/lmhead.h and restated in the comments below);
  *   - logits y[m,v] = sum_k x[m,k] * q[v,k] * s[v,k/G] (+ bias[v]), exact
@@ -43,7 +46,12 @@
  *      order);
  *   R5 top-K order is value descending, then index ascending; the top-1 after
  *      rescoring is the first maximum of the whole scattered vector;
- *   R7 the scale is fl32(amax * fl32(r / qmax)), the page's literal form.
+ *   R7 the scale is fl32(amax * fl32(r / qmax)), the page's literal form;
+ *   R21 the asymmetric form: the pages name it (a per-group zero point in place
+ *      of the module's fixed nibble offset 8; an asymmetric lm_head checkpoint)
+ *      but give no quantizer for it, so it is plain min/max round-to-nearest
+ *      over [min(0, min w), max(0, max w)] with the scale rules of R2/R7 and a
+ *      rounded, clamped zero point; no clip search.
  */
 #include <math.h>
 #include <stdint.h>
@@ -229,6 +237,66 @@ int orc_quantize(const void* w, int w_dtype, int64_t V, int64_t K, int bits, int
 }
 
 /* ------------------------------------------------------------------------ */
+/* Asymmetric (zero-point) quantizer.  The module page keeps the constant its */
+/* kernel subtracts from every code (ZP_BIAS = 8 with HAS_ZP off, so the      */
+/* symmetric code is q + 8) and another page lists an asymmetric ("symFalse") */
+/* lm_head checkpoint; a per-group zero point z replaces that constant:       */
+/*     w ~ (n - z) * s,   n, z unsigned in [0, qr],  qr = 15 (int4) / 255.   */
+/* The pages give no asymmetric quantizer; the plain min/max round-to-nearest */
+/* one is used (reading R21), with zero kept exactly representable:          */
+/*   lo = min(0, min w), hi = max(0, max w); lo == hi (all zero): s = z = n = 0;*/
+/*   s = round16( max( fl32( fl32(hi - lo) * fl32(1 / qr) ), floor ) )        */
+/*   z = clamp( rint( fl32(-lo / s) ), 0, qr )                                */
+/*   n_k = clamp( rint( fl32(w_k / s) ) + z, 0, qr )                          */
+/* with the floor and the 16-bit rounding of the symmetric quantizer (R2).    */
+/* ------------------------------------------------------------------------ */
+int orc_quantize_asym(const void* w, int w_dtype, int64_t V, int64_t K, int bits, int64_t G,
+                      int scale_dtype, uint8_t* n_out, uint16_t* s_out, uint8_t* z_out) {
+    if (!w || !n_out || !s_out || !z_out) return ORC_EARG;
+    if (bits != 4 && bits != 8) return ORC_EARG;
+    if (G <= 0 || K % G != 0 || V < 0) return ORC_EARG;
+    if (scale_dtype != ORC_F16 && scale_dtype != ORC_BF16) return ORC_EARG;
+    const int qr = (bits == 4) ? 15 : 255;
+    const float c = (float)(1.0 / (double)qr);
+    const float floor_s = (scale_dtype == ORC_BF16) ? 1e-8f : (float)ldexp(1.0, -24);
+    const int64_t NG = K / G;
+    for (int64_t v = 0; v < V; ++v) {
+        for (int64_t g = 0; g < NG; ++g) {
+            const int64_t base = v * K + g * G;
+            float lo = 0.0f, hi = 0.0f;
+            for (int64_t k = 0; k < G; ++k) {
+                const float x = (float)load_as_double(w, w_dtype, base + k);
+                if (x < lo) lo = x;
+                if (x > hi) hi = x;
+            }
+            uint8_t* nd = n_out + base;
+            if (hi == lo) { /* all zero */
+                memset(nd, 0, (size_t)G);
+                s_out[v * NG + g] = 0;
+                z_out[v * NG + g] = 0;
+                continue;
+            }
+            float s32 = (hi - lo) * c;
+            if (s32 < floor_s) s32 = floor_s;
+            const float s = scale_round(s32, scale_dtype);
+            float zf = rintf(-lo / s);
+            if (zf < 0.0f) zf = 0.0f;
+            if (zf > (float)qr) zf = (float)qr;
+            for (int64_t k = 0; k < G; ++k) {
+                const float x = (float)load_as_double(w, w_dtype, base + k);
+                float n = rintf(x / s) + zf;
+                if (n < 0.0f) n = 0.0f;
+                if (n > (float)qr) n = (float)qr;
+                nd[k] = (uint8_t)n;
+            }
+            s_out[v * NG + g] = scale_bits(s, scale_dtype);
+            z_out[v * NG + g] = (uint8_t)zf;
+        }
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Packed blob.                                                               */
 /* Rows are grouped in blocks of 64 (the last block is padded with q = 0,     */
 /* s = 0).  A row of one block is cut into superchunks of `span` columns     */
@@ -335,6 +403,131 @@ int orc_unpack(const uint8_t* blob, int64_t V, int64_t K, int bits, int64_t G, i
 }
 
 /* ------------------------------------------------------------------------ */
+/* ------------------------------------------------------------------------ */
+/* Packed blob of the zero-point form: the codes n are stored as they are     */
+/* (nibble n, byte n), the scales as above, and after the scales one byte per */
+/* (row, group) holds z, at byte offset (b * NG + g) * 64 + 4 * (r mod 16) +  */
+/* (r div 16) of that region (a lane that owns rows r, r + 16, r + 32, r + 48 */
+/* of a block reads its four zero points as one 32-bit word).  Padding rows:  */
+/* n = 0, s = 0, z = 0.                                                       */
+/* ------------------------------------------------------------------------ */
+int64_t orc_packed_bytes_zp(int64_t V, int64_t K, int bits, int64_t G) {
+    if (!layout_ok(V, K, bits, G)) return -1;
+    int64_t vpad = (V + 63) / 64 * 64;
+    return vpad * K * bits / 8 + vpad * (K / G) * 3;
+}
+
+static int64_t zp_off(int64_t v, int64_t g, int64_t NG) {
+    const int64_t r = v % 64;
+    return ((v / 64) * NG + g) * 64 + 4 * (r % 16) + r / 16;
+}
+
+int orc_pack_zp(const uint8_t* n, const uint16_t* s, const uint8_t* z, int64_t V, int64_t K,
+                int bits, int64_t G, uint8_t* out) {
+    if (!n || !s || !z || !out || !layout_ok(V, K, bits, G)) return ORC_EARG;
+    int64_t vpad = (V + 63) / 64 * 64, NG = K / G;
+    int64_t wbytes = vpad * K * bits / 8, sbytes = vpad * NG * 2;
+    memset(out, 0, (size_t)(wbytes + sbytes + vpad * NG));
+    for (int64_t v = 0; v < V; ++v) {
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t off;
+            int sh;
+            elem_pos(v, k, K, bits, &off, &sh);
+            int nn = n[v * K + k];
+            if (bits == 4)
+                out[off] = (uint8_t)((out[off] & ~(0xF << sh)) | ((nn & 0xF) << sh));
+            else
+                out[off] = (uint8_t)nn;
+        }
+        for (int64_t g = 0; g < NG; ++g) {
+            int64_t e = ((v / 64) * NG + g) * 64 + v % 64;
+            uint16_t sv = s[v * NG + g];
+            out[wbytes + 2 * e] = (uint8_t)(sv & 0xFF);
+            out[wbytes + 2 * e + 1] = (uint8_t)(sv >> 8);
+            out[wbytes + sbytes + zp_off(v, g, NG)] = z[v * NG + g];
+        }
+    }
+    return ORC_OK;
+}
+
+int orc_unpack_zp(const uint8_t* blob, int64_t V, int64_t K, int bits, int64_t G, uint8_t* n,
+                  uint16_t* s, uint8_t* z) {
+    if (!blob || !n || !s || !z || !layout_ok(V, K, bits, G)) return ORC_EARG;
+    int64_t vpad = (V + 63) / 64 * 64, NG = K / G;
+    int64_t wbytes = vpad * K * bits / 8, sbytes = vpad * NG * 2;
+    for (int64_t v = 0; v < V; ++v) {
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t off;
+            int sh;
+            elem_pos(v, k, K, bits, &off, &sh);
+            n[v * K + k] = (bits == 4) ? (uint8_t)((blob[off] >> sh) & 0xF) : blob[off];
+        }
+        for (int64_t g = 0; g < NG; ++g) {
+            int64_t e = ((v / 64) * NG + g) * 64 + v % 64;
+            s[v * NG + g] = (uint16_t)(blob[wbytes + 2 * e] | (blob[wbytes + 2 * e + 1] << 8));
+            z[v * NG + g] = blob[wbytes + sbytes + zp_off(v, g, NG)];
+        }
+    }
+    return ORC_OK;
+}
+
+/* Logits of the zero-point form: y[m, j] = sum_k x[m,k] * ((n[v,k] - z[v,g]) */
+/* * s[v,g]) + bias[v], v = rows[j], exact products, fp64 sums k ascending.   */
+int orc_logits_zp(const void* x, int x_dtype, int64_t M, const uint8_t* n, const uint16_t* s,
+                  const uint8_t* z, int scale_dtype, int64_t V, int64_t K, int64_t G,
+                  const float* bias, const int64_t* rows, int64_t nrows, double* y) {
+    if (!x || !n || !s || !z || !y || G <= 0 || K % G != 0) return ORC_EARG;
+    if (!rows && nrows != V) return ORC_EARG;
+    const int64_t NG = K / G;
+    const int sb = (scale_dtype == ORC_F16) ? 10 : 7, sbias = (scale_dtype == ORC_F16) ? 15 : 127;
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t j = 0; j < nrows; ++j) {
+            int64_t v = rows ? rows[j] : j;
+            if (v < 0 || v >= V) return ORC_EARG;
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double xv = load_as_double(x, x_dtype, m * K + k);
+                int64_t g = k / G;
+                double wv = ((double)n[v * K + k] - (double)z[v * NG + g]) *
+                            dec16(s[v * NG + g], sb, sbias);
+                acc += xv * wv;
+            }
+            if (bias) acc += (double)bias[v];
+            y[m * nrows + j] = acc;
+        }
+    }
+    return ORC_OK;
+}
+
+/* Embedding rows of the zero-point form: out[t, k] = (n[v,k] - z[v,g]) *    */
+/* s[v,g], rounded once to out_dtype; ids outside [0, V) give zero rows.      */
+int orc_embed_zp(const uint8_t* n, const uint16_t* s, const uint8_t* z, int scale_dtype,
+                 int64_t V, int64_t K, int64_t G, const int32_t* ids, int64_t T, int out_dtype,
+                 void* out) {
+    if (!n || !s || !z || !ids || !out || G <= 0 || K % G != 0 || T < 0) return ORC_EARG;
+    if (scale_dtype != ORC_F16 && scale_dtype != ORC_BF16) return ORC_EARG;
+    if (out_dtype != ORC_F32 && out_dtype != ORC_F16 && out_dtype != ORC_BF16) return ORC_EARG;
+    const int64_t NG = K / G;
+    const int sb = (scale_dtype == ORC_F16) ? 10 : 7, sbias = (scale_dtype == ORC_F16) ? 15 : 127;
+    for (int64_t t = 0; t < T; ++t) {
+        const int64_t v = ids[t];
+        for (int64_t k = 0; k < K; ++k) {
+            double p = 0.0;
+            if (v >= 0 && v < V)
+                p = ((double)n[v * K + k] - (double)z[v * NG + k / G]) *
+                    dec16(s[v * NG + k / G], sb, sbias);
+            const float f = (float)p; /* exact: the product fits in fp32 */
+            if (out_dtype == ORC_F32)
+                ((float*)out)[t * K + k] = f;
+            else if (out_dtype == ORC_F16)
+                ((uint16_t*)out)[t * K + k] = enc16(f, 10, 15);
+            else
+                ((uint16_t*)out)[t * K + k] = enc16(f, 7, 127);
+        }
+    }
+    return ORC_OK;
+}
+
 /* Logits from the canonical quantized form (q int8 [V,K], s 16-bit [V,K/G]):*/
 /*   y[m, j] = sum_k x[m,k] * (q[v,k] * s[v, k/G]) + bias[v],  v = rows[j],   */
 /* every operand widened exactly to fp64, the sum taken k ascending.          */
