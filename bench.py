@@ -47,6 +47,7 @@ def algorithmic_bytes(M, V, K, bits, G):
 # Sources whose change invalidates a recorded traffic measurement of the
 # logits kernels.
 TRAFFIC_SOURCES = ["weight_only_quantized_lmhead_amd/csrc/logits.hip",
+                   "weight_only_quantized_lmhead_amd/csrc/logits_kernels.h",
                    "weight_only_quantized_lmhead_amd/csrc/lmh_internal.h",
                    "weight_only_quantized_lmhead_amd/build.py"]
 
@@ -250,6 +251,15 @@ def main() -> int:
         print("bench.py: fused quantize+pack blob differs from pack(quantize(w))", file=sys.stderr)
         return 1
     del fused
+    # the zero-point (asymmetric) form of the same head: round to nearest only
+    zbits = w.bits | lmh.ZP
+    zblob = lmh.quantize_pack(Wd, zbits, w.group, sdt)
+    torch.cuda.synchronize()
+    e0.record()
+    lmh.quantize_pack(Wd, zbits, w.group, sdt, out=zblob)
+    e1.record()
+    torch.cuda.synchronize()
+    qpz_ms = e0.elapsed_time(e1)
 
     # unquantized 16-bit reference rows for rescoring
     if w.w_dtype == "f32":
@@ -260,6 +270,7 @@ def main() -> int:
     blob_bytes = blob.numel()
     R = 1 if args.hot else max(2, math.ceil(1e9 / blob_bytes))
     blobs = [blob] + [blob.clone() for _ in range(R - 1)]
+    zblobs = [zblob] + [zblob.clone() for _ in range(R - 1)]
     xs = {M: to_dev(synth.activations(w, M), w.x_dtype) for M in Ms}
     outs = {M: torch.empty((M, w.V), dtype=torch.float32, device=dev) for M in Ms}
     wss = {M: lmh.logits_workspace(M, w.K, TD[w.x_dtype], dev) for M in Ms}
@@ -352,6 +363,15 @@ def main() -> int:
                                      "GB/s": round(B / (t_us * 1e-6) / 1e9, 1),
                                      "TFLOP/s": round(2.0 * M * w.V * w.K / (t_us * 1e-6) / 1e12, 2)}
         del o16
+    # zero-point heads: the same kernels with a per-row, per-group zero point
+    for M in Ms:
+        t_us = timed_loop(lambda i, M=M: lmh.logits(
+            xs[M], zblobs[i % R], w.V, w.K, zbits, w.group, sdt, out=outs[M], workspace=wss[M],
+            path=args.path), args.steps)
+        B = algorithmic_bytes(M, w.V, w.K, w.bits, w.group) + w.V * (w.K // w.group)
+        per_call[f"M={M} zp"] = {"us": round(t_us, 3), "algorithmic_bytes": B,
+                                  "GB/s": round(B / (t_us * 1e-6) / 1e9, 1),
+                                  "TFLOP/s": round(2.0 * M * w.V * w.K / (t_us * 1e-6) / 1e12, 2)}
     rs_us = timed_loop(lambda i: rescore(), args.steps)
     per_call[f"top{args.topk}_rescore"] = {"us": round(rs_us, 3), "M": m_rs}
     fu_us = timed_loop(one_call, args.steps)
@@ -416,6 +436,7 @@ def main() -> int:
         "per_call": per_call,
         "load_time": {"quantize_ms": round(quant_ms, 3), "pack_ms": round(pack_ms, 3),
                       "quantize_pack_ms": round(qp_ms, 3),
+                      "quantize_pack_zp_ms": round(qpz_ms, 3),
                       "clip": w.clip},
         "roofline": roofline,
         "cpu_baseline": cpu,

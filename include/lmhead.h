@@ -50,6 +50,27 @@
  *   Scale region, starting at byte V_pad*K*bits/8: 16-bit scales (fp16 or
  *     bf16 bit patterns), element offset (b*NG + g)*64 + r.
  *   Total size: V_pad*K*bits/8 + V_pad*NG*2 bytes (lmhead_packed_bytes).
+ *
+ * Zero-point (asymmetric) heads: `bits | LMH_ZP`
+ *   The module page keeps a constant that its kernel subtracts from every
+ *   nibble (ZP_BIAS = 8, with its HAS_ZP switch off), and the vLLM PR's page
+ *   lists an asymmetric ("symFalse") quantized lm_head checkpoint: in that
+ *   form each row and group has its own zero point z in place of the fixed 8,
+ *       w[v, k] ~ (n[v, k] - z[v, g]) * s[v, g],   g = k / G,
+ *   with unsigned codes n and z in [0, qr], qr = 15 (int4) or 255 (int8), so
+ *       y[m, v] = sum_k x[m, k] * (n[v, k] - z[v, g]) * s[v, g]  (+ bias[v]).
+ *   Passing bits | LMH_ZP (LMH_ZP = 0x10) to lmhead_packed_bytes,
+ *   lmhead_quantize_pack, lmhead_embed and every logits entry point selects
+ *   that form; lmhead_quantize_zp and lmhead_pack_zp are its codes-mode
+ *   quantizer and packer.  Its blob differs from the symmetric one in three
+ *   points: codes are stored as they are (nibble n, byte n; padding rows 0),
+ *   and after the scale region a zero-point region of V_pad*NG bytes holds z
+ *   for (block b, group g, row r) at byte offset
+ *         (b*NG + g)*64 + 4*(r % 16) + r / 16
+ *   (one 32-bit word holds the zero points of rows r, r+16, r+32, r+48: the
+ *   rows one MFMA lane unpacks); padding rows have z = 0.  Total size:
+ *   V_pad*K*bits/8 + V_pad*NG*3 bytes.  A symmetric head is the special case
+ *   z = 8 (int4) / 128 (int8), n = q + 8 / q + 128.
  *   Why: a lane that owns a row reads one 16-byte slot per 32 (int8: 16)
  *   columns, 64 consecutive rows read 1 KiB contiguously, and the same slot,
  *   read by 16 rows x 4 slots, is exactly one 16x16x32 MFMA B-operand tile
@@ -83,6 +104,7 @@ enum {
 
 enum { LMH_F32 = 0, LMH_F16 = 1, LMH_BF16 = 2 };
 enum { LMH_CLIP_RTN = 0, LMH_CLIP_MSE = 1 };
+enum { LMH_ZP = 0x10 }; /* OR'd into `bits`: the zero-point (asymmetric) form */
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* lmhead_status_string(int status);
@@ -91,8 +113,9 @@ const char* lmhead_status_string(int status);
 int lmhead_abi_version(void);
 
 /*
- * lmhead_packed_bytes -- size in bytes of the packed blob for a V x K head,
- * or 0 if the shape is not supported.  Host-only; launches nothing.
+ * lmhead_packed_bytes -- size in bytes of the packed blob for a V x K head
+ * (bits may carry LMH_ZP), or 0 if the shape is not supported.  Host-only;
+ * launches nothing.
  */
 size_t lmhead_packed_bytes(int64_t V, int64_t K, int bits, int64_t group);
 
@@ -134,6 +157,41 @@ int lmhead_pack(const int8_t* q, const void* s, int64_t V, int64_t K, int bits, 
                 void* packed_out, void* stream);
 
 /*
+ * lmhead_quantize_zp -- load-time quantizer of the zero-point form (see
+ *   "Zero-point heads" above).  The pages name that form but give no
+ *   quantizer for it; this one is plain per-group min/max round-to-nearest
+ *   over the group's range widened to include zero, so that w = 0 is exactly
+ *   representable (n = z).  For each row v and group g of G columns:
+ *     lo = min(0, min w), hi = max(0, max w); lo == hi (all zero) gives
+ *       s = 0, z = 0 and n = 0 for the group;
+ *     s = to16( max( fl32( fl32(hi - lo) * fl32(1 / qr) ), floor ) ), with
+ *       floor and to16 as for lmhead_quantize;
+ *     z = clamp( rint( fl32(-lo / s) ), 0, qr );
+ *     n = clamp( rint( fl32(w / s) ) + z, 0, qr )   (IEEE division, ties to
+ *       even).
+ *   No clip search.  Bit-exact, deterministic.
+ *   w      [V, K] row-major, w_dtype LMH_F32 / LMH_F16 / LMH_BF16.
+ *   n_out  [V, K] uint8 codes, row-major.
+ *   s_out  [V, K/G] 16-bit scale bit patterns, scale_dtype LMH_F16 / LMH_BF16.
+ *   z_out  [V, K/G] uint8 zero points, row-major (any alignment).
+ *   bits   4 or 8 (LMH_ZP may be set; it is implied).  Shape rules as for
+ *          lmhead_quantize.
+ */
+int lmhead_quantize_zp(const void* w, int w_dtype, int64_t V, int64_t K, int bits, int64_t group,
+                       int scale_dtype, uint8_t* n_out, void* s_out, uint8_t* z_out,
+                       void* stream);
+
+/*
+ * lmhead_pack_zp -- write the zero-point blob (layout above) from the codes
+ *   n [V, K] uint8, scales s [V, K/G] (16-bit patterns) and zero points
+ *   z [V, K/G] uint8 (any alignment).  Codes or zero points above qr are a
+ *   precondition violation.  packed_out must hold
+ *   lmhead_packed_bytes(V, K, bits | LMH_ZP, group) bytes.  Deterministic.
+ */
+int lmhead_pack_zp(const uint8_t* n, const void* s, const uint8_t* z, int64_t V, int64_t K,
+                   int bits, int64_t group, void* packed_out, void* stream);
+
+/*
  * lmhead_quantize_pack -- the quantizer and the packer fused: rows
  *   [row0, row0 + rows) of a V x K head go straight from the unquantized
  *   weight into their place in the packed blob, with no int8 copy of the
@@ -154,7 +212,10 @@ int lmhead_pack(const int8_t* q, const void* s, int64_t V, int64_t K, int bits, 
  *              the blocks of this chunk are written, other bytes are left
  *              as they are.
  *   clip, scale_dtype, bits, group as for lmhead_quantize; layout rules as
- *   for lmhead_pack.  rows == 0 is a valid empty call.  Deterministic.
+ *   for lmhead_pack.  With bits | LMH_ZP the arithmetic is that of
+ *   lmhead_quantize_zp and the blob the zero-point one (clip must be
+ *   LMH_CLIP_RTN, else LMH_E_UNSUPPORTED).  rows == 0 is a valid empty call.
+ *   Deterministic.
  */
 int lmhead_quantize_pack(const void* w, int w_dtype, int64_t ldw, int64_t V, int64_t K, int bits,
                          int64_t group, int scale_dtype, int clip, int64_t row0, int64_t rows,
@@ -164,6 +225,7 @@ int lmhead_quantize_pack(const void* w, int w_dtype, int64_t ldw, int64_t V, int
  * lmhead_embed -- the input-embedding lookup of a tied head, read from the
  *   same packed blob the logits use:
  *       out[t, k] = q[id, k] * s[id, k / G],   id = ids[t],
+ *   (zero-point heads, bits | LMH_ZP: (n[id, k] - z[id, k / G]) * s[id, k / G]),
  *   the product exact, rounded once to out_dtype (LMH_F32: exact; LMH_F16 /
  *   LMH_BF16: nearest, ties to even; an fp16 result beyond its range becomes
  *   +-inf).  vLLM PR #48870, Purpose: the quantized embedding table that
@@ -213,6 +275,9 @@ size_t lmhead_logits_workspace_bytes(int64_t M, int64_t K, int x_dtype);
  *   MFMA kernel runs the same per-group MFMA chains and fp32 scale FMAs in
  *   the same order, so they give bit-identical results.  The result does not
  *   depend on the stream or on other calls.
+ *   Zero-point heads (bits | LMH_ZP) run the same kernels with each row's
+ *   per-group zero point subtracted from its codes while they are unpacked
+ *   (n - z is exact in fp16), so the arithmetic is otherwise the same.
  */
 int lmhead_logits(const void* x, int x_dtype, int64_t M, const void* packed, int64_t V, int64_t K,
                   int bits, int64_t group, int scale_dtype, const float* bias, float* y,

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     assert len(names) >= 10
     for n in names:
         assert hasattr(L, n), f"{n} declared in lmhead.h but not exported"
-    assert L.lmhead_abi_version() == 1
+    assert L.lmhead_abi_version() == 2
 
 
 def test_status_strings():
@@ -254,3 +254,43 @@ def test_logits_typed_validation():
     assert lt(ydt=F32, y=P + 2) == E_ALIGN
     assert lt(ydt=BF16, ldy=100) == E_SHAPE
     assert lt(ydt=F16, M=0) == OK
+
+
+ZP = 0x10
+
+
+@pytest.mark.parametrize("V,K,bits,G", [(151936, 1024, 4, 64), (151936, 1024, 8, 128),
+                                        (1, 128, 4, 32), (65, 64, 8, 32), (100, 256, 4, 256)])
+def test_zero_point_packed_bytes_matches_layout(V, K, bits, G):
+    assert lmh.packed_bytes(V, K, bits | ZP, G) == oracle.packed_bytes_zp(V, K, bits, G)
+    assert lmh.lib().lmhead_packed_bytes(10, 128, 3 | ZP, 32) == 0
+
+
+def test_zero_point_validation():
+    L = lmh.lib()
+    qz = L.lmhead_quantize_zp
+    assert qz(P, F32, 4, 128, 5, 64, F16, P, P, P, None) == E_UNSUP
+    assert qz(P, 7, 4, 128, 4, 64, F16, P, P, P, None) == E_DTYPE
+    assert qz(P, F32, 4, 128, 4, 64, F32, P, P, P, None) == E_DTYPE
+    assert qz(P, F32, 4, 100, 4, 64, F16, P, P, P, None) == E_SHAPE
+    assert qz(P, F32, 4, 128, 4, 64, F16, P, P, None, None) == E_NULL   # z_out is required
+    assert qz(P, F32, 4, 128, 4, 64, F16, P + 8, P, P, None) == E_ALIGN
+    assert qz(P, F32, 0, 128, 4 | ZP, 64, F16, P, P, P, None) == OK
+    # the symmetric entry points do not take the flag
+    assert L.lmhead_quantize(P, F32, 4, 128, 4 | ZP, 64, F16, 0, P, P, None) == E_UNSUP
+    assert L.lmhead_pack(P, P, 4, 128, 4 | ZP, 64, P, None) == E_UNSUP
+    pz = L.lmhead_pack_zp
+    assert pz(P, P, P, 4, 100, 4, 64, P, None) == E_SHAPE
+    assert pz(P, P, None, 4, 128, 4, 64, P, None) == E_NULL
+    assert pz(P, P, P, 4, 128, 4, 64, P + 1, None) == E_ALIGN
+    assert pz(P, P, P, 0, 128, 8, 64, P, None) == OK
+    # fused quantize + pack: round to nearest only
+    qp = L.lmhead_quantize_pack
+    assert qp(P, F32, 128, 200, 128, 4 | ZP, 64, F16, 1, 0, 200, P, None) == E_UNSUP
+    assert qp(P, F32, 128, 200, 128, 4 | ZP, 64, F16, 0, 0, 0, P, None) == OK
+    # logits and embedding accept the flag (empty requests launch nothing)
+    assert _logits(bits=4 | ZP, M=0) == OK
+    assert _logits(bits=8 | ZP, G=64, V=0) == OK
+    assert _logits(bits=3 | ZP) == E_UNSUP
+    assert _logits(bits=4 | ZP, path=5) == E_UNSUP
+    assert L.lmhead_embed(P, 0, P, 128, 128, 4 | ZP, 64, F16, P, F16, 128, None) == OK

@@ -10,6 +10,10 @@ missing or fails to load, importing the binding's functions raises.
     packed = lmh.quantize_pack(w, bits=4, group=64, scale_dtype=torch.float16, clip="rtn")
     y = lmh.logits(x, packed, V, K, bits=4, group=64, scale_dtype=torch.float16)
     idx, val, top1 = lmh.topk_rescore(x, w_ref, y, topk=8)
+
+Zero-point (asymmetric) heads: pass ``bits | lmh.ZP`` wherever a ``bits``
+argument is taken (quantize_pack, embed, logits, logits_topk, packed_bytes);
+``quantize_zp`` / ``pack_zp`` are the codes-mode quantizer and packer.
 """
 from __future__ import annotations
 
@@ -26,6 +30,7 @@ LMH_OK = 0
 _DT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 _CLIP = {"rtn": 0, "mse": 1}
 PATH_AUTO, PATH_GEMV, PATH_MFMA, PATH_MFMA_LDS, PATH_MFMA_XRES = 0, 1, 2, 3, 4
+ZP = 0x10  # LMH_ZP: OR'd into `bits`, selects the zero-point form
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -51,6 +56,8 @@ def lib() -> ctypes.CDLL:
             "lmhead_packed_bytes": (sz, [i64, i64, i32, i64]),
             "lmhead_quantize": (i32, [vp, i32, i64, i64, i32, i64, i32, i32, vp, vp, vp]),
             "lmhead_pack": (i32, [vp, vp, i64, i64, i32, i64, vp, vp]),
+            "lmhead_quantize_zp": (i32, [vp, i32, i64, i64, i32, i64, i32, vp, vp, vp, vp]),
+            "lmhead_pack_zp": (i32, [vp, vp, vp, i64, i64, i32, i64, vp, vp]),
             "lmhead_quantize_pack": (i32, [vp, i32, i64, i64, i64, i32, i64, i32, i32, i64, i64,
                                            vp, vp]),
             "lmhead_embed": (i32, [vp, i64, vp, i64, i64, i32, i64, i32, vp, i32, i64, vp]),
@@ -125,6 +132,31 @@ def pack(q: torch.Tensor, s: torch.Tensor, bits: int, group: int) -> torch.Tenso
     out = torch.empty(packed_bytes(V, K, bits, group), dtype=torch.uint8, device=q.device)
     _check("lmhead_pack", lib().lmhead_pack(_ptr(q), _ptr(s), V, K, bits, group, _ptr(out),
                                             _stream(q)))
+    return out
+
+
+def quantize_zp(w: torch.Tensor, bits: int, group: int,
+                scale_dtype: torch.dtype = torch.float16
+                ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """(n uint8 [V,K], s [V,K/G] in scale_dtype, z uint8 [V,K/G]) -- lmhead_quantize_zp."""
+    _need_cuda(w)
+    V, K = w.shape
+    n = torch.empty((V, K), dtype=torch.uint8, device=w.device)
+    s = torch.empty((V, K // group), dtype=scale_dtype, device=w.device)
+    z = torch.empty((V, K // group), dtype=torch.uint8, device=w.device)
+    _check("lmhead_quantize_zp", lib().lmhead_quantize_zp(
+        _ptr(w), _DT[w.dtype], V, K, bits, group, _DT[scale_dtype], _ptr(n), _ptr(s), _ptr(z),
+        _stream(w)))
+    return n, s, z
+
+
+def pack_zp(n: torch.Tensor, s: torch.Tensor, z: torch.Tensor, bits: int, group: int) -> torch.Tensor:
+    """Zero-point packed blob (uint8) -- lmhead_pack_zp."""
+    _need_cuda(n, s, z)
+    V, K = n.shape
+    out = torch.empty(packed_bytes(V, K, bits | ZP, group), dtype=torch.uint8, device=n.device)
+    _check("lmhead_pack_zp", lib().lmhead_pack_zp(_ptr(n), _ptr(s), _ptr(z), V, K, bits, group,
+                                                  _ptr(out), _stream(n)))
     return out
 
 
@@ -295,10 +327,12 @@ class QuantizedHead:
     """A packed LM head resident on the GPU: quantize + pack once, then logits per call."""
 
     def __init__(self, w: torch.Tensor, bits: int, group: int,
-                 scale_dtype: torch.dtype = torch.float16, clip: str = "rtn"):
+                 scale_dtype: torch.dtype = torch.float16, clip: str = "rtn", zp: bool = False):
         self.V, self.K = w.shape
-        self.bits, self.group, self.scale_dtype = bits, group, scale_dtype
-        self.packed = quantize_pack(w, bits, group, scale_dtype, clip)
+        # zero-point heads carry the LMH_ZP flag in `bits` for every call
+        self.bits = bits | ZP if zp else bits
+        self.group, self.scale_dtype = group, scale_dtype
+        self.packed = quantize_pack(w, self.bits, group, scale_dtype, clip)
 
     def embed(self, ids: torch.Tensor, out_dtype: torch.dtype = torch.float16) -> torch.Tensor:
         """Input-embedding rows of the same packed table (tied head)."""

@@ -14,7 +14,7 @@ using lmh::BF16;
 using lmh::F16;
 using lmh::F32;
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -31,6 +31,13 @@ int check_layout(int64_t V, int64_t K, int bits, int64_t G) {
 }
 
 int from_hip(hipError_t e) { return e == hipSuccess ? LMH_OK : LMH_E_HIP; }
+
+// A `bits` argument: the code width, optionally with LMH_ZP (zero-point form).
+struct Width {
+    int bits;
+    bool zp;
+};
+Width width_of(int b) { return {b & ~LMH_ZP, (b & LMH_ZP) != 0}; }
 
 }  // namespace
 
@@ -52,37 +59,56 @@ const char* lmhead_status_string(int status) {
 
 int lmhead_abi_version(void) { return kAbiVersion; }
 
-size_t lmhead_packed_bytes(int64_t V, int64_t K, int bits, int64_t group) {
-    if (check_layout(V, K, bits, group) != LMH_OK) return 0;
+size_t lmhead_packed_bytes(int64_t V, int64_t K, int bits_arg, int64_t group) {
+    const Width wd = width_of(bits_arg);
+    if (check_layout(V, K, wd.bits, group) != LMH_OK) return 0;
     const int64_t vpad = (V + 63) / 64 * 64;
-    return (size_t)(vpad * K * bits / 8 + vpad * (K / group) * 2);
+    return (size_t)(vpad * K * wd.bits / 8 + vpad * (K / group) * (wd.zp ? 3 : 2));
 }
 
-int lmhead_quantize(const void* w, int w_dtype, int64_t V, int64_t K, int bits, int64_t group,
-                    int scale_dtype, int clip, int8_t* q_out, void* s_out, void* stream) {
+static int quantize_impl(const void* w, int w_dtype, int64_t V, int64_t K, int bits, int64_t group,
+                         int scale_dtype, int clip, int8_t* q_out, void* s_out, uint8_t* z_out,
+                         bool zp, void* stream) {
     if (bits != 4 && bits != 8) return LMH_E_UNSUPPORTED;
+    if (zp && clip != LMH_CLIP_RTN) return LMH_E_UNSUPPORTED;
     if (w_dtype != F32 && w_dtype != F16 && w_dtype != BF16) return LMH_E_DTYPE;
     if (scale_dtype != F16 && scale_dtype != BF16) return LMH_E_DTYPE;
     if (clip != LMH_CLIP_RTN && clip != LMH_CLIP_MSE) return LMH_E_UNSUPPORTED;
     if (V < 0 || K < 1 || group < 32 || group % 32 != 0 || K % group != 0) return LMH_E_SHAPE;
     if (V * K >= (int64_t(1) << 40)) return LMH_E_SHAPE;
     if (V == 0) return LMH_OK;
-    if (!w || !q_out || !s_out) return LMH_E_NULL;
+    if (!w || !q_out || !s_out || (zp && !z_out)) return LMH_E_NULL;
     if (!aligned16(w) || !aligned16(q_out)) return LMH_E_ALIGN;
     if (((uintptr_t)s_out & 1u) != 0) return LMH_E_ALIGN;
     return from_hip(lmh::launch_quantize(w, w_dtype, V, K, bits, group, scale_dtype,
                                          clip == LMH_CLIP_MSE ? 5 : 1, q_out, (uint16_t*)s_out,
-                                         (hipStream_t)stream));
+                                         zp ? z_out : nullptr, (hipStream_t)stream));
 }
 
-int lmhead_quantize_pack(const void* w, int w_dtype, int64_t ldw, int64_t V, int64_t K, int bits,
-                         int64_t group, int scale_dtype, int clip, int64_t row0, int64_t rows,
-                         void* packed_out, void* stream) {
+int lmhead_quantize(const void* w, int w_dtype, int64_t V, int64_t K, int bits, int64_t group,
+                    int scale_dtype, int clip, int8_t* q_out, void* s_out, void* stream) {
+    return quantize_impl(w, w_dtype, V, K, bits, group, scale_dtype, clip, q_out, s_out, nullptr,
+                         false, stream);
+}
+
+int lmhead_quantize_zp(const void* w, int w_dtype, int64_t V, int64_t K, int bits, int64_t group,
+                       int scale_dtype, uint8_t* n_out, void* s_out, uint8_t* z_out,
+                       void* stream) {
+    return quantize_impl(w, w_dtype, V, K, bits & ~LMH_ZP, group, scale_dtype, LMH_CLIP_RTN,
+                         (int8_t*)n_out, s_out, z_out, true, stream);
+}
+
+int lmhead_quantize_pack(const void* w, int w_dtype, int64_t ldw, int64_t V, int64_t K,
+                         int bits_arg, int64_t group, int scale_dtype, int clip, int64_t row0,
+                         int64_t rows, void* packed_out, void* stream) {
+    const Width wd = width_of(bits_arg);
+    const int bits = wd.bits;
     const int rc = check_layout(V, K, bits, group);
     if (rc != LMH_OK) return rc;
     if (w_dtype != F32 && w_dtype != F16 && w_dtype != BF16) return LMH_E_DTYPE;
     if (scale_dtype != F16 && scale_dtype != BF16) return LMH_E_DTYPE;
     if (clip != LMH_CLIP_RTN && clip != LMH_CLIP_MSE) return LMH_E_UNSUPPORTED;
+    if (wd.zp && clip != LMH_CLIP_RTN) return LMH_E_UNSUPPORTED;
     if (row0 < 0 || rows < 0 || row0 > V || rows > V - row0 || row0 % 64 != 0) return LMH_E_SHAPE;
     if (rows % 64 != 0 && row0 + rows != V) return LMH_E_SHAPE;
     if (ldw < K || ldw % 8 != 0) return LMH_E_SHAPE;
@@ -93,25 +119,37 @@ int lmhead_quantize_pack(const void* w, int w_dtype, int64_t ldw, int64_t V, int
     const int64_t units = (rows + 63) / 64 * (K / std::max<int64_t>(group, lmh::span_of(bits)));
     if ((units + 3) / 4 >= (int64_t(1) << 31)) return LMH_E_UNSUPPORTED;
     return from_hip(lmh::launch_quantize_pack(w, w_dtype, ldw, V, K, bits, group, scale_dtype,
-                                              clip == LMH_CLIP_MSE ? 5 : 1, row0, rows,
+                                              clip == LMH_CLIP_MSE ? 5 : 1, wd.zp, row0, rows,
                                               (uint8_t*)packed_out, (hipStream_t)stream));
+}
+
+static int pack_impl(const int8_t* q, const void* s, const uint8_t* z, bool zp, int64_t V,
+                     int64_t K, int bits, int64_t group, void* packed_out, void* stream) {
+    const int rc = check_layout(V, K, bits, group);
+    if (rc != LMH_OK) return rc;
+    if (V == 0) return LMH_OK;
+    if (!q || !s || !packed_out || (zp && !z)) return LMH_E_NULL;
+    if (!aligned16(q) || !aligned16(packed_out)) return LMH_E_ALIGN;
+    if (((uintptr_t)s & 1u) != 0) return LMH_E_ALIGN;
+    return from_hip(lmh::launch_pack(q, (const uint16_t*)s, zp ? z : nullptr, V, K, bits, group,
+                                     (uint8_t*)packed_out, (hipStream_t)stream));
 }
 
 int lmhead_pack(const int8_t* q, const void* s, int64_t V, int64_t K, int bits, int64_t group,
                 void* packed_out, void* stream) {
-    const int rc = check_layout(V, K, bits, group);
-    if (rc != LMH_OK) return rc;
-    if (V == 0) return LMH_OK;
-    if (!q || !s || !packed_out) return LMH_E_NULL;
-    if (!aligned16(q) || !aligned16(packed_out)) return LMH_E_ALIGN;
-    if (((uintptr_t)s & 1u) != 0) return LMH_E_ALIGN;
-    return from_hip(lmh::launch_pack(q, (const uint16_t*)s, V, K, bits, group, (uint8_t*)packed_out,
-                                     (hipStream_t)stream));
+    return pack_impl(q, s, nullptr, false, V, K, bits, group, packed_out, stream);
 }
 
-int lmhead_embed(const int32_t* ids, int64_t T, const void* packed, int64_t V, int64_t K, int bits,
-                 int64_t group, int scale_dtype, void* out, int out_dtype, int64_t ldo,
+int lmhead_pack_zp(const uint8_t* n, const void* s, const uint8_t* z, int64_t V, int64_t K,
+                   int bits, int64_t group, void* packed_out, void* stream) {
+    return pack_impl((const int8_t*)n, s, z, true, V, K, bits & ~LMH_ZP, group, packed_out, stream);
+}
+
+int lmhead_embed(const int32_t* ids, int64_t T, const void* packed, int64_t V, int64_t K,
+                 int bits_arg, int64_t group, int scale_dtype, void* out, int out_dtype, int64_t ldo,
                  void* stream) {
+    const Width wd = width_of(bits_arg);
+    const int bits = wd.bits;
     const int rc = check_layout(V, K, bits, group);
     if (rc != LMH_OK) return rc;
     if (scale_dtype != F16 && scale_dtype != BF16) return LMH_E_DTYPE;
@@ -125,7 +163,8 @@ int lmhead_embed(const int32_t* ids, int64_t T, const void* packed, int64_t V, i
     const int64_t threads = T * (K / lmh::span_of(bits)) * 4;
     if ((threads + 255) / 256 >= (int64_t(1) << 31)) return LMH_E_UNSUPPORTED;
     return from_hip(lmh::launch_embed(ids, T, (const uint8_t*)packed, V, K, bits, group,
-                                      scale_dtype, out, out_dtype, ldo, (hipStream_t)stream));
+                                      scale_dtype, wd.zp, out, out_dtype, ldo,
+                                      (hipStream_t)stream));
 }
 
 size_t lmhead_logits_workspace_bytes(int64_t M, int64_t K, int x_dtype) {
@@ -134,9 +173,11 @@ size_t lmhead_logits_workspace_bytes(int64_t M, int64_t K, int x_dtype) {
 }
 
 static int logits_impl(const void* x, int x_dtype, int64_t M, const void* packed, int64_t V,
-                       int64_t K, int bits, int64_t group, int scale_dtype, const float* bias,
+                       int64_t K, int bits_arg, int64_t group, int scale_dtype, const float* bias,
                        void* y, int y_dtype, int64_t ldy, void* workspace, size_t ws_bytes,
                        void* stream, int path) {
+    const Width wd = width_of(bits_arg);
+    const int bits = wd.bits;
     int rc = check_layout(V, K, bits, group);
     if (rc != LMH_OK) return rc;
     if (x_dtype != F16 && x_dtype != BF16) return LMH_E_DTYPE;
@@ -184,6 +225,7 @@ static int logits_impl(const void* x, int x_dtype, int64_t M, const void* packed
     a.M = (int)M;
     a.bits = bits;
     a.scale_bf16 = scale_dtype == BF16;
+    a.zp = wd.zp;
     const bool use_gemv = path == 1 || (path == 0 && gemv_ok && M <= lmh::kGemvAutoMaxM);
     if (use_gemv) return from_hip(lmh::launch_gemv(a, st));
     // automatic, from measurements on the 151936 x 1024 heads: the register-fed
@@ -278,7 +320,7 @@ int lmhead_logits_topk(const void* x, int x_dtype, int64_t M, const void* packed
                        const void* w_ref, int w_dtype, int topk, float* y, int64_t ldy,
                        int32_t* idx_out, float* val_out, int32_t* top1_out, void* workspace,
                        size_t ws_bytes, void* stream) {
-    int rc = check_layout(V, K, bits, group);
+    int rc = check_layout(V, K, bits & ~LMH_ZP, group);
     if (rc != LMH_OK) return rc;
     if (x_dtype != F16 && x_dtype != BF16) return LMH_E_DTYPE;
     if (scale_dtype != F16 && scale_dtype != BF16) return LMH_E_DTYPE;

@@ -39,19 +39,23 @@ constexpr int span_of(int bits) { return bits == 4 ? 128 : 64; }
 
 // Launch helpers (defined in the .hip files).  All return hipError_t of the
 // launch; arguments are already validated by the API layer.
+// Codes mode; z non-null selects the zero-point form (q then holds the
+// unsigned codes n and z [V, K/G] the zero points).
 hipError_t launch_quantize(const void* w, int w_dtype, int64_t V, int64_t K, int bits, int64_t G,
-                           int scale_dtype, int nratios, int8_t* q, uint16_t* s, hipStream_t st);
+                           int scale_dtype, int nratios, int8_t* q, uint16_t* s, uint8_t* z,
+                           hipStream_t st);
 // Fused quantize + pack of rows [row0, row0 + rows) (w points at row row0,
 // row stride ldw elements) straight into the blob of a V-row head.
 hipError_t launch_quantize_pack(const void* w, int w_dtype, int64_t ldw, int64_t V, int64_t K,
-                                int bits, int64_t G, int scale_dtype, int nratios, int64_t row0,
-                                int64_t rows, uint8_t* blob, hipStream_t st);
+                                int bits, int64_t G, int scale_dtype, int nratios, bool asym,
+                                int64_t row0, int64_t rows, uint8_t* blob, hipStream_t st);
 // Embedding rows of ids[0..T) from the blob into out (row stride ldo elements).
 hipError_t launch_embed(const int32_t* ids, int64_t T, const uint8_t* blob, int64_t V, int64_t K,
-                        int bits, int64_t G, int scale_dtype, void* out, int out_dtype, int64_t ldo,
-                        hipStream_t st);
-hipError_t launch_pack(const int8_t* q, const uint16_t* s, int64_t V, int64_t K, int bits,
-                       int64_t G, uint8_t* out, hipStream_t st);
+                        int bits, int64_t G, int scale_dtype, bool zp, void* out, int out_dtype,
+                        int64_t ldo, hipStream_t st);
+// z non-null: the zero-point layout (q holds the unsigned codes n).
+hipError_t launch_pack(const int8_t* q, const uint16_t* s, const uint8_t* z, int64_t V, int64_t K,
+                       int bits, int64_t G, uint8_t* out, hipStream_t st);
 
 struct LogitsArgs {
     const void* x;         // [M, K] fp16 (after conversion) row-major
@@ -63,6 +67,7 @@ struct LogitsArgs {
     int64_t ldy;
     int64_t V, K, G;
     int M, bits, scale_bf16;
+    int zp;                // zero-point head: a zero-point region follows the scales
 };
 
 hipError_t launch_x_to_f16(const uint16_t* x_bf16, int M, int K, _Float16* xh, int* xexp,
@@ -73,6 +78,10 @@ hipError_t launch_mfma(const LogitsArgs& a, hipStream_t st);
 bool xres_fits(int64_t K);
 hipError_t launch_mfma_xres(const LogitsArgs& a, hipStream_t st);
 hipError_t launch_mfma_lds(const LogitsArgs& a, hipStream_t st);
+// Logits kernel families (gemv, register MFMA, LDS-staged MFMA, activation
+// resident) and the zero-point instantiations of all of them (logits_zp.hip).
+enum { kFamGemv = 0, kFamMfma = 1, kFamMfmaLds = 2, kFamXres = 3 };
+hipError_t run_family_zp(int family, const LogitsArgs& a, hipStream_t st);
 hipError_t launch_dense(const void* x, int dtype, int M, const void* w, int64_t V, int64_t K,
                         float* y, int64_t ldy, hipStream_t st);
 hipError_t launch_topk_rescore(const void* x, int x_dtype, int M, const void* w, int w_dtype,

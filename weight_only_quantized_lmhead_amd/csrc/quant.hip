@@ -21,6 +21,15 @@
 //     codes ever reaches memory.  A launch may cover any run of whole 64-row
 //     blocks, which is what lets a caller quantize a head chunk by chunk.
 //
+// Zero-point heads (ASYM): unsigned codes n in [0, qr] (qr = 15 / 255) and a
+// per-group zero point z, w ~ (n - z) * s, in place of the symmetric module's
+// fixed offset 8.  The pages give no quantizer for that form; this one is the
+// plain min/max round-to-nearest over the group's range widened to include
+// zero (so zero is exactly representable): lo = min(0, min w), hi = max(0,
+// max w), s = round16(max(fl32(fl32(hi - lo) * fl32(1 / qr)), floor)),
+// z = clamp(rint(fl32(-lo / s)), 0, qr), n = clamp(rint(fl32(w / s)) + z, 0,
+// qr); an all-zero group gets s = z = n = 0.  No clip search.
+//
 // Quotient rounding.  q = rint(fl32(w / s)) is computed without a division
 // and without any data-dependent branch: fl32(w / s) == RN32(RN64(w * r))
 // with r = RN64(1 / s) (once per group and ratio).  Proof sketch: write the
@@ -63,6 +72,7 @@ struct QCfg {
 };
 
 struct QuantArgs {
+    int asym;            // zero-point form (informational; the kernels take ASYM)
     const void* w;       // row `row0` of the head
     int64_t ldw;         // row stride of w in elements
     int64_t row0, rows;  // rows present in w: [row0, row0 + rows)
@@ -73,14 +83,17 @@ struct QuantArgs {
     QCfg cf;
     uint8_t* wout;   // packed mode: weight region of the blob
     uint16_t* sout;  //              scale region of the blob
-    int8_t* q;       // codes mode: q [V, K]
+    uint8_t* zout;   //              zero-point region of the blob (ASYM)
+    int8_t* q;       // codes mode: q [V, K] (ASYM: the unsigned codes n)
     uint16_t* s;     //             s [V, NG]
+    uint8_t* z;      //             z [V, NG] (ASYM)
 };
 
 template <int BITS>
 struct QRange {
     static constexpr float lo = BITS == 4 ? -8.0f : -128.0f;
     static constexpr float hi = BITS == 4 ? 7.0f : 127.0f;
+    static constexpr float qr = BITS == 4 ? 15.0f : 255.0f;  // unsigned code range (ASYM)
 };
 
 // Eight consecutive weights of one row, widened exactly to fp32.
@@ -143,6 +156,18 @@ __device__ __forceinline__ void codes(const float* w, double r, float* q) {
     for (int i = 0; i < N; ++i) {
         const float x = (float)((double)w[i] * r);
         q[i] = __builtin_amdgcn_fmed3f(rintf(x), QRange<BITS>::lo, QRange<BITS>::hi);
+    }
+}
+
+// Zero-point codes: n = clamp(rint(fl32(w / s)) + z, 0, qr), the sum of two
+// small integers exact.
+template <int BITS, int N>
+__device__ __forceinline__ void codes_asym(const float* w, double r, float zf, float* n) {
+#pragma clang fp contract(off)
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const float x = (float)((double)w[i] * r);
+        n[i] = __builtin_amdgcn_fmed3f(rintf(x) + zf, 0.0f, QRange<BITS>::qr);
     }
 }
 
@@ -276,6 +301,31 @@ __device__ __forceinline__ float pick_scale(const Get& get, int G, const QCfg& c
     return best;
 }
 
+// Scale and zero point of a zero-point group (the header's ASYM rules):
+// returns s, sets zf = z and zero = the group is all zeros.
+template <int BITS, bool UNROLL, class Get>
+__device__ __forceinline__ float pick_asym(const Get& get, int G, const QCfg& cf, bool& zero,
+                                           float& zf) {
+#pragma clang fp contract(off)
+    constexpr int kU = UNROLL ? 16 : 1;
+    float lo = 0.0f, hi = 0.0f;
+#pragma unroll kU
+    for (int k = 0; k < G; k += 32) {
+        float w[32];
+        get.template operator()<32>(k, w);
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            lo = fminf(lo, w[i]);
+            hi = fmaxf(hi, w[i]);
+        }
+    }
+    zero = hi == lo;
+    const float sv = ratio_scale(hi - lo, cf.c[0], cf);
+    const double rr = 1.0 / (double)sv;
+    zf = __builtin_amdgcn_fmed3f(rintf((float)((double)(-lo) * rr)), 0.0f, QRange<BITS>::qr);
+    return sv;
+}
+
 __device__ __forceinline__ uint16_t scale_bits(float sv, bool zero, int sbf16) {
     if (zero) return 0;
     return sbf16 ? f32_to_bf16_rne(sv) : f32_to_f16_rne(sv);
@@ -285,8 +335,10 @@ __device__ __forceinline__ uint16_t scale_bits(float sv, bool zero, int sbf16) {
 // clamped) into slot words sw[t][j]: int4 chunk jj fills word j = jj of the
 // four slots (nibble q + 8; even columns in the low half-word, odd columns in
 // the high one); int8 chunk jj fills words 2jj and 2jj + 1 (byte q + 128).
-template <int BITS>
+// ASYM codes are stored as they are (nibble n, byte n).
+template <int BITS, bool ASYM>
 __device__ __forceinline__ void put_chunk(const float* q, int jj, uint32_t (&sw)[4][4]) {
+    constexpr float off = ASYM ? 0.0f : (BITS == 4 ? 8.0f : 128.0f);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const float* q8 = q + 8 * t;
@@ -294,8 +346,8 @@ __device__ __forceinline__ void put_chunk(const float* q, int jj, uint32_t (&sw)
             uint32_t lo = 0, hi = 0;
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
-                lo |= (uint32_t)(int)(q8[2 * p] + 8.0f) << (4 * p);
-                hi |= (uint32_t)(int)(q8[2 * p + 1] + 8.0f) << (4 * p);
+                lo |= (uint32_t)(int)(q8[2 * p] + off) << (4 * p);
+                hi |= (uint32_t)(int)(q8[2 * p + 1] + off) << (4 * p);
             }
             sw[t][jj] = lo | (hi << 16);
         } else {
@@ -303,7 +355,7 @@ __device__ __forceinline__ void put_chunk(const float* q, int jj, uint32_t (&sw)
             for (int e = 0; e < 2; ++e) {
                 uint32_t wd = 0;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) wd |= (uint32_t)(int)(q8[4 * e + i] + 128.0f) << (8 * i);
+                for (int i = 0; i < 4; ++i) wd |= (uint32_t)(int)(q8[4 * e + i] + off) << (8 * i);
                 sw[t][2 * jj + e] = wd;
             }
         }
@@ -343,7 +395,13 @@ __device__ __forceinline__ RowSrc<WDT> lane_row(const QuantArgs& a, int64_t v) {
 
 // Groups of GT <= 128 columns, held in registers.  Unit: one superchunk (or
 // one group when GT exceeds the span) in packed mode, one group in codes mode.
-template <int WDT, int BITS, int GT, bool PACKED>
+// Byte offset of the zero point of row r (of a 64-row block) in group g of
+// block b, within the blob's zero-point region.
+__device__ __forceinline__ int64_t zp_offset(int64_t b, int NG, int g, int r) {
+    return (b * NG + g) * 64 + 4 * (r & 15) + (r >> 4);
+}
+
+template <int WDT, int BITS, int GT, bool PACKED, bool ASYM>
 __global__ __launch_bounds__(256, 2) void
 quant_held_kernel(
     const QuantArgs a) {
@@ -366,28 +424,34 @@ quant_held_kernel(
         Held<WDT, GT> h;
         h.load(src, col0);
         bool zero;
-        const float sv = pick_scale<BITS, true>(HeldGet<WDT, GT>{h}, GT, a.cf, zero);
+        float zf = 0.0f;
+        const float sv = ASYM ? pick_asym<BITS, true>(HeldGet<WDT, GT>{h}, GT, a.cf, zero, zf)
+                              : pick_scale<BITS, true>(HeldGet<WDT, GT>{h}, GT, a.cf, zero);
         const uint16_t sb = scale_bits(sv, zero, a.cf.sbf16);
         const double rr = 1.0 / (double)sv;
         if constexpr (PACKED) {
             a.sout[(b * a.NG + col0 / GT) * 64 + r] = sb;
+            if constexpr (ASYM) a.zout[zp_offset(b, a.NG, col0 / GT, r)] = (uint8_t)(int)zf;
 #pragma unroll
             for (int ch = 0; ch < GT / 32; ++ch) {
                 float w[32], q[32];
                 h.template get<32>(32 * ch, w);
-                codes<BITS, 32>(w, rr, q);
+                if constexpr (ASYM) codes_asym<BITS, 32>(w, rr, zf, q);
+                else codes<BITS, 32>(w, rr, q);
                 const int cu = gi * (GT / 32) + ch;  // chunk index within the unit
-                put_chunk<BITS>(q, cu % CPS, sw);
+                put_chunk<BITS, ASYM>(q, cu % CPS, sw);
                 if (cu % CPS == CPS - 1) store_slots(a.wout, b, a.NC, (col_u + 32 * cu) / span, r, sw);
                 __builtin_amdgcn_sched_barrier(0);
             }
         } else if (src.valid) {
             a.s[v * a.NG + col0 / GT] = sb;
+            if constexpr (ASYM) a.z[v * a.NG + col0 / GT] = (uint8_t)(int)zf;
 #pragma unroll
             for (int ch = 0; ch < GT / 32; ++ch) {
                 float w[32], q[32];
                 h.template get<32>(32 * ch, w);
-                codes<BITS, 32>(w, rr, q);
+                if constexpr (ASYM) codes_asym<BITS, 32>(w, rr, zf, q);
+                else codes<BITS, 32>(w, rr, q);
                 store_codes32(a.q + v * a.K + col0 + 32 * ch, q);
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -396,7 +460,7 @@ quant_held_kernel(
 }
 
 // Longer groups, streamed once per pass.  Unit: one group.
-template <int WDT, int BITS, bool PACKED>
+template <int WDT, int BITS, bool PACKED, bool ASYM>
 __global__ __launch_bounds__(256, 2) void quant_stream_kernel(const QuantArgs a) {
 #pragma clang fp contract(off)
     const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -408,12 +472,15 @@ __global__ __launch_bounds__(256, 2) void quant_stream_kernel(const QuantArgs a)
     const RowSrc<WDT> src = lane_row<WDT>(a, v);
     const int col0 = g * a.G;
     bool zero;
-    const float sv = pick_scale<BITS, false>(StreamGet<WDT>{src, col0}, a.G, a.cf, zero);
+    float zf = 0.0f;
+    const float sv = ASYM ? pick_asym<BITS, false>(StreamGet<WDT>{src, col0}, a.G, a.cf, zero, zf)
+                          : pick_scale<BITS, false>(StreamGet<WDT>{src, col0}, a.G, a.cf, zero);
     const uint16_t sb = scale_bits(sv, zero, a.cf.sbf16);
     const double rr = 1.0 / (double)sv;
     if constexpr (PACKED) {
         constexpr int span = span_of(BITS);
         a.sout[(b * a.NG + g) * 64 + r] = sb;
+        if constexpr (ASYM) a.zout[zp_offset(b, a.NG, g, r)] = (uint8_t)(int)zf;
 #pragma unroll 1
         for (int c = col0 / span; c < (col0 + a.G) / span; ++c) {
             uint32_t sw[4][4];
@@ -421,37 +488,41 @@ __global__ __launch_bounds__(256, 2) void quant_stream_kernel(const QuantArgs a)
             for (int ch = 0; ch < span / 32; ++ch) {
                 float w[32], q[32];
                 get_stream<WDT, 32>(src, c * span + 32 * ch, w);
-                codes<BITS, 32>(w, rr, q);
-                put_chunk<BITS>(q, ch, sw);
+                if constexpr (ASYM) codes_asym<BITS, 32>(w, rr, zf, q);
+                else codes<BITS, 32>(w, rr, q);
+                put_chunk<BITS, ASYM>(q, ch, sw);
             }
             store_slots(a.wout, b, a.NC, c, r, sw);
         }
     } else if (src.valid) {
         a.s[v * a.NG + g] = sb;
+        if constexpr (ASYM) a.z[v * a.NG + g] = (uint8_t)(int)zf;
 #pragma unroll 1
         for (int col = col0; col < col0 + a.G; col += 32) {
             float w[32], q[32];
             get_stream<WDT, 32>(src, col, w);
-            codes<BITS, 32>(w, rr, q);
+            if constexpr (ASYM) codes_asym<BITS, 32>(w, rr, zf, q);
+            else codes<BITS, 32>(w, rr, q);
             store_codes32(a.q + v * a.K + col, q);
         }
     }
 }
 
-template <int WDT, int BITS, bool PACKED>
+template <int WDT, int BITS, bool PACKED, bool ASYM>
 void launch_q3(const QuantArgs& a, dim3 grid, hipStream_t st) {
     switch (a.G) {
     case 32:
-        hipLaunchKernelGGL((quant_held_kernel<WDT, BITS, 32, PACKED>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((quant_held_kernel<WDT, BITS, 32, PACKED, ASYM>), grid, dim3(256), 0, st, a);
         break;
     case 64:
-        hipLaunchKernelGGL((quant_held_kernel<WDT, BITS, 64, PACKED>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((quant_held_kernel<WDT, BITS, 64, PACKED, ASYM>), grid, dim3(256), 0, st, a);
         break;
     case 128:
-        hipLaunchKernelGGL((quant_held_kernel<WDT, BITS, 128, PACKED>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((quant_held_kernel<WDT, BITS, 128, PACKED, ASYM>), grid, dim3(256), 0, st,
+                           a);
         break;
     default:
-        hipLaunchKernelGGL((quant_stream_kernel<WDT, BITS, PACKED>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((quant_stream_kernel<WDT, BITS, PACKED, ASYM>), grid, dim3(256), 0, st, a);
         break;
     }
 }
@@ -460,9 +531,14 @@ template <bool PACKED>
 hipError_t launch_q(const QuantArgs& a, int w_dtype, int bits, hipStream_t st) {
     if (a.nunits <= 0) return hipSuccess;
     const dim3 grid((unsigned)((a.nunits + 3) / 4));
-#define LMH_Q_CASE(WDT)                                                \
-    if (bits == 4) launch_q3<WDT, 4, PACKED>(a, grid, st);             \
-    else launch_q3<WDT, 8, PACKED>(a, grid, st);
+#define LMH_Q_CASE(WDT)                                                                 \
+    if (a.asym) {                                                                       \
+        if (bits == 4) launch_q3<WDT, 4, PACKED, true>(a, grid, st);                    \
+        else launch_q3<WDT, 8, PACKED, true>(a, grid, st);                              \
+    } else {                                                                            \
+        if (bits == 4) launch_q3<WDT, 4, PACKED, false>(a, grid, st);                   \
+        else launch_q3<WDT, 8, PACKED, false>(a, grid, st);                             \
+    }
     switch (w_dtype) {
     case F32: LMH_Q_CASE(F32) break;
     case F16: LMH_Q_CASE(F16) break;
@@ -472,9 +548,10 @@ hipError_t launch_q(const QuantArgs& a, int w_dtype, int bits, hipStream_t st) {
     return hipGetLastError();
 }
 
-QCfg make_cfg(int bits, int scale_dtype, int nratios) {
+QCfg make_cfg(int bits, int scale_dtype, int nratios, bool asym) {
     static const double kRatios[5] = {1.0, 0.95, 0.9, 0.85, 0.8};
-    const int qmax = bits == 4 ? 7 : 127;
+    // symmetric: c_i = fl32(ratio_i / qmax); zero-point: c_0 = fl32(1 / qr)
+    const int qmax = asym ? (bits == 4 ? 15 : 255) : (bits == 4 ? 7 : 127);
     QCfg cf;
     for (int i = 0; i < 5; ++i) cf.c[i] = (float)(kRatios[i] / (double)qmax);
     cf.sbf16 = scale_dtype == BF16;
@@ -483,8 +560,10 @@ QCfg make_cfg(int bits, int scale_dtype, int nratios) {
     return cf;
 }
 
-// One thread per 16-byte weight slot of the blob.
-template <int BITS>
+// One thread per 16-byte weight slot of the blob.  ZP: the codes are the
+// unsigned n (stored as they are; padding rows 0), else the signed q (stored
+// biased by 8 / 128; padding rows q = 0).
+template <int BITS, bool ZP>
 __global__ __launch_bounds__(256) void pack_weights_kernel(const int8_t* __restrict__ q, int64_t V,
                                                            int64_t K, int64_t nslots, int NC,
                                                            uint4* __restrict__ out) {
@@ -498,7 +577,7 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const int8_t* __restr
     const int64_t v = b * 64 + r;
     uint32_t word[4];
     if (v >= V) {
-        const uint32_t pad = BITS == 4 ? 0x88888888u : 0x80808080u;
+        const uint32_t pad = ZP ? 0u : (BITS == 4 ? 0x88888888u : 0x80808080u);
         for (int j = 0; j < 4; ++j) word[j] = pad;
     } else if constexpr (BITS == 4) {
         for (int j = 0; j < 4; ++j) {
@@ -508,7 +587,7 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const int8_t* __restr
                 // column i8 goes to nibble position p: even columns 0,2,4,6 -> p 0..3,
                 // odd columns 1,3,5,7 -> p 4..7
                 const int p = (i8 & 1) ? 4 + (i8 >> 1) : (i8 >> 1);
-                wd |= (uint32_t)((src[i8] + 8) & 0xF) << (4 * p);
+                wd |= (uint32_t)((src[i8] + (ZP ? 0 : 8)) & 0xF) << (4 * p);
             }
             word[j] = wd;
         }
@@ -516,7 +595,8 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const int8_t* __restr
         for (int j = 0; j < 4; ++j) {
             const int8_t* src = q + v * K + (int64_t)c * 64 + 32 * (j >> 1) + 8 * t + 4 * (j & 1);
             uint32_t wd = 0;
-            for (int i4 = 0; i4 < 4; ++i4) wd |= (uint32_t)(uint8_t)(src[i4] + 128) << (8 * i4);
+            for (int i4 = 0; i4 < 4; ++i4)
+                wd |= (uint32_t)(uint8_t)(src[i4] + (ZP ? 0 : 128)) << (8 * i4);
             word[j] = wd;
         }
     }
@@ -536,13 +616,32 @@ __global__ __launch_bounds__(256) void pack_scales_kernel(const uint16_t* __rest
     out[e] = v < V ? s[v * NG + g] : (uint16_t)0;
 }
 
+// One thread per byte of the zero-point region: byte e holds, for block b and
+// group g ((b*NG + g) = e / 64), row r = (e%64)/4 + 16 ((e%64) % 4).
+__global__ __launch_bounds__(256) void pack_zeros_kernel(const uint8_t* __restrict__ z, int64_t V,
+                                                         int NG, int64_t n,
+                                                         uint8_t* __restrict__ out) {
+    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= n) return;
+    const int pos = (int)(e & 63);
+    const int r = (pos >> 2) + 16 * (pos & 3);
+    const int64_t bg = e >> 6;
+    const int g = (int)(bg % NG);
+    const int64_t b = bg / NG;
+    const int64_t v = b * 64 + r;
+    out[e] = v < V ? z[v * NG + g] : (uint8_t)0;
+}
+
 inline unsigned grid_for(int64_t n, int block) { return (unsigned)((n + block - 1) / block); }
 
 }  // namespace
 
 hipError_t launch_quantize(const void* w, int w_dtype, int64_t V, int64_t K, int bits, int64_t G,
-                           int scale_dtype, int nratios, int8_t* q, uint16_t* s, hipStream_t st) {
+                           int scale_dtype, int nratios, int8_t* q, uint16_t* s, uint8_t* z,
+                           hipStream_t st) {
     QuantArgs a{};
+    a.asym = z != nullptr;
+    a.z = z;
     a.w = w;
     a.ldw = K;
     a.row0 = 0;
@@ -554,18 +653,19 @@ hipError_t launch_quantize(const void* w, int w_dtype, int64_t V, int64_t K, int
     a.NC = 0;
     a.upb = a.NG;  // codes mode: one unit per group
     a.nunits = (V + 63) / 64 * a.upb;
-    a.cf = make_cfg(bits, scale_dtype, nratios);
+    a.cf = make_cfg(bits, scale_dtype, nratios, a.asym);
     a.q = q;
     a.s = s;
     return launch_q<false>(a, w_dtype, bits, st);
 }
 
 hipError_t launch_quantize_pack(const void* w, int w_dtype, int64_t ldw, int64_t V, int64_t K,
-                                int bits, int64_t G, int scale_dtype, int nratios, int64_t row0,
-                                int64_t rows, uint8_t* blob, hipStream_t st) {
+                                int bits, int64_t G, int scale_dtype, int nratios, bool asym,
+                                int64_t row0, int64_t rows, uint8_t* blob, hipStream_t st) {
     const int span = span_of(bits);
     const int64_t vpad = (V + 63) / 64 * 64;
     QuantArgs a{};
+    a.asym = asym;
     a.w = w;
     a.ldw = ldw;
     a.row0 = row0;
@@ -578,30 +678,40 @@ hipError_t launch_quantize_pack(const void* w, int w_dtype, int64_t ldw, int64_t
     // unit: a superchunk, or a whole group when the group is longer
     a.upb = (int)(K / (G > span ? G : span));
     a.nunits = (rows + 63) / 64 * a.upb;
-    a.cf = make_cfg(bits, scale_dtype, nratios);
+    a.cf = make_cfg(bits, scale_dtype, nratios, asym);
     a.wout = blob;
     a.sout = (uint16_t*)(blob + vpad * K * bits / 8);
+    a.zout = asym ? blob + vpad * K * bits / 8 + vpad * a.NG * 2 : nullptr;
     return launch_q<true>(a, w_dtype, bits, st);
 }
 
-hipError_t launch_pack(const int8_t* q, const uint16_t* s, int64_t V, int64_t K, int bits,
-                       int64_t G, uint8_t* out, hipStream_t st) {
+hipError_t launch_pack(const int8_t* q, const uint16_t* s, const uint8_t* z, int64_t V, int64_t K,
+                       int bits, int64_t G, uint8_t* out, hipStream_t st) {
     const int64_t NB = (V + 63) / 64;
     const int NC = (int)(K / span_of(bits));
     const int NG = (int)(K / G);
     const int64_t nslots = NB * NC * 256;
-    if (bits == 4)
-        hipLaunchKernelGGL(pack_weights_kernel<4>, dim3(grid_for(nslots, 256)), dim3(256), 0, st, q,
-                           V, K, nslots, NC, (uint4*)out);
-    else
-        hipLaunchKernelGGL(pack_weights_kernel<8>, dim3(grid_for(nslots, 256)), dim3(256), 0, st, q,
-                           V, K, nslots, NC, (uint4*)out);
+#define LMH_PACKW(B_, Z_)                                                                        \
+    hipLaunchKernelGGL((pack_weights_kernel<B_, Z_>), dim3(grid_for(nslots, 256)), dim3(256), 0, st, \
+                       q, V, K, nslots, NC, (uint4*)out)
+    if (bits == 4) {
+        if (z) LMH_PACKW(4, true); else LMH_PACKW(4, false);
+    } else {
+        if (z) LMH_PACKW(8, true); else LMH_PACKW(8, false);
+    }
+#undef LMH_PACKW
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t nsc = NB * NG * 64;
     uint16_t* sout = (uint16_t*)(out + NB * 64 * K * bits / 8);
     hipLaunchKernelGGL(pack_scales_kernel, dim3(grid_for(nsc, 256)), dim3(256), 0, st, s, V, NG, nsc,
                        sout);
+    if (z) {
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(pack_zeros_kernel, dim3(grid_for(nsc, 256)), dim3(256), 0, st, z, V, NG,
+                           nsc, out + NB * 64 * K * bits / 8 + nsc * 2);
+    }
     return hipGetLastError();
 }
 
