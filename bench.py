@@ -66,9 +66,10 @@ def traffic_file(workload: str) -> str:
     return os.path.join(ROOT, "profiles", f"logits_{workload}_hbm_traffic.md")
 
 
-def recorded_traffic(workload: str, kernel_prefix: str):
-    """HBM bytes per launch of the kernel from the committed counter summary,
-    or None when there is none or the kernel sources changed since."""
+def recorded_traffic(workload: str, kernel_prefix: str, zp: bool = False):
+    """HBM bytes per launch of the kernel (the symmetric or the zero-point
+    instantiation) from the committed counter summary, or None when there is
+    none or the kernel sources changed since."""
     f = traffic_file(workload)
     if not os.path.exists(f):
         return None
@@ -78,7 +79,8 @@ def recorded_traffic(workload: str, kernel_prefix: str):
             if rec.get("sources_sha") != sources_sha():
                 return None
             for k in rec["kernels"]:
-                if k["kernel"].startswith(kernel_prefix):
+                name = k["kernel"].split(" grid")[0]
+                if name.startswith(kernel_prefix) and name.endswith("true>" if zp else "false>"):
                     return k
     return None
 
@@ -90,8 +92,10 @@ def _short_kernel(name: str) -> str:
     if m:
         n = int(m.group(1))
         base, rest = m.group(2)[:n], m.group(2)[n:]
-        targs = ",".join(re.findall(r"Li(\d+)E", rest))
-        return f"{base}<{targs}>"
+        targs = rest.split("EEv")[0] if "EEv" in rest else rest
+        vals = [v if t == "i" else ("true" if v == "1" else "false")
+                for t, v in re.findall(r"L([ib])(\d+)E", targs + "E")]
+        return f"{base}<{','.join(vals)}>"
     name = name.replace("void ", "").replace("lmh::(anonymous namespace)::", "")
     return name.split("(")[0][:60]
 
@@ -124,7 +128,9 @@ def summarize(args) -> int:
     out.append("")
     text = "\n".join(out) + "\n"
     if args.fetch and args.write:
-        blob = lmh.packed_bytes(w.V, w.K, w.bits, w.group)
+        # the largest copies are the clones of the zero-point head (the
+        # symmetric head's clones are smaller by one byte per row and group)
+        blob = lmh.packed_bytes(w.V, w.K, w.bits | lmh.ZP, w.group)
 
         def per_kernel(path, counter):
             # keyed by kernel and grid size (one logits kernel serves several M)
@@ -143,7 +149,7 @@ def summarize(args) -> int:
         copy_w = max(wv["__amd_rocclr_copyBuffer"])
         kf, kw = blob / 1024 / copy_f, blob / 1024 / copy_w
         t = ["## HBM traffic (rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE)\n",
-             f"Calibration: the copy kernel that clones the {blob}-byte packed head reads "
+             f"Calibration: the copy kernel that clones the {blob}-byte zero-point packed head reads "
              f"FETCH_SIZE = {copy_f:.1f} KiB and WRITE_SIZE = {copy_w:.1f} KiB per dispatch, so "
              f"bytes read = FETCH_SIZE x {kf:.5f} x 1024 and bytes written = WRITE_SIZE x {kw:.5f} x 1024.\n",
              "| kernel | dispatches | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | read (B) | written (B) | total (B) |",
