@@ -374,6 +374,11 @@ size_t lmhead_logits_topk_workspace_bytes(int64_t M, int64_t V, int64_t K, int x
  *   then live in the workspace only.  Arguments otherwise as for
  *   lmhead_logits and lmhead_topk_rescore (same shape rules, alignment,
  *   dtypes and V <= 2097152); topk 1..64, topk <= V.
+ *   One activation row (M = 1, the decode case) with topk <= 16 and at most
+ *   4096 row blocks (V <= 262144) takes a fused path: the GEMV itself writes
+ *   each 64-row block's sorted top-(topk+1) list of its fp32 logits, and one
+ *   merge kernel selects and rescores -- no second pass over the logits, and
+ *   with y NULL the logits are never stored.  The result is the same.
  *   workspace: at least lmhead_logits_topk_workspace_bytes(M, V, K, x_dtype,
  *   topk) bytes, 16-byte aligned; contents on entry do not matter.
  */

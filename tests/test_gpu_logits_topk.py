@@ -86,3 +86,52 @@ def test_full_size_rows_match_separate_calls(V):
     i1, v1, t1 = lmh.logits_topk(x, blob, V, K, bits, G, torch.float16, wref, 8)
     torch.cuda.synchronize()
     assert torch.equal(i1, i0) and torch.equal(v1, v0) and torch.equal(t1, t0)
+
+
+def _dev_head(V, K, bits, G, seed, zp=False, zero=False):
+    gen = torch.Generator(device=DEV).manual_seed(seed)
+    Wd = torch.randn(V, K, device=DEV, generator=gen) * 0.02
+    if zero:
+        Wd.zero_()
+    bb = bits | lmh.ZP if zp else bits
+    blob = lmh.quantize_pack(Wd, bb, G, torch.float16)
+    return Wd.half(), blob, bb
+
+
+@pytest.mark.parametrize("V,topk", [(5, 4), (64, 8), (65, 16), (64 * 256, 16), (64 * 256 + 1, 1),
+                                    (64 * 4096, 8), (64 * 4096 + 3, 8), (3000, 17)])
+@pytest.mark.parametrize("zp", [False, True])
+def test_decode_path_edges(V, topk, zp):
+    """M = 1 runs the GEMV with its per-block top-K lists and one merge kernel
+    (topk <= 16, at most 4096 row blocks; else the two-pass path): single and
+    ragged blocks, V below a block, the largest merged list count and one
+    block more, topk 16 and 17, with a bias and on zero-point heads.  The
+    result equals the separate logits + rescoring calls bit for bit."""
+    need_gpu()
+    K, bits, G = 256, 4, 64
+    wref, blob, bb = _dev_head(V, K, bits, G, seed=V + topk, zp=zp)
+    gen = torch.Generator(device=DEV).manual_seed(7)
+    bias = torch.randn(V, device=DEV, generator=gen)
+    x = to_dev(synth.random_x(1, K, seed=topk, dtype="f16"), "f16")
+    y0 = lmh.logits(x, blob, V, K, bb, G, torch.float16, bias=bias)
+    i0, v0, t0 = lmh.topk_rescore(x, wref, y0, topk)
+    y1 = torch.full((1, V + 5), float("nan"), device=DEV)[:, :V]
+    i1, v1, t1 = lmh.logits_topk(x, blob, V, K, bb, G, torch.float16, wref, topk, bias=bias, out=y1)
+    i2, v2, t2 = lmh.logits_topk(x, blob, V, K, bb, G, torch.float16, wref, topk, bias=bias)
+    torch.cuda.synchronize()
+    for i, v, t in ((i1, v1, t1), (i2, v2, t2)):
+        assert torch.equal(i, i0) and torch.equal(v, v0) and torch.equal(t, t0)
+    assert torch.equal(y1, y0)
+
+
+def test_decode_path_all_ties():
+    """An all-zero head: every logit is 0, so the top-K are the first K indices
+    (index ascending on ties) and the top-1 is row 0."""
+    need_gpu()
+    V, K, bits, G, topk = 64 * 37 + 9, 512, 4, 128, 16
+    wref, blob, bb = _dev_head(V, K, bits, G, seed=1, zero=True)
+    x = to_dev(synth.random_x(1, K, seed=2, dtype="bf16"), "bf16")
+    idx, val, top1 = lmh.logits_topk(x, blob, V, K, bb, G, torch.float16, wref, topk)
+    torch.cuda.synchronize()
+    assert idx.cpu().numpy()[0].tolist() == list(range(topk))
+    assert (val == 0).all() and int(top1[0]) == 0

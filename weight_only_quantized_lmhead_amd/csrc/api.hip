@@ -172,10 +172,12 @@ size_t lmhead_logits_workspace_bytes(int64_t M, int64_t K, int x_dtype) {
     return (size_t)(((M * K * 2 + 255) / 256) * 256 + ((M * 4 + 255) / 256) * 256);
 }
 
+// `lists` (internal, lmhead_logits_topk's fused path): the GEMV also writes
+// per-block top-`list_T` lists there, and y may be null.
 static int logits_impl(const void* x, int x_dtype, int64_t M, const void* packed, int64_t V,
                        int64_t K, int bits_arg, int64_t group, int scale_dtype, const float* bias,
                        void* y, int y_dtype, int64_t ldy, void* workspace, size_t ws_bytes,
-                       void* stream, int path) {
+                       void* stream, int path, lmh::u64* lists = nullptr, int list_T = 0) {
     const Width wd = width_of(bits_arg);
     const int bits = wd.bits;
     int rc = check_layout(V, K, bits, group);
@@ -185,8 +187,8 @@ static int logits_impl(const void* x, int x_dtype, int64_t M, const void* packed
     if (M < 0 || M > 65535) return LMH_E_SHAPE;
     if (path < 0 || path > 4) return LMH_E_UNSUPPORTED;
     if (M == 0 || V == 0) return LMH_OK;
-    if (ldy < V) return LMH_E_SHAPE;
-    if (!x || !packed || !y) return LMH_E_NULL;
+    if (y && ldy < V) return LMH_E_SHAPE;
+    if (!x || !packed || (!y && !lists)) return LMH_E_NULL;
     if (!aligned16(x) || !aligned16(packed)) return LMH_E_ALIGN;
     if (y_dtype != F32 && y_dtype != F16 && y_dtype != BF16) return LMH_E_DTYPE;
     if (((uintptr_t)y & (y_dtype == F32 ? 3u : 1u)) != 0) return LMH_E_ALIGN;
@@ -226,6 +228,8 @@ static int logits_impl(const void* x, int x_dtype, int64_t M, const void* packed
     a.bits = bits;
     a.scale_bf16 = scale_dtype == BF16;
     a.zp = wd.zp;
+    a.lists = lists;
+    a.list_T = list_T;
     const bool use_gemv = path == 1 || (path == 0 && gemv_ok && M <= lmh::kGemvAutoMaxM);
     if (use_gemv) return from_hip(lmh::launch_gemv(a, st));
     // automatic, from measurements on the 151936 x 1024 heads: the register-fed
@@ -306,13 +310,20 @@ int lmhead_topk_rescore(const void* x, int x_dtype, int64_t M, const void* w_ref
 
 static int64_t round256(int64_t n) { return (n + 255) / 256 * 256; }
 
-// Workspace of lmhead_logits_topk: [x conversion][top-K lists][fp32 logits
-// scratch, used when y is NULL]; every region rounded up to 256 bytes.
+// Workspace of lmhead_logits_topk: [x conversion][top-K lists (pass-1 lists,
+// or the fused GEMV's per-block lists, whichever is larger)][fp32 logits
+// scratch, used when y is NULL on the unfused path]; every region rounded up
+// to 256 bytes.
+static int64_t topk_lists_region(int64_t M, int64_t V, int topk) {
+    return std::max(round256((int64_t)lmh::topk_ws_bytes(M, V, topk)),
+                    round256((int64_t)lmh::topk_fused_lists_bytes(M, V, topk)));
+}
+
 size_t lmhead_logits_topk_workspace_bytes(int64_t M, int64_t V, int64_t K, int x_dtype, int topk) {
     if (M <= 0 || V <= 0 || K <= 0 || topk < 1 || topk > 64) return 0;
     if (x_dtype != F16 && x_dtype != BF16) return 0;
     return (size_t)(round256((int64_t)lmhead_logits_workspace_bytes(M, K, x_dtype)) +
-                    round256((int64_t)lmh::topk_ws_bytes(M, V, topk)) + round256(M * V * 4));
+                    topk_lists_region(M, V, topk) + round256(M * V * 4));
 }
 
 int lmhead_logits_topk(const void* x, int x_dtype, int64_t M, const void* packed, int64_t V,
@@ -342,7 +353,21 @@ int lmhead_logits_topk(const void* x, int x_dtype, int64_t M, const void* packed
     if (!aligned16(workspace)) return LMH_E_ALIGN;
     char* ws = (char*)workspace;
     const int64_t xws = round256((int64_t)lmhead_logits_workspace_bytes(M, K, x_dtype));
-    const int64_t tws = round256((int64_t)lmh::topk_ws_bytes(M, V, topk));
+    const int64_t tws = topk_lists_region(M, V, topk);
+    // one activation row through the GEMV: its epilogue writes each 64-row
+    // block's sorted top-T list, and one merge kernel selects and rescores
+    // (no separate pass over the logits; y is stored only when given)
+    const bool gemv_auto = M <= lmh::kGemvAutoMaxM && M <= lmh::kGemvMaxM && M * K <= lmh::kGemvMaxMK;
+    if (gemv_auto && lmh::topk_fused_ok(V, topk)) {
+        const int T = (int)(topk + 1 <= V ? topk + 1 : V);
+        lmh::u64* lists = (lmh::u64*)(ws + xws);
+        rc = logits_impl(x, x_dtype, M, packed, V, K, bits, group, scale_dtype, bias, y, F32, ldy,
+                         ws, (size_t)xws, stream, 1, lists, T);
+        if (rc != LMH_OK) return rc;
+        return from_hip(lmh::launch_topk_merge_rescore(lists, x, x_dtype, (int)M, w_ref, w_dtype, V,
+                                                       K, y, ldy, topk, T, idx_out, val_out,
+                                                       top1_out, (hipStream_t)stream));
+    }
     float* yy = y ? y : (float*)(ws + xws + tws);
     const int64_t ly = y ? ldy : V;
     // the logits (automatic kernel), then the two top-K passes over them

@@ -68,6 +68,8 @@ struct LogitsArgs {
     int64_t V, K, G;
     int M, bits, scale_bf16;
     int zp;                // zero-point head: a zero-point region follows the scales
+    u64* lists;            // GEMV top-K epilogue (M = 1, fp32 y): per-block sorted lists, or nullptr
+    int list_T;            //   entries per list
 };
 
 hipError_t launch_x_to_f16(const uint16_t* x_bf16, int M, int K, _Float16* xh, int* xexp,
@@ -89,6 +91,14 @@ hipError_t launch_topk_rescore(const void* x, int x_dtype, int M, const void* w,
                                int32_t* idx, float* val, int32_t* top1, void* ws,
                                hipStream_t st);
 size_t topk_ws_bytes(int64_t M, int64_t V, int topk);
+// Fused top-K (GEMV epilogue lists + merge): whether it serves (V, topk), the
+// bytes of its lists, and the merge + rescoring launch.
+bool topk_fused_ok(int64_t V, int topk);
+size_t topk_fused_lists_bytes(int64_t M, int64_t V, int topk);
+hipError_t launch_topk_merge_rescore(const u64* lists, const void* x, int x_dtype, int M,
+                                     const void* w, int w_dtype, int64_t V, int64_t K, float* y,
+                                     int64_t ldy, int topk, int T, int32_t* idx, float* val,
+                                     int32_t* top1, hipStream_t st);
 int64_t topk_max_v();  // largest row length lmhead_topk_rescore supports
 
 // Largest M the lane-per-row GEMV accepts when forced (it runs by default only

@@ -162,7 +162,15 @@ __device__ __forceinline__ void store4(YT<OUT>* p, f4 v) {
 // superchunk (G <= span); GPS == 1 covers G >= span, the scale of superchunk c
 // then being that of group c / SPG.  With ZP the lane also reads its row's
 // zero point of each group (one byte, beside the scale).
-template <int BITS, int MM, int GPS, int D, int KS, int OUT, bool ZP>
+//
+// TK (top-K epilogue, fp32 logits): the wave that holds a block's final 64
+// logits of activation row m also writes that block's T largest as a sorted
+// list of order codes (value descending, then index ascending; see
+// topk_code) to lists[(m*NB + blk)*T ...]: each lane ranks its own code
+// against the 64 codes of the wave (read lane by lane into scalar
+// registers), and the lanes of rank < T store.  Rows past V take codes below
+// every real entry.  y may then be null (logits not stored).
+template <int BITS, int MM, int GPS, int D, int KS, int OUT, bool ZP, bool TK>
 __global__ __launch_bounds__(256) void gemv_kernel(const uint4* __restrict__ wq,
                                                    const uint16_t* __restrict__ sc,
                                                    const uint8_t* __restrict__ zq,
@@ -170,7 +178,8 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint4* __restrict__ wq,
                                                    const int* __restrict__ xexp,
                                                    const float* __restrict__ bias,
                                                    void* __restrict__ y, int64_t ldy, int V, int K,
-                                                   int NB, int NC, int NG, int SPG, int sbf16) {
+                                                   int NB, int NC, int NG, int SPG, int sbf16,
+                                                   u64* __restrict__ lists, int T) {
     constexpr int SPAN = BITS == 4 ? 128 : 64;
     constexpr int CPS = SPAN / 32;    // 32-column chunks per superchunk
     constexpr int CPG = CPS / GPS;    // chunks per group
@@ -304,13 +313,37 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint4* __restrict__ wq,
         }
     }
     const int v = blk * 64 + lane;
-    if (live && v < V) {
-        const float b = bias ? bias[v] : 0.0f;
+    if constexpr (!TK) {
+        if (live && v < V) {
+            const float b = bias ? bias[v] : 0.0f;
+#pragma unroll
+            for (int m = 0; m < MM; ++m) {
+                float r = acc[m];
+                if (xexp) r = ldexpf(r, xexp[m]);
+                ((YT<OUT>*)y)[(int64_t)m * ldy + v] = to_out<OUT>(r + b);
+            }
+        }
+    } else {
+        static_assert(OUT == F32, "the top-K epilogue ranks fp32 logits");
+        if (!live) return;  // wave-uniform: every lane of the wave takes part below
+        const float b = (bias && v < V) ? bias[v] : 0.0f;
 #pragma unroll
         for (int m = 0; m < MM; ++m) {
             float r = acc[m];
             if (xexp) r = ldexpf(r, xexp[m]);
-            ((YT<OUT>*)y)[(int64_t)m * ldy + v] = to_out<OUT>(r + b);
+            r = r + b;
+            if (y && v < V) ((float*)y)[(int64_t)m * ldy + v] = r;
+            const u64 c = v < V ? topk_code(r, v) : (u64)(64 - lane);
+            const uint32_t chi = (uint32_t)(c >> 32), clo = (uint32_t)c;
+            int rank = 0;
+#pragma unroll
+            for (int j = 0; j < 64; ++j) {
+                const u64 cj = ((u64)(uint32_t)__builtin_amdgcn_readlane((int)chi, j) << 32) |
+                               (uint32_t)__builtin_amdgcn_readlane((int)clo, j);
+                rank += cj > c;
+            }
+            u64* o = lists + ((int64_t)m * NB + blk) * T;
+            if (rank < T) o[rank] = c;
         }
     }
 }
@@ -1075,11 +1108,23 @@ hipError_t gemv_dispatch_gps(const LogitsArgs& a, int gps, hipStream_t st) {
     // and the split falls on group boundaries
     auto splits = [&](int ks) { return NC % (2 * ks) == 0 && (NC / ks) % SPG == 0; };
     const int KS = splits(4) ? 4 : splits(2) ? 2 : 1;
-#define LMH_GEMV(G_, KS_)                                                                          \
-    hipLaunchKernelGGL((gemv_kernel<BITS, MM, G_, D, KS_, OUT, ZP>), dim3((NB * KS_ + 3) / 4),    \
+    // the top-K epilogue: fp32 logits, one activation row (its only user)
+    constexpr bool kTK = OUT == F32 && MM == 1;
+    const bool tk = kTK && a.lists != nullptr;
+#define LMH_GEMV_TK(G_, KS_, TK_)                                                                  \
+    hipLaunchKernelGGL((gemv_kernel<BITS, MM, G_, D, KS_, OUT, ZP, TK_>), dim3((NB * KS_ + 3) / 4), \
                        dim3(256), lds, st, rg.wq, rg.sc, rg.zq, (const h2*)a.x, a.xexp, a.bias,    \
-                       a.y, a.ldy, (int)a.V,                                                      \
-                       (int)a.K, NB, NC, NG, SPG, a.scale_bf16)
+                       a.y, a.ldy, (int)a.V, (int)a.K, NB, NC, NG, SPG, a.scale_bf16, a.lists,    \
+                       a.list_T)
+#define LMH_GEMV(G_, KS_)                                                                          \
+    do {                                                                                           \
+        if constexpr (kTK) {                                                                       \
+            if (tk) LMH_GEMV_TK(G_, KS_, true);                                                    \
+            else LMH_GEMV_TK(G_, KS_, false);                                                      \
+        } else {                                                                                   \
+            LMH_GEMV_TK(G_, KS_, false);                                                           \
+        }                                                                                          \
+    } while (0)
 #define LMH_GEMV_KS(G_) \
     if (KS == 4) LMH_GEMV(G_, 4); else if (KS == 2) LMH_GEMV(G_, 2); else LMH_GEMV(G_, 1)
     if (gps == 1) { LMH_GEMV_KS(1); }
@@ -1088,6 +1133,7 @@ hipError_t gemv_dispatch_gps(const LogitsArgs& a, int gps, hipStream_t st) {
     else { LMH_GEMV_KS(4); }
 #undef LMH_GEMV_KS
 #undef LMH_GEMV
+#undef LMH_GEMV_TK
     return hipGetLastError();
 }
 

@@ -34,6 +34,15 @@
 //   that reach it are ranked as in pass 1.  Then the exact fp32 dot products
 //   of the selected rows (all rows at once), the scatter into y, idx/val and
 //   the top-1.
+//
+// Fused form (one activation row, topk <= 16): the GEMV itself writes one
+// sorted list of T codes per 64-row block, so pass 1 (and its read of y)
+// disappears; the merge takes up to 4096 lists (16 per thread): each wave's
+// T-th largest thread maximum bounds the row's T-th largest from below (that
+// wave alone has T entries at or above it), the largest of the four is the
+// first threshold, the lists whose heads reach it (at most 4T threads' worth)
+// give the second threshold (their T-th largest head: exactly T lists reach
+// it), and the entries at or above it of those T lists are ranked as above.
 #include "lmh_internal.h"
 
 #include <math.h>
@@ -346,7 +355,131 @@ __global__ __launch_bounds__(256) void topk_select_rescore_kernel(
                top1_out);
 }
 
+constexpr int kMergeMaxT = 17;     // topk <= 16, plus the top-1 candidate
+constexpr int kMergeLPT = 16;      // lists per thread: up to 4096 lists (64-row blocks) per row
+constexpr int kMergeMaxQual = 4 * kMergeMaxT * kMergeLPT;
+
+struct MergeShared {
+    SelectShared s;
+    u64 wthr[4];
+    u64 thr2;
+    u64 qh[kMergeMaxQual];  // heads of the lists that reach the first threshold
+    int ql[kMergeMaxQual];  // and their list numbers
+};
+
+// The top T of C <= 4096 sorted lists of T codes into sh.s.sel, sorted (see
+// the header).  Thread i owns lists i, i + 256, ...  Ends with a barrier.
+__device__ __forceinline__ void merge_lists(const u64* __restrict__ L, int C, int T,
+                                            MergeShared& sh) {
+    const int tid = threadIdx.x, wv = tid >> 6;
+    u64 hd[kMergeLPT];
+    u64 tmax = 0;
+#pragma unroll
+    for (int i = 0; i < kMergeLPT; ++i) {
+        const int l = tid + 256 * i;
+        hd[i] = l < C ? L[(int64_t)l * T] : 0;
+        tmax = hd[i] > tmax ? hd[i] : tmax;
+    }
+    sh.s.heads[tid] = tmax;
+    if (tid < 4) sh.wthr[tid] = 0;
+    if (tid == 0) {
+        sh.s.nq = sh.s.cnt = 0;
+        sh.thr2 = 0;
+    }
+    lds_barrier();
+    // first threshold: the largest of the waves' T-th largest thread maxima
+    // (0 when no wave has T lists: then every list takes part)
+    if (tmax != 0) {
+        int r = 0;
+#pragma unroll 16
+        for (int j = 0; j < 64; ++j) r += sh.s.heads[wv * 64 + j] > tmax;
+        if (r == T - 1) sh.wthr[wv] = tmax;
+    }
+    lds_barrier();
+    u64 thr1 = sh.wthr[0];
+#pragma unroll
+    for (int k = 1; k < 4; ++k) thr1 = sh.wthr[k] > thr1 ? sh.wthr[k] : thr1;
+    if (tmax != 0 && tmax >= thr1) {
+#pragma unroll
+        for (int i = 0; i < kMergeLPT; ++i) {
+            if (hd[i] != 0 && hd[i] >= thr1) {
+                const int q = atomicAdd(&sh.s.nq, 1);
+                sh.qh[q] = hd[i];
+                sh.ql[q] = tid + 256 * i;
+            }
+        }
+    }
+    lds_barrier();
+    const int nq = sh.s.nq;  // <= 4T threads x 16 lists
+    // second threshold: the T-th largest qualifying head (0 when fewer than T)
+    for (int q = tid; q < nq; q += 256) {
+        const u64 me = sh.qh[q];
+        int r = 0;
+        for (int j = 0; j < nq; ++j) r += sh.qh[j] > me;
+        if (r == T - 1) sh.thr2 = me;
+    }
+    lds_barrier();
+    const u64 thr2 = sh.thr2;
+    // the entries at or above it of the (at most T) lists whose heads reach it
+    for (int e = tid; e < nq * T; e += 256) {
+        const int q = e / T;
+        if (sh.qh[q] >= thr2) {
+            const u64 c = L[(int64_t)sh.ql[q] * T + (e - q * T)];
+            if (c != 0 && c >= thr2) sh.s.cs[atomicAdd(&sh.s.cnt, 1)] = c;
+        }
+    }
+    lds_barrier();
+    const int S = sh.s.cnt;  // T <= S <= T*T
+    for (int k = tid; k < S; k += 256) {
+        const u64 me = sh.s.cs[k];
+        int r = 0;
+#pragma unroll 8
+        for (int j = 0; j < S; ++j) r += sh.s.cs[j] > me;
+        if (r < T) sh.s.sel[r] = me;
+    }
+    lds_barrier();
+}
+
+// Merge of the GEMV's per-block lists, then rescoring as in pass 2.
+__global__ __launch_bounds__(256) void topk_merge_rescore_kernel(
+    const u64* __restrict__ lists, int C, int T, int topk, const void* __restrict__ x, int x_dtype,
+    const void* __restrict__ w, int w_dtype, int64_t V, int64_t K, int vec, float* __restrict__ y,
+    int64_t ldy, int32_t* __restrict__ idx_out, float* __restrict__ val_out,
+    int32_t* __restrict__ top1_out) {
+    __shared__ MergeShared sh;
+    const int64_t m = blockIdx.x;
+    merge_lists(lists + m * (int64_t)C * T, C, T, sh);
+    finish_row(sh.s, T, topk, m, V, x, x_dtype, w, w_dtype, K, vec, y, ldy, idx_out, val_out,
+               top1_out);
+}
+
+inline int rescore_vec(const void* x, const void* w, int w_dtype, int64_t K) {
+    const int esz = w_dtype == F32 ? 4 : 2;
+    return K % 8 == 0 && ((uintptr_t)x & 15u) == 0 && ((uintptr_t)w & 15u) == 0 &&
+           (K * esz) % 16 == 0;
+}
+
 }  // namespace
+
+bool topk_fused_ok(int64_t V, int topk) {
+    return topk + 1 <= kMergeMaxT && (V + 63) / 64 <= 256 * kMergeLPT;
+}
+
+size_t topk_fused_lists_bytes(int64_t M, int64_t V, int topk) {
+    const int64_t T = topk + 1 <= V ? topk + 1 : V;
+    return (size_t)(M * ((V + 63) / 64) * T * 8);
+}
+
+hipError_t launch_topk_merge_rescore(const u64* lists, const void* x, int x_dtype, int M,
+                                     const void* w, int w_dtype, int64_t V, int64_t K, float* y,
+                                     int64_t ldy, int topk, int T, int32_t* idx, float* val,
+                                     int32_t* top1, hipStream_t st) {
+    const int C = (int)((V + 63) / 64);
+    hipLaunchKernelGGL(topk_merge_rescore_kernel, dim3(M), dim3(256), 0, st, lists, C, T, topk, x,
+                       x_dtype, w, w_dtype, V, K, rescore_vec(x, w, w_dtype, K), y, ldy, idx, val,
+                       top1);
+    return hipGetLastError();
+}
 
 int64_t topk_max_v() { return (int64_t)256 * 32 * kMaxLists; }
 
@@ -374,9 +507,7 @@ hipError_t launch_topk_rescore(const void* x, int x_dtype, int M, const void* w,
         hipLaunchKernelGGL(topk_block_kernel<32>, dim3(C, M), dim3(256), 0, st, y, ldy, V, T, lists);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int esz = w_dtype == F32 ? 4 : 2;
-    const int vec = K % 8 == 0 && ((uintptr_t)x & 15u) == 0 && ((uintptr_t)w & 15u) == 0 &&
-                    (K * esz) % 16 == 0;
+    const int vec = rescore_vec(x, w, w_dtype, K);
     hipLaunchKernelGGL(topk_select_rescore_kernel, dim3(M), dim3(256), 0, st, lists, C, T, topk, x,
                        x_dtype, w, w_dtype, V, K, vec, y, ldy, idx, val, top1);
     return hipGetLastError();
