@@ -337,11 +337,11 @@ def main() -> int:
         # the library's automatic choice (lmhead_logits)
         if M == 1 and w.K <= 32768:
             return "gemv"
-        if M <= 16:
-            return "mfma"
         if M > 32 and w.K <= 1024 and (w.bits == 8 or w.group >= 64):
             return "mfma_xres"
-        return "mfma_lds"
+        if M > 32 or (M > 16 and w.K <= 1024) or (w.bits == 8 and w.K <= 1024):
+            return "mfma_lds"
+        return "mfma"
 
     per_call = {}
     for M in Ms:
