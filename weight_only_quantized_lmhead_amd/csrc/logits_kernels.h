@@ -155,10 +155,13 @@ __device__ __forceinline__ void store4(YT<OUT>* p, f4 v) {
 // order, so the result does not depend on timing).  Splitting K puts KS times
 // as many loads in flight per row block and gives the launch KS times as many
 // waves, which spreads a ragged number of blocks evenly over the CUs.
-// Superchunks stream through a ring of D register buffers; loads past the end
-// of the wave's range are clamped to its last superchunk (and their
-// contribution dropped) so every load is unconditional and the compiler can
-// keep exact vmcnt accounting (no drain at the loop head).  GPS = groups per
+// Superchunks stream through a ring of D register buffers (D = 1 for int4,
+// 2 for int8, whose waves cover twice as many superchunks): a buffer is
+// refilled as soon as it has been consumed, unless the wave's range has no
+// further superchunk (a wave-uniform test; for M > 1 the refill past the end
+// loads the last superchunk again); a ring slot past the end of the range
+// (fewer superchunks than D) loads the last one again and its contribution is
+// dropped.  GPS = groups per
 // superchunk (G <= span); GPS == 1 covers G >= span, the scale of superchunk c
 // then being that of group c / SPG.  With ZP the lane also reads its row's
 // zero point of each group (one byte, beside the scale).
@@ -295,7 +298,9 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint4* __restrict__ wq,
                     acc[m] = fmaf(sv, q, acc[m]);
                 }
             }
-            load(p, c + D);
+            // (the forced M = 2..4 variants keep the unconditional clamped
+            // load: the branch costs them registers)
+            if (MM > 1 || c + D < cend) load(p, c + D);
         }
     }
     if constexpr (KS > 1) {
@@ -1097,7 +1102,10 @@ struct Regions {
 
 template <int BITS, int MM, int OUT, bool ZP>
 hipError_t gemv_dispatch_gps(const LogitsArgs& a, int gps, hipStream_t st) {
-    constexpr int D = 1;
+    // ring depth: measured on the 151936-row heads at M = 1 (int8 g128: 29.2
+    // against 32.0 us with D = 1; int4 loses with D = 2, its registers double;
+    // the forced M = 2..4 variants keep D = 1 for the same reason)
+    constexpr int D = BITS == 8 && MM == 1 ? 2 : 1;
     const int NB = (int)((a.V + 63) / 64);
     const int NC = (int)(a.K / span_of(BITS));
     const int NG = (int)(a.K / a.G);
