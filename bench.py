@@ -66,10 +66,11 @@ def traffic_file(workload: str) -> str:
     return os.path.join(ROOT, "profiles", f"logits_{workload}_hbm_traffic.md")
 
 
-def recorded_traffic(workload: str, kernel_prefix: str, zp: bool = False):
-    """HBM bytes per launch of the kernel (the symmetric or the zero-point
-    instantiation) from the committed counter summary, or None when there is
-    none or the kernel sources changed since."""
+def recorded_traffic(workload: str, kernel_prefix: str, suffix: str):
+    """HBM bytes per launch of the kernel whose summary name starts with
+    `kernel_prefix` and whose template arguments end with `suffix` (e.g. the
+    GEMV's zero-point and top-K flags) from the committed counter summary, or
+    None when there is none or the kernel sources changed since."""
     f = traffic_file(workload)
     if not os.path.exists(f):
         return None
@@ -80,7 +81,7 @@ def recorded_traffic(workload: str, kernel_prefix: str, zp: bool = False):
                 return None
             for k in rec["kernels"]:
                 name = k["kernel"].split(" grid")[0]
-                if name.startswith(kernel_prefix) and name.endswith("true>" if zp else "false>"):
+                if name.startswith(kernel_prefix) and name.endswith(suffix):
                     return k
     return None
 
@@ -396,7 +397,8 @@ def main() -> int:
 
     m1 = per_call[f"M={Ms[0]}"]
     value = m1["us"]
-    tr = recorded_traffic(w.name, "gemv_kernel") if m1["kernel"] == "gemv" else None
+    # the symmetric GEMV without the top-K epilogue (template flags ZP, TK)
+    tr = recorded_traffic(w.name, "gemv_kernel<", ",false,false>") if m1["kernel"] == "gemv" else None
     roofline = {
         "bound": "hbm", "kernel": f"lmh gemv, M={Ms[0]}", "achieved": m1["GB/s"], "peak": HBM_PEAK_GBS,
         "unit": "GB/s", "frac": m1["frac_hbm_peak"], "traffic": tr["bytes"] if tr else None,
