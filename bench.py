@@ -178,6 +178,50 @@ def summarize(args) -> int:
     return 0
 
 
+def decode_agreement(args, w, lmh, synth, to_dev, blob, Wref, sdt, dev):
+    """Top-1 agreement of the quantized head with the unquantized 16-bit weight
+    (lmhead_dense_logits: exact 16-bit products, fp32 sums) over N seeded
+    decode states, before and after exact top-K rescoring (vLLM PR #48870,
+    review comment, point 2), and the overlap of the quantized and reference
+    top-K sets.  Each state is one activation row; they are run in batches."""
+    import torch
+
+    n, K = args.agreement, args.topk
+    X = to_dev(synth.decode_states(w, 0, n), w.x_dtype)
+    ref1 = torch.empty(n, dtype=torch.int64, device=dev)
+    margin = torch.empty(n, dtype=torch.float32, device=dev)
+    ref_sets, q_sets = [], []
+    for i in range(0, n, 4):  # the dense control takes up to 4 rows per call
+        yd = lmh.dense_logits(X[i:i + 4], Wref)
+        ref1[i:i + 4] = torch.argmax(yd, dim=1)
+        t2 = torch.topk(yd, 2, dim=1).values
+        margin[i:i + 4] = t2[:, 0] - t2[:, 1]
+        ref_sets.append(torch.topk(yd, K, dim=1).indices)
+    B = 64
+    q1 = torch.empty(n, dtype=torch.int64, device=dev)
+    r1 = torch.empty(n, dtype=torch.int64, device=dev)
+    for i in range(0, n, B):
+        xb = X[i:i + B]
+        yq = lmh.logits(xb, blob, w.V, w.K, w.bits, w.group, sdt)
+        q1[i:i + B] = torch.argmax(yq, dim=1)
+        q_sets.append(torch.topk(yq, K, dim=1).indices)
+        _, _, t1 = lmh.logits_topk(xb, blob, w.V, w.K, w.bits, w.group, sdt, Wref, K)
+        r1[i:i + B] = t1.long()
+    rs, qs = torch.cat(ref_sets), torch.cat(q_sets)
+    overlap = (rs.unsqueeze(2) == qs.unsqueeze(1)).any(dim=2).float().mean().item()
+    flip_q = q1 != ref1
+    flip_r = r1 != ref1
+    worst = margin[flip_r].max().item() if flip_r.any() else 0.0
+    return {"states": n, "topk": K,
+            "reference": "unquantized 16-bit weight, fp32-accumulated GEMV (lmhead_dense_logits)",
+            "top1_agreement_quantized": round(1.0 - flip_q.float().mean().item(), 6),
+            "top1_agreement_rescored": round(1.0 - flip_r.float().mean().item(), 6),
+            "flips_quantized": int(flip_q.sum().item()), "flips_rescored": int(flip_r.sum().item()),
+            "max_reference_margin_of_rescored_flips": worst,
+            "states_with_reference_margin_below_1e-3": int((margin < 1e-3).sum().item()),
+            "topk_set_overlap": round(overlap, 6)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -189,6 +233,10 @@ def main() -> int:
     ap.add_argument("--path", type=int, default=0, help="0 automatic, 1 GEMV, 2 register-fed MFMA, 3 LDS-staged MFMA, 4 activation-resident MFMA")
     ap.add_argument("--hot", action="store_true", help="reuse one copy of the head (cache-hot; labelled)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--agreement", type=int, default=0, metavar="N",
+                    help="also report, over N seeded decode states (one activation row each), the "
+                         "top-1 agreement with the unquantized 16-bit weight before and after exact "
+                         "top-K rescoring, and the top-K set overlap")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--summarize", action="store_true",
                     help="write a profiles/ summary from rocprofv3 CSV files instead of timing")
@@ -395,6 +443,8 @@ def main() -> int:
         per_call[f"embed_T={T}"] = {"us": round(e_us, 3), "algorithmic_bytes": eb,
                                      "GB/s": round(eb / (e_us * 1e-6) / 1e9, 1)}
 
+    agreement = decode_agreement(args, w, lmh, synth, to_dev, blob, Wref, sdt, dev) if args.agreement else None
+
     m1 = per_call[f"M={Ms[0]}"]
     value = m1["us"]
     # the symmetric GEMV without the top-K epilogue (template flags ZP, TK)
@@ -449,6 +499,8 @@ def main() -> int:
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if agreement is not None:
+        line["agreement"] = agreement
     print(json.dumps(line), flush=True)
     return 0
 

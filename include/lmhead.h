@@ -322,7 +322,7 @@ int lmhead_logits_typed(const void* x, int x_dtype, int64_t M, const void* packe
  *   16-bit weight: the bandwidth control of the fp16 logits GEMV (vLLM PR
  *   #48870, review comment, point 1).  fp32 accumulation.
  *   x [M, K] and W [V, K] row-major, both LMH_F16 or both LMH_BF16; K % 8 == 0.
- *   y [M, ldy] fp32, ldy >= V (4-byte alignment).  M <= 8.
+ *   y [M, ldy] fp32, ldy >= V (4-byte alignment).  M <= 4.
  */
 int lmhead_dense_logits(const void* x, int x_dtype, int64_t M, const void* w, int w_dtype,
                         int64_t V, int64_t K, float* y, int64_t ldy, void* stream);

@@ -135,3 +135,28 @@ def test_decode_path_all_ties():
     torch.cuda.synchronize()
     assert idx.cpu().numpy()[0].tolist() == list(range(topk))
     assert (val == 0).all() and int(top1[0]) == 0
+
+
+@pytest.mark.parametrize("M,topk", [(1, 8), (64, 8), (64, 16)])
+def test_rescoring_recovers_the_reference_top1(M, topk):
+    """Whenever the unquantized weight's top-1 (lmhead_dense_logits: exact 16-bit
+    products, fp32 sums) is among the quantized top-K and wins by a clear
+    margin, the rescored top-1 is that row (the rescoring recomputes those K
+    rows from the same weight)."""
+    need_gpu()
+    V, K, bits, G = 64 * 200 + 5, 512, 4, 64
+    w, blob = _head(V, K, bits, G, seed=M + topk)
+    wref = torch.from_numpy(w.astype(np.float16)).to(DEV)
+    wl = synth.WORKLOADS["tiny_w4g64_50304x512"]
+    x = to_dev(synth.decode_states(wl, 0, M), "f16")
+    yq = lmh.logits(x, blob, V, K, bits, G, torch.float16)
+    ref = torch.cat([lmh.dense_logits(x[i:i + 4], wref) for i in range(0, M, 4)])
+    _, _, top1 = lmh.logits_topk(x, blob, V, K, bits, G, torch.float16, wref, topk)
+    torch.cuda.synchronize()
+    ref1 = torch.argmax(ref, dim=1)
+    t2 = torch.topk(ref, 2, dim=1).values
+    clear = (t2[:, 0] - t2[:, 1]) > 1e-3
+    inset = (torch.topk(yq, topk, dim=1).indices == ref1[:, None]).any(dim=1)
+    sel = clear & inset
+    assert sel.any()
+    assert torch.equal(top1.long()[sel], ref1[sel])
