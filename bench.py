@@ -386,7 +386,7 @@ def main() -> int:
         # the library's automatic choice (lmhead_logits)
         if M == 1 and w.K <= 32768:
             return "gemv"
-        if M > 32 and w.K <= 1024 and (w.bits == 8 or w.group >= 64):
+        if M > 64 and w.K <= 1024 and w.bits == 4 and w.group >= 64:
             return "mfma_xres"
         if M > 32 or (M > 16 and w.K <= 1024) or (w.bits == 8 and w.K <= 1024):
             return "mfma_lds"

@@ -232,19 +232,20 @@ static int logits_impl(const void* x, int x_dtype, int64_t M, const void* packed
     a.list_T = list_T;
     const bool use_gemv = path == 1 || (path == 0 && gemv_ok && M <= lmh::kGemvAutoMaxM);
     if (use_gemv) return from_hip(lmh::launch_gemv(a, st));
-    // automatic, from an M = 2..40 sweep on the 151936 x 1024 int4 g64 and
-    // int8 g128 heads and the 248064 x 5120 int4 g128 head:
-    //   - from 33 rows the activation-resident kernel (M = 64..256: 6-18 %
-    //     faster than the LDS-staged one) unless K > 1024 or an int4 head has
-    //     32-column groups (it runs out of registers there);
-    //   - the LDS-staged kernel for 17..32 rows when K <= 1024 (10-15 % faster
-    //     than register-fed there), for every M >= 2 on int8 heads with
-    //     K <= 1024 (4-6 %), and beyond 32 rows when K > 1024 (the
-    //     register-fed kernel would read the weights once per 32 rows);
+    // automatic, from sweeps over M = 2..256 on the 151936 x 1024 int4 g64
+    // and int8 g128 heads and the 248064 x 5120 int4 g128 head:
+    //   - from 65 rows on int4 heads with K <= 1024 and G >= 64 the
+    //     activation-resident kernel (M = 96/128/256: 2-4 % faster than the
+    //     LDS-staged one; it runs out of registers with 32-column groups);
+    //   - the LDS-staged kernel for 17..64 rows when K <= 1024, for every
+    //     M >= 2 on int8 heads with K <= 1024 (2..16 rows: 4-6 % faster than
+    //     register-fed; 33..256: 0-8 % faster than activation-resident), and
+    //     beyond 32 rows when K > 1024 (the register-fed kernel would read the
+    //     weights once per 32 rows);
     //   - else the register-fed kernel (2..16 rows; 17..32 rows when K > 1024,
     //     where it is 6-9 % faster than the LDS-staged one).
-    const bool use_xres = path == 4 || (path == 0 && M > 32 && lmh::xres_fits(K) &&
-                                        (bits == 8 || group >= 64));
+    const bool use_xres = path == 4 || (path == 0 && M > 64 && lmh::xres_fits(K) && bits == 4 &&
+                                        group >= 64);
     if (use_xres) return from_hip(lmh::launch_mfma_xres(a, st));
     const bool narrow = K <= 1024;
     const bool use_lds = path == 3 || (path == 0 && (M > 32 || (M > 16 && narrow) ||
