@@ -384,11 +384,12 @@ def main() -> int:
 
     def auto_kernel(M):
         # the library's automatic choice (lmhead_logits)
-        if M == 1 and w.K <= 32768:
+        if (M == 1 or (M == 2 and w.bits == 4)) and M * w.K <= 32768:
             return "gemv"
         if M > 64 and w.K <= 1024 and w.bits == 4 and w.group >= 64:
             return "mfma_xres"
-        if M > 32 or (M > 16 and w.K <= 1024) or (w.bits == 8 and w.K <= 1024):
+        narrow = w.K <= 1024
+        if (M > 16 or w.bits == 8) if narrow else not (24 < M <= 32):
             return "mfma_lds"
         return "mfma"
 

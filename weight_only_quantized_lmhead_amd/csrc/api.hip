@@ -230,26 +230,29 @@ static int logits_impl(const void* x, int x_dtype, int64_t M, const void* packed
     a.zp = wd.zp;
     a.lists = lists;
     a.list_T = list_T;
-    const bool use_gemv = path == 1 || (path == 0 && gemv_ok && M <= lmh::kGemvAutoMaxM);
+    // the GEMV for one activation row, and for two on int4 heads (measured:
+    // 20.3 against 20.8 us at K = 1024, 133 against 141 us at K = 5120)
+    const bool use_gemv = path == 1 || (path == 0 && gemv_ok &&
+                                        (M <= lmh::kGemvAutoMaxM || (M == 2 && bits == 4)));
     if (use_gemv) return from_hip(lmh::launch_gemv(a, st));
     // automatic, from sweeps over M = 2..256 on the 151936 x 1024 int4 g64
     // and int8 g128 heads and the 248064 x 5120 int4 g128 head:
     //   - from 65 rows on int4 heads with K <= 1024 and G >= 64 the
     //     activation-resident kernel (M = 96/128/256: 2-4 % faster than the
     //     LDS-staged one; it runs out of registers with 32-column groups);
-    //   - the LDS-staged kernel for 17..64 rows when K <= 1024, for every
-    //     M >= 2 on int8 heads with K <= 1024 (2..16 rows: 4-6 % faster than
-    //     register-fed; 33..256: 0-8 % faster than activation-resident), and
-    //     beyond 32 rows when K > 1024 (the register-fed kernel would read the
-    //     weights once per 32 rows);
-    //   - else the register-fed kernel (2..16 rows; 17..32 rows when K > 1024,
-    //     where it is 6-9 % faster than the LDS-staged one).
+    //   - when K <= 1024: the LDS-staged kernel for 17..64 rows and for every
+    //     M >= 2 on int8 heads (2..16 rows: 4-6 % faster than register-fed;
+    //     33..256: 0-8 % faster than activation-resident), else the
+    //     register-fed kernel (3..16 rows on int4 heads);
+    //   - when K > 1024: the register-fed kernel for 25..32 rows (3 % faster),
+    //     else the LDS-staged one (2..24 rows: 1.5-3 % faster; beyond 32 rows
+    //     the register-fed kernel would read the weights once per 32 rows).
     const bool use_xres = path == 4 || (path == 0 && M > 64 && lmh::xres_fits(K) && bits == 4 &&
                                         group >= 64);
     if (use_xres) return from_hip(lmh::launch_mfma_xres(a, st));
     const bool narrow = K <= 1024;
-    const bool use_lds = path == 3 || (path == 0 && (M > 32 || (M > 16 && narrow) ||
-                                                     (bits == 8 && narrow)));
+    const bool use_lds = path == 3 || (path == 0 && (narrow ? (M > 16 || bits == 8)
+                                                            : !(M > 24 && M <= 32)));
     return from_hip(use_lds ? lmh::launch_mfma_lds(a, st) : lmh::launch_mfma(a, st));
 }
 
