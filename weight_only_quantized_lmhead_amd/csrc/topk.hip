@@ -147,18 +147,6 @@ __device__ __forceinline__ void to_f32x8(uint4 q, float* f) {
     }
 }
 
-template <int WD>
-__device__ __forceinline__ void load_w8(const void* __restrict__ w, int64_t off, float* f) {
-    if constexpr (WD == F32) {
-        const float4 a = *(const float4*)((const float*)w + off);
-        const float4 b = *(const float4*)((const float*)w + off + 4);
-        f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
-        f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
-    } else {
-        to_f32x8<WD>(*(const uint4*)((const uint16_t*)w + off), f);
-    }
-}
-
 // Exact fp32 dot products of x row m with the reference rows idx[t], t < topk.
 // All rows at once, so their loads are in flight together: row t goes to a
 // group of G = 256/P consecutive threads (P = topk rounded up to a power of
@@ -183,13 +171,45 @@ __device__ __forceinline__ void rescore_rows_t(const int* idx, int topk, int64_t
     const int64_t kend = on ? K : 0;
     float acc = 0.0f;
     if (vec) {
-#pragma unroll 4
-        for (int64_t k = 8 * sub; k < kend; k += 8 * G) {
-            float xf[8], wf[8];
-            to_f32x8<XD>(*(const uint4*)((const uint16_t*)x + m * K + k), xf);
-            load_w8<WD>(w, v * K + k, wf);
+        // batches of kB chunks: all their loads are issued before the first
+        // multiply, so a long row costs a few round trips to memory, not one
+        // per chunk; the sum still runs over the chunks in order
+        constexpr int kB = 8;
+        constexpr int WU = WD == F32 ? 2 : 1;  // 16-byte loads per 8 weights
+        for (int64_t k0 = 8 * sub; k0 < kend; k0 += (int64_t)8 * G * kB) {
+            uint4 xr[kB], wr[kB][WU];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) acc = fmaf(xf[q], wf[q], acc);
+            for (int b = 0; b < kB; ++b) {
+                const int64_t k = k0 + (int64_t)8 * G * b;
+                if (k < kend) {
+                    xr[b] = *(const uint4*)((const uint16_t*)x + m * K + k);
+#pragma unroll
+                    for (int u = 0; u < WU; ++u)
+                        wr[b][u] = WD == F32 ? *(const uint4*)((const float*)w + v * K + k + 4 * u)
+                                             : *(const uint4*)((const uint16_t*)w + v * K + k);
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < kB; ++b) {
+                const int64_t k = k0 + (int64_t)8 * G * b;
+                if (k < kend) {
+                    float xf[8], wf[8];
+                    to_f32x8<XD>(xr[b], xf);
+                    if constexpr (WD == F32) {
+#pragma unroll
+                        for (int u = 0; u < 2; ++u) {
+                            wf[4 * u] = __uint_as_float(wr[b][u].x);
+                            wf[4 * u + 1] = __uint_as_float(wr[b][u].y);
+                            wf[4 * u + 2] = __uint_as_float(wr[b][u].z);
+                            wf[4 * u + 3] = __uint_as_float(wr[b][u].w);
+                        }
+                    } else {
+                        to_f32x8<WD>(wr[b][0], wf);
+                    }
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) acc = fmaf(xf[q], wf[q], acc);
+                }
+            }
         }
     } else {
 #pragma unroll 4
