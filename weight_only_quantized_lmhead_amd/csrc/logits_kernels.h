@@ -13,18 +13,23 @@
 // fp32 and multiplied by the group scale in fp32 (the scale never touches a
 // 16-bit product).
 //
-// Kernels
-//   x_to_f16     bf16 x -> fp16 x * 2^-e per row (exact power-of-two scale,
-//                e chosen so max|x| lands in [2^14, 2^15)); y is scaled back.
-//   gemv         M <= 4 (and M*K <= 32768).  A wave owns 64 vocabulary rows
-//                (one row block, one lane per row, all of K: no cross-lane
-//                reduction).  x is staged in LDS once per workgroup and read
-//                as 16-byte broadcasts.
-//   mfma         larger M.  A wave owns one row block (4 MFMA column tiles of
-//                16 rows) and MT row tiles of 16 activations; each 16-byte
-//                slot load is one 16x16x32 B operand per 32-column word.
-//   dense        unquantized 16-bit control GEMV (the fp16 logits of the
-//                review comment, point 1).
+// Kernels (which one runs for which M and head is decided in api.hip)
+//   gemv         M <= 4 (and M*K <= 32768).  A lane owns one vocabulary row of
+//                a 64-row block over a contiguous 1/KS of K (KS waves per
+//                block, partial sums added in LDS in wave order).  x is
+//                staged in LDS once per workgroup and read as 16-byte
+//                broadcasts.  Optionally (TK) it also writes each block's
+//                sorted top-K list for the fused decode path.
+//   mfma         register-fed MFMA.  A wave owns one row block (4 MFMA column
+//                tiles of 16 rows) and MT row tiles of 16 activations; each
+//                16-byte slot load is one 16x16x32 B operand per 32-column
+//                word.
+//   mfma_lds     the same tiles, every operand staged in LDS by direct
+//                global-to-LDS loads; 32- or 64-row activation tiles.
+//   mfma_xres    a 64-row activation tile resident in LDS, weights streamed
+//                through a register ring (large M, K <= 1024).
+// (logits.hip adds the bf16 -> fp16 activation conversion and the dense
+// 16-bit control GEMV.)
 //
 // Zero-point heads (the asymmetric layout: unsigned codes n and one 8-bit
 // zero point z per row and group, w = (n - z) * s) use the same kernels with
