@@ -384,7 +384,7 @@ def main() -> int:
 
     def auto_kernel(M):
         # the library's automatic choice (lmhead_logits)
-        if (M == 1 or (M == 2 and w.bits == 4)) and M * w.K <= 32768:
+        if M <= 2 and M * w.K <= 32768:
             return "gemv"
         if M > 64 and w.K <= 1024 and w.bits == 4 and w.group >= 64:
             return "mfma_xres"

@@ -267,8 +267,8 @@ size_t lmhead_logits_workspace_bytes(int64_t M, int64_t K, int x_dtype);
  *           written.  Needs only 4-byte alignment.
  *   workspace / ws_bytes: at least lmhead_logits_workspace_bytes(M, K, x_dtype)
  *           (may be NULL/0 for fp16 x).
- *   M = 1 (and M = 2 on int4 heads) runs a GEMV with one lane per vocabulary
- *   row (all of K per wave); larger M runs a 16x16x32 fp16 MFMA kernel (its
+ *   M = 1 and M = 2 run a GEMV with one lane per vocabulary row (all of K
+ *   per wave); larger M runs a 16x16x32 fp16 MFMA kernel (its
  *   code unpacking is shared by all activation rows), chosen from
  *   measurements: for K <= 1024, the activation-resident one from M = 65 on
  *   int4 heads with G >= 64, the LDS-staged one for M = 17..64 and for int8

@@ -230,10 +230,10 @@ static int logits_impl(const void* x, int x_dtype, int64_t M, const void* packed
     a.zp = wd.zp;
     a.lists = lists;
     a.list_T = list_T;
-    // the GEMV for one activation row, and for two on int4 heads (measured:
-    // 20.3 against 20.8 us at K = 1024, 133 against 141 us at K = 5120)
-    const bool use_gemv = path == 1 || (path == 0 && gemv_ok &&
-                                        (M <= lmh::kGemvAutoMaxM || (M == 2 && bits == 4)));
+    // the GEMV for one or two activation rows (measured at M = 2 against the
+    // best MFMA kernel: int4 K = 1024 20.3 vs 20.8 us, int4 K = 5120 133 vs
+    // 141 us, int8 K = 1024 29.5 vs 31.6 us)
+    const bool use_gemv = path == 1 || (path == 0 && gemv_ok && M <= lmh::kGemvAutoMaxM);
     if (use_gemv) return from_hip(lmh::launch_gemv(a, st));
     // automatic, from sweeps over M = 2..256 on the 151936 x 1024 int4 g64
     // and int8 g128 heads and the 248064 x 5120 int4 g128 head:
@@ -241,11 +241,11 @@ static int logits_impl(const void* x, int x_dtype, int64_t M, const void* packed
     //     activation-resident kernel (M = 96/128/256: 2-4 % faster than the
     //     LDS-staged one; it runs out of registers with 32-column groups);
     //   - when K <= 1024: the LDS-staged kernel for 17..64 rows and for every
-    //     M >= 2 on int8 heads (2..16 rows: 4-6 % faster than register-fed;
+    //     M >= 3 on int8 heads (2..16 rows: 4-6 % faster than register-fed;
     //     33..256: 0-8 % faster than activation-resident), else the
     //     register-fed kernel (3..16 rows on int4 heads);
     //   - when K > 1024: the register-fed kernel for 25..32 rows (3 % faster),
-    //     else the LDS-staged one (2..24 rows: 1.5-3 % faster; beyond 32 rows
+    //     else the LDS-staged one (3..24 rows: 1.5-3 % faster; beyond 32 rows
     //     the register-fed kernel would read the weights once per 32 rows).
     const bool use_xres = path == 4 || (path == 0 && M > 64 && lmh::xres_fits(K) && bits == 4 &&
                                         group >= 64);
@@ -369,8 +369,9 @@ int lmhead_logits_topk(const void* x, int x_dtype, int64_t M, const void* packed
     // one activation row through the GEMV: its epilogue writes each 64-row
     // block's sorted top-T list, and one merge kernel selects and rescores
     // (no separate pass over the logits; y is stored only when given)
-    const bool gemv_auto = M <= lmh::kGemvAutoMaxM && M <= lmh::kGemvMaxM && M * K <= lmh::kGemvMaxMK;
-    if (gemv_auto && lmh::topk_fused_ok(V, topk)) {
+    // (the GEMV's top-K epilogue exists for one activation row only)
+    const bool gemv_one = M == 1 && K <= lmh::kGemvMaxMK;
+    if (gemv_one && lmh::topk_fused_ok(V, topk)) {
         const int T = (int)(topk + 1 <= V ? topk + 1 : V);
         lmh::u64* lists = (lmh::u64*)(ws + xws);
         rc = logits_impl(x, x_dtype, M, packed, V, K, bits, group, scale_dtype, bias, y, F32, ldy,

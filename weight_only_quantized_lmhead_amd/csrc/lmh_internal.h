@@ -101,11 +101,11 @@ hipError_t launch_topk_merge_rescore(const u64* lists, const void* x, int x_dtyp
                                      int32_t* top1, hipStream_t st);
 int64_t topk_max_v();  // largest row length lmhead_topk_rescore supports
 
-// Largest M the lane-per-row GEMV accepts when forced (it runs by default only
-// for M = 1: from M = 2 on the MFMA kernel is faster, its unpacking being
-// shared by all rows), and the largest M*K it stages in LDS (64 KiB of fp16).
+// Largest M the lane-per-row GEMV accepts when forced, the largest it runs by
+// default (from M = 3 on an MFMA kernel is faster, its unpacking being shared
+// by all rows), and the largest M*K it stages in LDS (64 KiB of fp16).
 constexpr int kGemvMaxM = 4;
-constexpr int kGemvAutoMaxM = 1;
+constexpr int kGemvAutoMaxM = 2;
 constexpr int64_t kGemvMaxMK = 32768;
 
 }  // namespace lmh
