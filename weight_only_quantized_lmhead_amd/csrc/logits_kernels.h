@@ -194,7 +194,11 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint4* __restrict__ wq,
     constexpr int NA = MM == 1 ? 4 : (MM == 2 ? 2 : 1);  // independent partial sums per group
     static_assert(KS == 1 || KS == 2 || KS == 4, "K split over 1, 2 or 4 waves");
     const int lane = threadIdx.x & 63;
-    const int wv = threadIdx.x >> 6;
+    // the wave index, as a wave-uniform value the block and K-range arithmetic
+    // runs on the scalar unit (measured: faster at M = 1 and on int8 heads,
+    // slower for two rows of an int4 head, which keep the vector form)
+    const int wv = MM == 1 || BITS == 8 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)
+                                        : threadIdx.x >> 6;
     const int blk_raw = blockIdx.x * (4 / KS) + wv / KS;
     const int ks = wv % KS;
     const bool live = blk_raw < NB;
@@ -410,7 +414,7 @@ __global__ __launch_bounds__(256, MT >= 4 ? 1 : 2) void mfma_kernel(
     __shared__ __attribute__((aligned(16))) _Float16 xs[2 * STAGE];
 
     const int lane = threadIdx.x & 63;
-    const int wv = threadIdx.x >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int blk = rg * 4 + wv;
     const bool live = blk < NB;
     const int blkc = live ? blk : NB - 1;
@@ -650,7 +654,7 @@ void mfma_lds_kernel(
     const int nsteps = ntile * NC;
     if (nsteps == 0) return;
 
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 15, t = lane >> 4;
     // fixed parts of this lane's activation loads: wave instruction q = wv + 4i
     // fills LDS pieces [64q, 64q+64); piece P = row*P8 + sp holds global piece
@@ -923,14 +927,19 @@ void mfma_lds_kernel(
 // slot comes from HBM once and from that XCD's L2 for the other tiles.
 constexpr int kXresMaxK = 1024;
 
-template <int BITS, int GPS, int D, bool TR, int OUT, bool ZP>
-__global__ __launch_bounds__(512, 1) void mfma_xres_kernel(
+template <int NT_>
+constexpr int xres_waves() { return NT_ == 4 ? 8 : 16; }
+
+template <int BITS, int GPS, int D, bool TR, int OUT, bool ZP, int NT_>
+__global__ __launch_bounds__(64 * xres_waves<NT_>(), 1) void mfma_xres_kernel(
     const uint4* __restrict__ wq, const uint16_t* __restrict__ sc, const uint8_t* __restrict__ zq,
     const _Float16* __restrict__ x,
     const int* __restrict__ xexp, const float* __restrict__ bias, void* __restrict__ y,
     int64_t ldy, int V, int K, int M, int NB, int NC, int NG, int SPG, int sbf16, int NMT,
     int VRX) {
-    constexpr int MT = 4, NT = 4, ROWS = 64;
+    constexpr int MT = 4, NT = NT_, ROWS = 64;
+    constexpr int WAVES = xres_waves<NT_>(), NTH = 64 * WAVES;
+    constexpr int PARTS = 4 / NT;  // a row block's 64 columns in PARTS units of 16 NT
     constexpr int SPAN = BITS == 4 ? 128 : 64;
     constexpr int CPS = SPAN / 32;
     constexpr int CPG = CPS / GPS;
@@ -945,7 +954,7 @@ __global__ __launch_bounds__(512, 1) void mfma_xres_kernel(
     const int m0 = mtile * ROWS;
     const int P = K / 8;                       // 16-byte pieces per row
     const int msk = (P & 15) == 0 ? 15 : 7;    // piece p of row m sits at p ^ (m & msk)
-    for (int i = threadIdx.x; i < ROWS * P; i += 512) {
+    for (int i = threadIdx.x; i < ROWS * P; i += NTH) {
         const int m = i / P, p = i - m * P;
         const int mr = min(m0 + m, M - 1);     // rows past M: any valid row, never stored
         xs[m * P + (p ^ (m & msk))] = *(const uint4*)(x + (int64_t)mr * K + p * 8);
@@ -953,12 +962,17 @@ __global__ __launch_bounds__(512, 1) void mfma_xres_kernel(
     if (xexp && threadIdx.x < ROWS) xe_s[threadIdx.x] = xexp[min(m0 + (int)threadIdx.x, M - 1)];
     __syncthreads();
 
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, t = lane >> 4;
     // 4-element output stores need rows aligned to 4 elements
     constexpr int OSZ = OUT == F32 ? 4 : 2;
     const bool vec16 = ((uintptr_t)y & (4 * OSZ - 1)) == 0 && (ldy & 3) == 0;
-    const int nblk = rb1 - rb0 > wv ? (rb1 - rb0 - wv + 7) / 8 : 0;
+    // the wave's units: u = wv + WAVES i, row block rb0 + u / PARTS, columns
+    // from 16 nb on; WAVES is a multiple of PARTS, so nb is the wave's own
+    static_assert(WAVES % PARTS == 0, "each wave keeps one column range");
+    const int nb = (wv % PARTS) * NT;
+    const int nunit = (rb1 - rb0) * PARTS;
+    const int nblk = nunit > wv ? (nunit - wv + WAVES - 1) / WAVES : 0;
     const int nsteps = nblk * NC;
     if (nsteps == 0) return;
 
@@ -973,12 +987,12 @@ __global__ __launch_bounds__(512, 1) void mfma_xres_kernel(
     auto load = [&](int p, int s) {
         const int sl = min(s, nsteps - 1);
         const int i = sl / NC, c = sl - i * NC;
-        const int blk = rb0 + wv + 8 * i;
-        const uint4* wp = wq + ((int64_t)blk * NC + c) * 256 + t * 64 + r;
+        const int blk = rb0 + wv / PARTS + (WAVES / PARTS) * i;
+        const uint4* wp = wq + ((int64_t)blk * NC + c) * 256 + t * 64 + r + 16 * nb;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) wbuf[p][nt] = wp[16 * nt];
         const int g0 = GPS > 1 ? c * GPS : c / SPG;
-        const uint16_t* sp = sc + ((int64_t)blk * NG + g0) * 64 + (TR ? 4 * t : r);
+        const uint16_t* sp = sc + ((int64_t)blk * NG + g0) * 64 + (TR ? 4 * t : r) + 16 * nb;
 #pragma unroll
         for (int g = 0; g < GPS; ++g)
 #pragma unroll
@@ -1011,7 +1025,7 @@ __global__ __launch_bounds__(512, 1) void mfma_xres_kernel(
                 f4 sv[NT];  // the scale of each of the lane's 4 result elements
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
-                    const ZC zc = ZP ? zc_byte(zbuf[p][g], nt) : zc_sym<BITS>();
+                    const ZC zc = ZP ? zc_byte(zbuf[p][g], nb + nt) : zc_sym<BITS>();
 #pragma unroll
                     for (int jj = 0; jj < CPG; ++jj) {
                         h2 p0, p1, p2, p3;
@@ -1082,8 +1096,9 @@ __global__ __launch_bounds__(512, 1) void mfma_xres_kernel(
                 // row m = m0 + 16 mt + r and the 4 columns v = blk*64 + 16 nt +
                 // 4 t + e, e = 0..3, contiguous: one 16-byte store each (when
                 // y's rows are 16-byte aligned and all 4 columns exist)
-                const int blk = rb0 + wv + 8 * ci;
-                const int vlim = V - blk * 64 - 4 * t;  // 16 nt + e < vlim: column inside V
+                const int blk = rb0 + wv / PARTS + (WAVES / PARTS) * ci;
+                const int cb = blk * 64 + 16 * nb;  // the unit's first column
+                const int vlim = V - cb - 4 * t;  // 16 nt + e < vlim: column inside V
                 int mlim = M - m0 - r;                  // 16 mt < mlim: row inside M
                 // (kept opaque so the row tests stay here instead of being
                 // hoisted out of the loop)
@@ -1093,8 +1108,8 @@ __global__ __launch_bounds__(512, 1) void mfma_xres_kernel(
                 for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        bv[nt][e] = (bias && 16 * nt + e < vlim) ? bias[blk * 64 + 16 * nt + 4 * t + e] : 0.0f;
-                YT<OUT>* yrow = (YT<OUT>*)y + (int64_t)(m0 + r) * ldy + (int64_t)blk * 64 + 4 * t;
+                        bv[nt][e] = (bias && 16 * nt + e < vlim) ? bias[cb + 16 * nt + 4 * t + e] : 0.0f;
+                YT<OUT>* yrow = (YT<OUT>*)y + (int64_t)(m0 + r) * ldy + (int64_t)cb + 4 * t;
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
                     if (16 * mt < mlim) {
@@ -1122,10 +1137,52 @@ __global__ __launch_bounds__(512, 1) void mfma_xres_kernel(
                 }
                 } else {
                 // the block's results: y[m, v] = acc * 2^xexp[m] + bias[v] for
-                // rows m = m0 + 16 mt + 4 t + e and columns v = blk * 64 + 16 nt + r,
+                // rows m = m0 + 16 mt + 4 t + e and columns v = cb + 16 nt + r,
                 // through one row pointer that steps down the lane's rows
-                const int blk = rb0 + wv + 8 * ci;
-                const int vlim = V - blk * 64 - r;  // 16 nt < vlim: column inside V
+                const int blk = rb0 + wv / PARTS + (WAVES / PARTS) * ci;
+                const int cb = blk * 64 + 16 * nb;  // the unit's first column
+                if (xexp == nullptr && V - cb >= 16 * NT) {
+                    // every column of the unit inside V, fp16 x: no column
+                    // tests, and row tests only in a tile that extends past M
+                    // (one per row of NT stores)
+                    float bv[NT];
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) bv[nt] = bias ? bias[cb + 16 * nt + r] : 0.0f;
+                    YT<OUT>* yrow = (YT<OUT>*)y + (int64_t)(m0 + 4 * t) * ldy + (int64_t)cb + r;
+                    auto row_out = [&](int mt, int e) {
+#pragma unroll
+                        for (int nt = 0; nt < NT; ++nt)
+                            yrow[16 * nt] = to_out<OUT>(acc[mt][nt][e] + bv[nt]);
+                    };
+                    if (M - m0 >= 64) {
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                row_out(mt, e);
+                                yrow += ldy;
+                            }
+                            yrow += 12 * ldy;
+                        }
+                    } else {
+                        int mlim = M - m0 - 4 * t;  // 16 mt + e < mlim: row inside M
+                        asm volatile("" : "+v"(mlim));
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                if (16 * mt + e < mlim) row_out(mt, e);
+                                yrow += ldy;
+                            }
+                            yrow += 12 * ldy;
+                        }
+                    }
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = (f4){0.f, 0.f, 0.f, 0.f};
+                } else {
+                const int vlim = V - cb - r;  // 16 nt < vlim: column inside V
                 int mlim = M - m0 - 4 * t;          // 16 mt + e < mlim: row inside M
                 // (kept opaque so the row tests stay here instead of being
                 // hoisted out of the loop, where they would pin 32 SGPRs)
@@ -1133,8 +1190,8 @@ __global__ __launch_bounds__(512, 1) void mfma_xres_kernel(
                 float bv[NT];
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt)
-                    bv[nt] = (bias && 16 * nt < vlim) ? bias[blk * 64 + 16 * nt + r] : 0.0f;
-                YT<OUT>* yrow = (YT<OUT>*)y + (int64_t)(m0 + 4 * t) * ldy + (int64_t)blk * 64 + r;
+                    bv[nt] = (bias && 16 * nt < vlim) ? bias[cb + 16 * nt + r] : 0.0f;
+                YT<OUT>* yrow = (YT<OUT>*)y + (int64_t)(m0 + 4 * t) * ldy + (int64_t)cb + r;
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
@@ -1153,6 +1210,7 @@ __global__ __launch_bounds__(512, 1) void mfma_xres_kernel(
                         yrow += ldy;
                     }
                     yrow += 12 * ldy;  // the lane's next rows are 16 further on
+                }
                 }
                 }
             }
@@ -1301,7 +1359,7 @@ hipError_t mfma_lds_dispatch(const LogitsArgs& a, hipStream_t st) {
     return mfma_lds_dispatch_mt<BITS, 4, 2, 4, OUT, ZP>(a, st);
 }
 
-template <int BITS, int D, bool TR, int OUT, bool ZP>
+template <int BITS, int D, bool TR, int OUT, bool ZP, int NT_>
 hipError_t mfma_xres_dispatch_d(const LogitsArgs& a, hipStream_t st) {
     const int NB = (int)((a.V + 63) / 64);
     const int NC = (int)(a.K / span_of(BITS));
@@ -1314,7 +1372,8 @@ hipError_t mfma_xres_dispatch_d(const LogitsArgs& a, hipStream_t st) {
     const int VRX = NMT >= 32 ? 1 : 32 / NMT;
     const dim3 grid((unsigned)(8 * NMT * VRX));
 #define LMH_XRES(G_)                                                                              \
-    hipLaunchKernelGGL((mfma_xres_kernel<BITS, G_, D, TR, OUT, ZP>), grid, dim3(512), 0, st,    \
+    hipLaunchKernelGGL((mfma_xres_kernel<BITS, G_, D, TR, OUT, ZP, NT_>), grid,                  \
+                       dim3(64 * xres_waves<NT_>()), 0, st,                                       \
                        rg.wq, rg.sc, rg.zq,                                                       \
                        (const _Float16*)a.x, a.xexp, a.bias, a.y, a.ldy, (int)a.V, (int)a.K, a.M, \
                        NB, NC, NG, SPG, a.scale_bf16, NMT, VRX)
@@ -1343,8 +1402,8 @@ template <int BITS, int OUT, bool ZP>
 hipError_t xres_dispatch(const LogitsArgs& a, hipStream_t st) {
     // (zero-point int4 heads: a 2-deep ring, which leaves room for the zero
     // point words without spilling)
-    if constexpr (BITS == 4) return mfma_xres_dispatch_d<4, ZP ? 2 : 3, false, OUT, ZP>(a, st);
-    else return mfma_xres_dispatch_d<8, 2, true, OUT, ZP>(a, st);
+    if constexpr (BITS == 4) return mfma_xres_dispatch_d<4, 2, false, OUT, ZP, 2>(a, st);
+    else return mfma_xres_dispatch_d<8, 2, true, OUT, ZP, 2>(a, st);
 }
 
 // The kernel family `f` for the head's code width and the output type.
