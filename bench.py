@@ -386,7 +386,7 @@ def main() -> int:
         # the library's automatic choice (lmhead_logits)
         if M <= 2 and M * w.K <= 32768:
             return "gemv"
-        if w.K <= 1024 and w.group >= 64 and (M >= 64 if w.bits == 4 else M > 64):
+        if M > 32 and w.K <= 1024 and w.group >= 64:
             return "mfma_xres"
         narrow = w.K <= 1024
         if (M > 16 or w.bits == 8) if narrow else not (24 < M <= 32):

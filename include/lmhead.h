@@ -271,9 +271,9 @@ size_t lmhead_logits_workspace_bytes(int64_t M, int64_t K, int x_dtype);
  *   per wave); larger M runs a 16x16x32 fp16 MFMA kernel (its
  *   code unpacking is shared by all activation rows), chosen from
  *   measurements: for K <= 1024 and G >= 64, the activation-resident one
- *   from M = 64 on int4 heads and from M = 65 on int8 heads; otherwise for
- *   K <= 1024 the LDS-staged one for M = 17..63 and for int8 heads, else the
- *   register-fed one; for K > 1024, the register-fed one for
+ *   from M = 33 on; otherwise for K <= 1024 the LDS-staged one for
+ *   M = 17..32 and for int8 heads, else the register-fed one; for K > 1024,
+ *   the register-fed one for
  *   M = 25..32, else the LDS-staged one (see lmhead_logits_path).  Every
  *   MFMA kernel runs the same per-group MFMA chains and fp32 scale FMAs in
  *   the same order, so they give bit-identical results.  The result does not

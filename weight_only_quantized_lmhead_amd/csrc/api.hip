@@ -237,21 +237,19 @@ static int logits_impl(const void* x, int x_dtype, int64_t M, const void* packed
     if (use_gemv) return from_hip(lmh::launch_gemv(a, st));
     // automatic, from sweeps over M = 2..256 on the 151936 x 1024 int4 g64
     // and int8 g128 heads and the 248064 x 5120 int4 g128 head:
-    //   - when K <= 1024 and G >= 64, the activation-resident kernel from 64
-    //     rows on int4 heads and from 65 on int8 heads (int4 M = 64: 35 vs
-    //     41.5 us, M = 96..256: 6-10 % faster than the LDS-staged one; int8
-    //     M = 128 / 256: 2 / 5 % faster, equal at 48..64; with 32-column
-    //     groups it runs out of registers);
-    //   - when K <= 1024: the LDS-staged kernel for 17..63 rows and for every
-    //     M >= 3 on int8 heads (int8 2..32 rows: 25 % faster than
-    //     activation-resident; int4 33..56: 0-3 %), else the register-fed
-    //     kernel (3..16 rows on int4 heads; the LDS-staged one is 4-6 %
-    //     slower there);
+    //   - when K <= 1024 and G >= 64, the activation-resident kernel from 33
+    //     rows on (int4 M = 33..64: 29-33 us against 38-42 for the LDS-staged
+    //     kernel's 64-row tiles; M = 96..256 6-10 % faster; int8 M = 40..256:
+    //     0-14 % faster; with 32-column groups it runs out of registers);
+    //   - when K <= 1024: the LDS-staged kernel for 17..32 rows (int4: 25-28
+    //     us against 30-32 activation-resident) and for every M >= 3 on int8
+    //     heads (int8 2..32 rows: 15-25 % faster than activation-resident),
+    //     else the register-fed kernel (3..16 rows on int4 heads; the
+    //     LDS-staged one is 4-6 % slower there);
     //   - when K > 1024: the register-fed kernel for 25..32 rows (3 % faster),
     //     else the LDS-staged one (3..24 rows: 1.5-3 % faster; beyond 32 rows
     //     the register-fed kernel would read the weights once per 32 rows).
-    const bool use_xres = path == 4 || (path == 0 && lmh::xres_fits(K) && group >= 64 &&
-                                        (bits == 4 ? M >= 64 : M > 64));
+    const bool use_xres = path == 4 || (path == 0 && M > 32 && lmh::xres_fits(K) && group >= 64);
     if (use_xres) return from_hip(lmh::launch_mfma_xres(a, st));
     const bool narrow = K <= 1024;
     const bool use_lds = path == 3 || (path == 0 && (narrow ? (M > 16 || bits == 8)

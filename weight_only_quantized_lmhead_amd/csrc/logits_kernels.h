@@ -927,6 +927,15 @@ void mfma_lds_kernel(
 // slot comes from HBM once and from that XCD's L2 for the other tiles.
 constexpr int kXresMaxK = 1024;
 
+// Wait for every outstanding vector-memory operation of the wave.  Issued
+// right after the epilogue's bias loads, so that no path leaves a load in
+// flight into a register that another path of the loop reuses: the compiler's
+// wait insertion cannot tell the paths apart, and would otherwise make the
+// no-bias stores wait for the ring loads too.
+__device__ __forceinline__ void wait_vm_all() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt untouched
+}
+
 template <int NT_>
 constexpr int xres_waves() { return NT_ == 4 ? 8 : 16; }
 
@@ -1104,11 +1113,17 @@ __global__ __launch_bounds__(64 * xres_waves<NT_>(), 1) void mfma_xres_kernel(
                 // hoisted out of the loop)
                 asm volatile("" : "+v"(mlim));
                 f4 bv[NT];
+                if (bias) {
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt)
+                    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        bv[nt][e] = (bias && 16 * nt + e < vlim) ? bias[cb + 16 * nt + 4 * t + e] : 0.0f;
+                        for (int e = 0; e < 4; ++e)
+                            bv[nt][e] = 16 * nt + e < vlim ? bias[cb + 16 * nt + 4 * t + e] : 0.0f;
+                    wait_vm_all();
+                } else {
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) bv[nt] = (f4){0.f, 0.f, 0.f, 0.f};
+                }
                 YT<OUT>* yrow = (YT<OUT>*)y + (int64_t)(m0 + r) * ldy + (int64_t)cb + 4 * t;
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
@@ -1146,8 +1161,14 @@ __global__ __launch_bounds__(64 * xres_waves<NT_>(), 1) void mfma_xres_kernel(
                     // tests, and row tests only in a tile that extends past M
                     // (one per row of NT stores)
                     float bv[NT];
+                    if (bias) {
 #pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) bv[nt] = bias ? bias[cb + 16 * nt + r] : 0.0f;
+                        for (int nt = 0; nt < NT; ++nt) bv[nt] = bias[cb + 16 * nt + r];
+                        wait_vm_all();
+                    } else {
+#pragma unroll
+                        for (int nt = 0; nt < NT; ++nt) bv[nt] = 0.0f;
+                    }
                     YT<OUT>* yrow = (YT<OUT>*)y + (int64_t)(m0 + 4 * t) * ldy + (int64_t)cb + r;
                     auto row_out = [&](int mt, int e) {
 #pragma unroll
@@ -1188,9 +1209,14 @@ __global__ __launch_bounds__(64 * xres_waves<NT_>(), 1) void mfma_xres_kernel(
                 // hoisted out of the loop, where they would pin 32 SGPRs)
                 asm volatile("" : "+v"(mlim));
                 float bv[NT];
+                if (bias) {
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt)
-                    bv[nt] = (bias && 16 * nt < vlim) ? bias[cb + 16 * nt + r] : 0.0f;
+                    for (int nt = 0; nt < NT; ++nt) bv[nt] = 16 * nt < vlim ? bias[cb + 16 * nt + r] : 0.0f;
+                    wait_vm_all();
+                } else {
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) bv[nt] = 0.0f;
+                }
                 YT<OUT>* yrow = (YT<OUT>*)y + (int64_t)(m0 + 4 * t) * ldy + (int64_t)cb + r;
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
