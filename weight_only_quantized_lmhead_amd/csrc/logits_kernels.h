@@ -913,18 +913,21 @@ void mfma_lds_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Activation-resident MFMA kernel (large M, K <= kXresMaxK).  A workgroup of 8
-// waves loads one 64-row activation tile x[m0 .. m0+63, 0 .. K) into LDS once
-// (16-byte pieces swizzled as in mfma_lds_kernel) and then sweeps a
-// contiguous range of row blocks, one block per wave at a time, with no
-// further barrier: each wave streams its blocks' weight slots and scales
-// through a D-deep register ring (loads past its last step are clamped to
-// that step and their contribution dropped, so every load is unconditional
-// and the wait counts stay exact), reads its A operands from the resident
-// tile, and stores a block's 64 x 64 results as soon as its last superchunk
-// is done.  The workgroups of one XCD cover NMT activation tiles times VRX
-// vocabulary ranges with the NMT tiles of a range side by side, so a weight
-// slot comes from HBM once and from that XCD's L2 for the other tiles.
+// Activation-resident MFMA kernel (M > 32, K <= kXresMaxK).  A workgroup of
+// 16 waves (8 with NT = 4) loads one 64-row activation tile
+// x[m0 .. m0+63, 0 .. K) into LDS once (16-byte pieces swizzled as in
+// mfma_lds_kernel) and then sweeps a contiguous range of row blocks with no
+// further barrier.  A wave's unit of work is 16 NT columns of a row block
+// (NT = 2: half a block, so 32 accumulator registers and 4 waves per SIMD to
+// hide each other's latency); each wave streams its units' weight slots and
+// scales through a D-deep register ring (loads past its last step are clamped
+// to that step and their contribution dropped, so every load is
+// unconditional and the wait counts stay exact), reads its A operands from
+// the resident tile, and stores a unit's 64 x 16 NT results as soon as its
+// last superchunk is done.  The workgroups of one XCD cover NMT activation
+// tiles times VRX vocabulary ranges with the NMT tiles of a range side by
+// side, so a weight slot comes from HBM once and from that XCD's L2 for the
+// other tiles.
 constexpr int kXresMaxK = 1024;
 
 // Wait for every outstanding vector-memory operation of the wave.  Issued
@@ -985,7 +988,7 @@ __global__ __launch_bounds__(64 * xres_waves<NT_>(), 1) void mfma_xres_kernel(
     const int nsteps = nblk * NC;
     if (nsteps == 0) return;
 
-    // ring stage: the 4 slots, and per group and column tile the scales of the
+    // ring stage: the NT slots, and per group and column tile the scales of the
     // lane's vocabulary rows: row 16 nt + r (one 2-byte load), or with TR the
     // 4 rows 16 nt + 4 t .. + 3 (one 8-byte load); with ZP per group the zero
     // points of the rows the lane unpacks, 16 nt + r (one 4-byte load)
@@ -1101,8 +1104,8 @@ __global__ __launch_bounds__(64 * xres_waves<NT_>(), 1) void mfma_xres_kernel(
             load(p, s + D);
             if (real && cc == NC - 1) {
                 if constexpr (TR) {
-                // the block's results: y[m, v] = acc * 2^xexp[m] + bias[v] for
-                // row m = m0 + 16 mt + r and the 4 columns v = blk*64 + 16 nt +
+                // the unit's results: y[m, v] = acc * 2^xexp[m] + bias[v] for
+                // row m = m0 + 16 mt + r and the 4 columns v = cb + 16 nt +
                 // 4 t + e, e = 0..3, contiguous: one 16-byte store each (when
                 // y's rows are 16-byte aligned and all 4 columns exist)
                 const int blk = rb0 + wv / PARTS + (WAVES / PARTS) * ci;
@@ -1151,7 +1154,7 @@ __global__ __launch_bounds__(64 * xres_waves<NT_>(), 1) void mfma_xres_kernel(
                     yrow += 16 * ldy;
                 }
                 } else {
-                // the block's results: y[m, v] = acc * 2^xexp[m] + bias[v] for
+                // the unit's results: y[m, v] = acc * 2^xexp[m] + bias[v] for
                 // rows m = m0 + 16 mt + 4 t + e and columns v = cb + 16 nt + r,
                 // through one row pointer that steps down the lane's rows
                 const int blk = rb0 + wv / PARTS + (WAVES / PARTS) * ci;
