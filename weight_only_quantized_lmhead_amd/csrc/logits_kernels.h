@@ -964,18 +964,30 @@ __global__ __launch_bounds__(64 * xres_waves<NT_>(), 1) void mfma_xres_kernel(
     const int NV = 8 * VRX;
     const int rb0 = (int)((int64_t)NB * vr / NV), rb1 = (int)((int64_t)NB * (vr + 1) / NV);
     const int m0 = mtile * ROWS;
+    // rows at a fixed pitch of kXresMaxK / 8 pieces (2 KiB), whatever K is, so
+    // that a lane's read addresses differ between tiles and steps by constants;
+    // piece p of row m sits at p ^ (m & 15)
+    constexpr int PP = kXresMaxK / 8;
     const int P = K / 8;                       // 16-byte pieces per row
-    const int msk = (P & 15) == 0 ? 15 : 7;    // piece p of row m sits at p ^ (m & msk)
     for (int i = threadIdx.x; i < ROWS * P; i += NTH) {
         const int m = i / P, p = i - m * P;
         const int mr = min(m0 + m, M - 1);     // rows past M: any valid row, never stored
-        xs[m * P + (p ^ (m & msk))] = *(const uint4*)(x + (int64_t)mr * K + p * 8);
+        xs[m * PP + (p ^ (m & 15))] = *(const uint4*)(x + (int64_t)mr * K + p * 8);
     }
     if (xexp && threadIdx.x < ROWS) xe_s[threadIdx.x] = xexp[min(m0 + (int)threadIdx.x, M - 1)];
     __syncthreads();
 
     const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, t = lane >> 4;
+    // the lane's A operand of chunk ch of superchunk cc, activation tile mt:
+    // row 16 mt + r, piece cc * CPS * 4 + 4 ch + t, stored at that piece ^ r;
+    // when a superchunk spans 16 pieces (int4) the XOR touches only the
+    // 4 ch + t part, so the address is aoff[ch] + cc * 256 + mt * 16 * PP * 16
+    // bytes
+    constexpr bool kFixedA = CPS * 4 == 16;
+    uint32_t aoff[CPS];
+#pragma unroll
+    for (int ch = 0; ch < CPS; ++ch) aoff[ch] = (uint32_t)(r * PP + ((4 * ch + t) ^ r)) * 16u;
     // 4-element output stores need rows aligned to 4 elements
     constexpr int OSZ = OUT == F32 ? 4 : 2;
     const bool vec16 = ((uintptr_t)y & (4 * OSZ - 1)) == 0 && (ldy & 3) == 0;
@@ -1065,11 +1077,17 @@ __global__ __launch_bounds__(64 * xres_waves<NT_>(), 1) void mfma_xres_kernel(
                 // tile mt are issued before the scale FMAs of tile mt - 1 read
                 // their results, so the chains' latency is hidden
                 auto read_a = [&](int mt, h8 (&a)[CPG]) {
-                    const int m = 16 * mt + r;
 #pragma unroll
                     for (int jj = 0; jj < CPG; ++jj) {
-                        const int pc = cc * (SPAN / 8) + 4 * (g * CPG + jj) + t;
-                        a[jj] = __builtin_bit_cast(h8, xs[m * P + (pc ^ (m & msk))]);
+                        if constexpr (kFixedA) {
+                            const uint32_t off = aoff[g * CPG + jj] + (uint32_t)cc * 256u +
+                                                 (uint32_t)mt * (16 * PP * 16);
+                            a[jj] = __builtin_bit_cast(h8, *(const uint4*)((const char*)xs + off));
+                        } else {
+                            const int m = 16 * mt + r;
+                            const int pc = cc * (SPAN / 8) + 4 * (g * CPG + jj) + t;
+                            a[jj] = __builtin_bit_cast(h8, xs[m * PP + (pc ^ r)]);
+                        }
                     }
                 };
                 f4 pq[2][NT];
