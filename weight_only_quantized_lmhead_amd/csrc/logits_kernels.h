@@ -174,7 +174,8 @@ __device__ __forceinline__ void store4(YT<OUT>* p, f4 v) {
 // TK (top-K epilogue, fp32 logits): the wave that holds a block's final 64
 // logits of activation row m also writes that block's T largest as a sorted
 // list of order codes (value descending, then index ascending; see
-// topk_code) to lists[(m*NB + blk)*T ...]: each lane ranks its own code
+// topk_code), entry j at lists[(m*T + j)*NB + blk] (entry-major, so that the
+// merge reads the lists' heads as one contiguous run): each lane ranks its own code
 // against the 64 codes of the wave (read lane by lane into scalar
 // registers), and the lanes of rank < T store.  Rows past V take codes below
 // every real entry.  y may then be null (logits not stored).
@@ -367,8 +368,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint4* __restrict__ wq,
                                (uint32_t)__builtin_amdgcn_readlane((int)clo, j);
                 rank += cj > c;
             }
-            u64* o = lists + ((int64_t)m * NB + blk) * T;
-            if (rank < T) o[rank] = c;
+            if (rank < T) lists[((int64_t)m * T + rank) * NB + blk] = c;
         }
     }
 }

@@ -388,7 +388,8 @@ struct MergeShared {
 };
 
 // The top T of C <= 4096 sorted lists of T codes into sh.s.sel, sorted (see
-// the header).  Thread i owns lists i, i + 256, ...  Ends with a barrier.
+// the header).  The lists are stored entry-major: entry j of list l at
+// L[j*C + l].  Thread i owns lists i, i + 256, ...  Ends with a barrier.
 __device__ __forceinline__ void merge_lists(const u64* __restrict__ L, int C, int T,
                                             MergeShared& sh) {
     const int tid = threadIdx.x, wv = tid >> 6;
@@ -397,7 +398,7 @@ __device__ __forceinline__ void merge_lists(const u64* __restrict__ L, int C, in
 #pragma unroll
     for (int i = 0; i < kMergeLPT; ++i) {
         const int l = tid + 256 * i;
-        hd[i] = l < C ? L[(int64_t)l * T] : 0;
+        hd[i] = l < C ? L[l] : 0;
         tmax = hd[i] > tmax ? hd[i] : tmax;
     }
     sh.s.heads[tid] = tmax;
@@ -444,7 +445,7 @@ __device__ __forceinline__ void merge_lists(const u64* __restrict__ L, int C, in
     for (int e = tid; e < nq * T; e += 256) {
         const int q = e / T;
         if (sh.qh[q] >= thr2) {
-            const u64 c = L[(int64_t)sh.ql[q] * T + (e - q * T)];
+            const u64 c = L[(int64_t)(e - q * T) * C + sh.ql[q]];
             if (c != 0 && c >= thr2) sh.s.cs[atomicAdd(&sh.s.cnt, 1)] = c;
         }
     }
