@@ -383,15 +383,10 @@ def main() -> int:
         return a_.elapsed_time(b_) / n * 1e3  # us per call
 
     def auto_kernel(M):
-        # the library's automatic choice (lmhead_logits)
-        if M <= 2 and M * w.K <= 32768:
-            return "gemv"
-        if M > 32 and w.K <= 1024 and w.group >= 64:
-            return "mfma_xres"
-        narrow = w.K <= 1024
-        if (M > 16 or w.bits == 8) if narrow else not (24 < M <= 32):
-            return "mfma_lds"
-        return "mfma"
+        # the library's automatic choice (lmhead_logits), as the library reports it
+        names = {lmh.PATH_GEMV: "gemv", lmh.PATH_MFMA: "mfma", lmh.PATH_MFMA_LDS: "mfma_lds",
+                 lmh.PATH_MFMA_XRES: "mfma_xres"}
+        return names[lmh.auto_path(M, w.K, w.bits, w.group)]
 
     per_call = {}
     for M in Ms:

@@ -304,6 +304,17 @@ int lmhead_logits_path(const void* x, int x_dtype, int64_t M, const void* packed
                        void* stream);
 
 /*
+ * lmhead_logits_auto_path -- the kernel lmhead_logits (path 0) runs for a
+ *   head of the given shape, as a lmhead_logits_path number (1..4), in *path.
+ *   Host only: no device work, no GPU needed.  M >= 1; K, bits (4 or 8,
+ *   optionally | LMH_ZP) and group as for lmhead_logits.  Returns LMH_OK,
+ *   LMH_E_NULL (path NULL), LMH_E_SHAPE or LMH_E_UNSUPPORTED (invalid shape
+ *   or width, as lmhead_logits would report); *path is written only on
+ *   LMH_OK.  The choice depends on M, K, the code width and G only.
+ */
+int lmhead_logits_auto_path(int64_t M, int64_t K, int bits, int64_t group, int* path);
+
+/*
  * lmhead_logits_typed -- lmhead_logits_path with the output type chosen by
  *   the caller: y_dtype LMH_F32 (exactly lmhead_logits_path), LMH_F16 or
  *   LMH_BF16.  The arithmetic is unchanged; the final fp32 value (after the

@@ -294,3 +294,40 @@ def test_zero_point_validation():
     assert _logits(bits=3 | ZP) == E_UNSUP
     assert _logits(bits=4 | ZP, path=5) == E_UNSUP
     assert L.lmhead_embed(P, 0, P, 128, 128, 4 | ZP, 64, F16, P, F16, 128, None) == OK
+
+
+def _auto(M, K=1024, bits=4, G=64):
+    out = ctypes.c_int(-1)
+    rc = lmh.lib().lmhead_logits_auto_path(M, K, bits, G, ctypes.byref(out))
+    return rc, out.value
+
+
+def test_auto_path_choice():
+    # the automatic kernel choice, host only: the GEMV for one or two rows, the
+    # activation-resident kernel beyond 32 rows when the tile fits (K <= 1024,
+    # G >= 64), the LDS-staged kernel for 17..32 rows and for int8 heads, and
+    # the register-fed kernel for 3..16 rows of an int4 head
+    GEMV, MFMA, LDS, XRES = (lmh.PATH_GEMV, lmh.PATH_MFMA, lmh.PATH_MFMA_LDS,
+                             lmh.PATH_MFMA_XRES)
+    for M, want in [(1, GEMV), (2, GEMV), (3, MFMA), (16, MFMA), (17, LDS), (32, LDS),
+                    (33, XRES), (64, XRES), (256, XRES), (65535, XRES)]:
+        assert _auto(M) == (OK, want), M
+    for M, want in [(1, GEMV), (2, GEMV), (3, LDS), (32, LDS), (33, XRES), (256, XRES)]:
+        assert _auto(M, bits=8, G=128) == (OK, want), M
+    assert _auto(256, G=32) == (OK, LDS)              # 32-column groups: no resident tile
+    assert _auto(256, K=2048) == (OK, LDS)            # the 64-row tile of K > 1024 exceeds LDS
+    for M, want in [(2, GEMV), (3, LDS), (24, LDS), (25, MFMA), (32, MFMA), (33, LDS)]:
+        assert _auto(M, K=5120, G=128) == (OK, want), M
+    assert _auto(2, K=32768, G=128) == (OK, LDS)       # 2 x 32768 halves exceed the GEMV's LDS
+    assert _auto(1, bits=4 | lmh.ZP) == (OK, GEMV)     # zero-point heads choose alike
+    assert _auto(64, bits=8 | lmh.ZP, G=128) == (OK, XRES)
+    assert lmh.auto_path(256, 1024, 4, 64) == XRES
+
+
+def test_auto_path_validation():
+    assert _auto(0) == (E_SHAPE, -1)
+    assert _auto(65536) == (E_SHAPE, -1)
+    assert _auto(1, bits=3) == (E_UNSUP, -1)
+    assert _auto(1, K=192) == (E_SHAPE, -1)
+    assert _auto(1, K=384, G=96) == (E_UNSUP, -1)
+    assert lmh.lib().lmhead_logits_auto_path(1, 1024, 4, 64, None) == E_NULL

@@ -68,6 +68,7 @@ def lib() -> ctypes.CDLL:
                                          vp, sz, i32, vp]),
             "lmhead_logits_typed": (i32, [vp, i32, i64, vp, i64, i64, i32, i64, i32, vp, vp, i32, i64,
                                           vp, sz, i32, vp]),
+            "lmhead_logits_auto_path": (i32, [i64, i64, i32, i64, vp]),
             "lmhead_dense_logits": (i32, [vp, i32, i64, vp, i32, i64, i64, vp, i64, vp]),
             "lmhead_topk_workspace_bytes": (sz, [i64, i64, i32]),
             "lmhead_topk_rescore": (i32, [vp, i32, i64, vp, i32, i64, i64, vp, i64, i32, vp, vp,
@@ -225,6 +226,14 @@ def embed(ids: torch.Tensor, packed: torch.Tensor, V: int, K: int, bits: int, gr
         _ptr(ids), T, _ptr(packed), V, K, bits, group, _DT[scale_dtype], _ptr(out), _DT[out.dtype],
         out.stride(0), _stream(packed)))
     return out
+
+
+def auto_path(M: int, K: int, bits: int, group: int) -> int:
+    """The kernel lmhead_logits runs for this shape (PATH_GEMV .. PATH_MFMA_XRES); host only."""
+    out = ctypes.c_int(0)
+    _check("lmhead_logits_auto_path",
+           lib().lmhead_logits_auto_path(M, K, bits, group, ctypes.byref(out)))
+    return out.value
 
 
 def logits_workspace(M: int, K: int, x_dtype: torch.dtype, device) -> Optional[torch.Tensor]:

@@ -174,6 +174,33 @@ size_t lmhead_logits_workspace_bytes(int64_t M, int64_t K, int x_dtype) {
 
 // `lists` (internal, lmhead_logits_topk's fused path): the GEMV also writes
 // per-block top-`list_T` lists there, and y may be null.
+//
+// The automatic kernel choice (path 0), from sweeps over M = 2..256 on the
+// 151936 x 1024 int4 g64 and int8 g128 heads and the 248064 x 5120 int4 g128
+// head:
+//   - the GEMV for one or two activation rows (at M = 2 against the best MFMA
+//     kernel: int4 K = 1024 20.3 vs 20.8 us, int4 K = 5120 133 vs 141 us,
+//     int8 K = 1024 29.5 vs 31.6 us);
+//   - when K <= 1024 and G >= 64, the activation-resident kernel from 33
+//     rows on (int4 M = 33..64: 29-33 us against 38-42 for the LDS-staged
+//     kernel's 64-row tiles; M = 96..256 6-10 % faster; int8 M = 40..256:
+//     0-14 % faster; with 32-column groups it runs out of registers);
+//   - when K <= 1024: the LDS-staged kernel for 17..32 rows (int4: 25-28
+//     us against 30-32 activation-resident) and for every M >= 3 on int8
+//     heads (int8 2..32 rows: 15-25 % faster than activation-resident),
+//     else the register-fed kernel (3..16 rows on int4 heads; the
+//     LDS-staged one is 4-6 % slower there);
+//   - when K > 1024: the register-fed kernel for 25..32 rows (3 % faster),
+//     else the LDS-staged one (3..24 rows: 1.5-3 % faster; beyond 32 rows
+//     the register-fed kernel would read the weights once per 32 rows).
+static int auto_path(int64_t M, int64_t K, int bits, int64_t group) {
+    if (M <= lmh::kGemvAutoMaxM && M <= lmh::kGemvMaxM && M * K <= lmh::kGemvMaxMK) return 1;
+    if (M > 32 && lmh::xres_fits(K) && group >= 64) return 4;
+    const bool narrow = K <= 1024;
+    const bool lds = narrow ? (M > 16 || bits == 8) : !(M > 24 && M <= 32);
+    return lds ? 3 : 2;
+}
+
 static int logits_impl(const void* x, int x_dtype, int64_t M, const void* packed, int64_t V,
                        int64_t K, int bits_arg, int64_t group, int scale_dtype, const float* bias,
                        void* y, int y_dtype, int64_t ldy, void* workspace, size_t ws_bytes,
@@ -230,31 +257,20 @@ static int logits_impl(const void* x, int x_dtype, int64_t M, const void* packed
     a.zp = wd.zp;
     a.lists = lists;
     a.list_T = list_T;
-    // the GEMV for one or two activation rows (measured at M = 2 against the
-    // best MFMA kernel: int4 K = 1024 20.3 vs 20.8 us, int4 K = 5120 133 vs
-    // 141 us, int8 K = 1024 29.5 vs 31.6 us)
-    const bool use_gemv = path == 1 || (path == 0 && gemv_ok && M <= lmh::kGemvAutoMaxM);
-    if (use_gemv) return from_hip(lmh::launch_gemv(a, st));
-    // automatic, from sweeps over M = 2..256 on the 151936 x 1024 int4 g64
-    // and int8 g128 heads and the 248064 x 5120 int4 g128 head:
-    //   - when K <= 1024 and G >= 64, the activation-resident kernel from 33
-    //     rows on (int4 M = 33..64: 29-33 us against 38-42 for the LDS-staged
-    //     kernel's 64-row tiles; M = 96..256 6-10 % faster; int8 M = 40..256:
-    //     0-14 % faster; with 32-column groups it runs out of registers);
-    //   - when K <= 1024: the LDS-staged kernel for 17..32 rows (int4: 25-28
-    //     us against 30-32 activation-resident) and for every M >= 3 on int8
-    //     heads (int8 2..32 rows: 15-25 % faster than activation-resident),
-    //     else the register-fed kernel (3..16 rows on int4 heads; the
-    //     LDS-staged one is 4-6 % slower there);
-    //   - when K > 1024: the register-fed kernel for 25..32 rows (3 % faster),
-    //     else the LDS-staged one (3..24 rows: 1.5-3 % faster; beyond 32 rows
-    //     the register-fed kernel would read the weights once per 32 rows).
-    const bool use_xres = path == 4 || (path == 0 && M > 32 && lmh::xres_fits(K) && group >= 64);
-    if (use_xres) return from_hip(lmh::launch_mfma_xres(a, st));
-    const bool narrow = K <= 1024;
-    const bool use_lds = path == 3 || (path == 0 && (narrow ? (M > 16 || bits == 8)
-                                                            : !(M > 24 && M <= 32)));
-    return from_hip(use_lds ? lmh::launch_mfma_lds(a, st) : lmh::launch_mfma(a, st));
+    if (path == 0) path = auto_path(M, K, bits, group);
+    if (path == 1) return from_hip(lmh::launch_gemv(a, st));
+    if (path == 4) return from_hip(lmh::launch_mfma_xres(a, st));
+    return from_hip(path == 3 ? lmh::launch_mfma_lds(a, st) : lmh::launch_mfma(a, st));
+}
+
+int lmhead_logits_auto_path(int64_t M, int64_t K, int bits_arg, int64_t group, int* path) {
+    if (!path) return LMH_E_NULL;
+    const Width wd = width_of(bits_arg);
+    const int rc = check_layout(1, K, wd.bits, group);
+    if (rc != LMH_OK) return rc;
+    if (M < 1 || M > 65535) return LMH_E_SHAPE;
+    *path = auto_path(M, K, wd.bits, group);
+    return LMH_OK;
 }
 
 int lmhead_logits(const void* x, int x_dtype, int64_t M, const void* packed, int64_t V, int64_t K,
