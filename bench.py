@@ -452,6 +452,18 @@ def main() -> int:
         "traffic_source": os.path.relpath(traffic_file(w.name), ROOT) if tr else None,
     }
 
+    # a practical ceiling beside the 8 TB/s figure: a device-to-device copy of
+    # one packed head between the rotating copies (identical contents), bytes
+    # read + written per copy over its time
+    if R >= 2:
+        def copy_loop(i):
+            blobs[(i + 1) % R].copy_(blobs[i % R])
+
+        t_copy = timed_loop(copy_loop, 50)
+        copy_gbs = 2.0 * blob_bytes / (t_copy * 1e-6) / 1e9
+        roofline["copy_GBps"] = round(copy_gbs, 1)
+        roofline["frac_of_copy"] = round(m1["GB/s"] / copy_gbs, 4)
+
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
