@@ -942,13 +942,14 @@ __device__ __forceinline__ void wait_vm_all() {
 template <int NT_>
 constexpr int xres_waves() { return NT_ == 4 ? 8 : 16; }
 
-template <int BITS, int GPS, int D, bool TR, int OUT, bool ZP, int NT_>
+// SB: the scale type as a template flag (0 fp16, 1 bf16), so that the per-step
+// scale conversion is one instruction per scale and carries no select.
+template <int BITS, int GPS, int D, bool TR, int OUT, bool ZP, int NT_, int SB>
 __global__ __launch_bounds__(64 * xres_waves<NT_>(), 1) void mfma_xres_kernel(
     const uint4* __restrict__ wq, const uint16_t* __restrict__ sc, const uint8_t* __restrict__ zq,
     const _Float16* __restrict__ x,
     const int* __restrict__ xexp, const float* __restrict__ bias, void* __restrict__ y,
-    int64_t ldy, int V, int K, int M, int NB, int NC, int NG, int SPG, int sbf16, int NMT,
-    int VRX) {
+    int64_t ldy, int V, int K, int M, int NB, int NC, int NG, int SPG, int NMT, int VRX) {
     constexpr int MT = 4, NT = NT_, ROWS = 64;
     constexpr int WAVES = xres_waves<NT_>(), NTH = 64 * WAVES;
     constexpr int PARTS = 4 / NT;  // a row block's 64 columns in PARTS units of 16 NT
@@ -1063,13 +1064,13 @@ __global__ __launch_bounds__(64 * xres_waves<NT_>(), 1) void mfma_xres_kernel(
                     }
                     if constexpr (TR) {
                         const uint2 sw = sbuf[p][g][nt];
-                        sv[nt] = real ? (f4){scale_to_f32((uint16_t)sw.x, sbf16),
-                                             scale_to_f32((uint16_t)(sw.x >> 16), sbf16),
-                                             scale_to_f32((uint16_t)sw.y, sbf16),
-                                             scale_to_f32((uint16_t)(sw.y >> 16), sbf16)}
+                        sv[nt] = real ? (f4){scale_to_f32((uint16_t)sw.x, SB),
+                                             scale_to_f32((uint16_t)(sw.x >> 16), SB),
+                                             scale_to_f32((uint16_t)sw.y, SB),
+                                             scale_to_f32((uint16_t)(sw.y >> 16), SB)}
                                       : (f4){0.f, 0.f, 0.f, 0.f};
                     } else {
-                        const float v1 = real ? scale_to_f32(sbuf[p][g][nt], sbf16) : 0.0f;
+                        const float v1 = real ? scale_to_f32(sbuf[p][g][nt], SB) : 0.0f;
                         sv[nt] = (f4){v1, v1, v1, v1};
                     }
                 }
@@ -1418,17 +1419,23 @@ hipError_t mfma_xres_dispatch_d(const LogitsArgs& a, hipStream_t st) {
     // one workgroup per CU: per XCD, NMT activation tiles x VRX vocabulary ranges
     const int VRX = NMT >= 32 ? 1 : 32 / NMT;
     const dim3 grid((unsigned)(8 * NMT * VRX));
-#define LMH_XRES(G_)                                                                              \
-    hipLaunchKernelGGL((mfma_xres_kernel<BITS, G_, D, TR, OUT, ZP, NT_>), grid,                  \
+#define LMH_XRES_SB(G_, SB_)                                                                      \
+    hipLaunchKernelGGL((mfma_xres_kernel<BITS, G_, D, TR, OUT, ZP, NT_, SB_>), grid,             \
                        dim3(64 * xres_waves<NT_>()), 0, st,                                       \
                        rg.wq, rg.sc, rg.zq,                                                       \
                        (const _Float16*)a.x, a.xexp, a.bias, a.y, a.ldy, (int)a.V, (int)a.K, a.M, \
-                       NB, NC, NG, SPG, a.scale_bf16, NMT, VRX)
+                       NB, NC, NG, SPG, NMT, VRX)
+#define LMH_XRES(G_)                                                                              \
+    do {                                                                                          \
+        if (a.scale_bf16) LMH_XRES_SB(G_, 1);                                                     \
+        else LMH_XRES_SB(G_, 0);                                                                  \
+    } while (0)
     if (gps == 1) LMH_XRES(1);
     else if constexpr (BITS == 8) LMH_XRES(2);
     else if (gps == 2) LMH_XRES(2);
     else LMH_XRES(4);
 #undef LMH_XRES
+#undef LMH_XRES_SB
     return hipGetLastError();
 }
 
