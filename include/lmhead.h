@@ -347,8 +347,8 @@ size_t lmhead_topk_workspace_bytes(int64_t M, int64_t V, int topk);
 
 /*
  * lmhead_topk_rescore -- exact rescoring of the top-K quantized logits (vLLM
- *   PR #48870, review comment, point 2: take the top-K of the quantized logits,
- *   recompute those K rows exactly from the unquantized weight, scatter back).
+ *   PR #48870, review comment, point 2: the K largest quantized logits of a row
+ *   are overwritten by exact dot products with the unquantized weight rows).
  *   For each row m of y [M, ldy] (fp32, in/out):
  *     I = the topk largest of y[m, 0..V), ordered by value descending, then
  *         index ascending;

@@ -11,16 +11,18 @@ The arithmetic lives in ``lmh_oracle.c`` (plain C, built with
 marshals numpy arrays.  Every function states which passage it follows:
 
 * quantize   -- page "radiance_lmhead_int4.py", docstring "How" paragraph
-                (per-group bf16 scale, symmetric q in [-8, 7], clip-ratio search
-                1.0 .. 0.8 x amax/7 by least squared error, scale rounded before
-                q), module constants (CLIP_RATIOS, QMAX, ZP_BIAS) and
+                (one bf16 scale per group; codes -8..7; the clip ratio that
+                gives the smallest squared error among five, from 1.0 down to
+                0.8; the scale is rounded to bf16 before the codes are
+                picked), module constants (CLIP_RATIOS, QMAX, ZP_BIAS) and
                 ``quantize_int4_rows``;  int8 per the W8-g128 rows of the table
                 on vLLM PR #48870 and the int8 per-row head of its review comment.
 * logits     -- vLLM PR #48870, Purpose: a fused dequant-GEMM gives the logits of
                 dequantize-then-F.linear without forming the dense weight.
 * dense      -- vLLM PR #48870, review comment point 1 (the fp16 logits GEMV).
-* topk_rescore -- vLLM PR #48870, review comment point 2 (take top-K of the
-                quantized logits, recompute those K rows exactly, scatter back).
+* topk_rescore -- vLLM PR #48870, review comment point 2 (the K largest
+                quantized logits of a row are replaced by exact dot products
+                with the unquantized weight rows they index).
 
 Parity pins for each function are in ``tests/test_oracle_*.py``.
 """

@@ -2,8 +2,8 @@
 //
 // vLLM PR #48870 ("Fused WNA16 GEMM for tied quantized lm_head logits",
 // Purpose and perf table): the logits come straight from the packed codes and
-// scales; the dense weight is never formed.  Its review comment (point 1)
-// notes that M = 1 is purely bandwidth-bound: the only lever is bytes moved.
+// scales; the dense weight is never formed.  Review comment, point 1: at one
+// activation row the kernel's time is set by the bytes it reads from HBM.
 //
 // Codes are unpacked exactly into fp16 in registers with the exponent trick:
 // OR-ing a nibble n into the fp16 pattern 0x6400 gives 1024 + n, so one

@@ -1,9 +1,8 @@
 // Top-K selection of the quantized logits and exact rescoring of those rows.
 //
-// vLLM PR #48870, review comment, point 2: take the top-K of the quantized
-// logits, recompute those K rows exactly from the unquantized weight, and
-// scatter the exact values back (K = 8 costs 32 KB of weight reads next to a
-// 311 MB int8 head).
+// vLLM PR #48870, review comment, point 2: the K best quantized logits of a
+// row are replaced by exact dot products with the 16-bit weight rows they
+// index; with K = 8 those rows are 32 KB against the 311 MB int8 head.
 //
 // Order: value descending, then index ascending (a total order, so the
 // selection is unique and deterministic).  -0 and +0 count as equal, as in a
