@@ -170,21 +170,65 @@ def widen16(bits: np.ndarray, dtype: int) -> np.ndarray:
 
 # ---- quantizer ----------------------------------------------------------------
 
+def default_threads() -> int:
+    """Host threads the oracle's row-parallel calls use: the cores this process
+    may run on, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _row_ranges(n: int, threads: Optional[int]):
+    """Contiguous row ranges for the worker threads (none shorter than 64 rows)."""
+    t = default_threads() if threads is None else max(1, int(threads))
+    t = max(1, min(t, n // 64 if n >= 64 else 1))
+    edges = [n * i // t for i in range(t + 1)]
+    return [(edges[i], edges[i + 1]) for i in range(t) if edges[i + 1] > edges[i]]
+
+
+def _parallel(fn, ranges):
+    """Run fn(lo, hi) for every range on its own thread.  The C calls release
+    the GIL (ctypes), so the ranges run side by side; every row's arithmetic is
+    the same as in one call over all rows."""
+    if len(ranges) <= 1:
+        return [fn(lo, hi) for lo, hi in ranges]
+    from concurrent.futures import ThreadPoolExecutor
+
+    with ThreadPoolExecutor(max_workers=len(ranges)) as ex:
+        return list(ex.map(lambda r: fn(*r), ranges))
+
+
 def quantize(w: np.ndarray, bits: int, group: int, scale_dtype: int,
              ratios: Sequence[float] = RTN_RATIOS, w_dtype: Optional[int] = None,
-             return_pick: bool = False):
+             return_pick: bool = False, threads: Optional[int] = None):
     """(q int8 [V,K], s uint16 [V,K/G]) per the page's quantize_int4_rows, generalised
-    to int8 (qmax 127, qmin -128) and fp16/bf16 scales; readings R1-R4, R7."""
+    to int8 (qmax 127, qmin -128) and fp16/bf16 scales; readings R1-R4, R7.
+    Rows are quantized independently, so `threads` (default: the host's cores,
+    at most 16) only splits the rows into ranges run side by side."""
     w = np.ascontiguousarray(w)
     V, K = w.shape
     wd = _dtype_code(w, w_dtype)
+    if group <= 0 or K % group != 0:
+        raise ValueError("oracle quantize: bad arguments (K not a multiple of G)")
+    NG = K // group
     q = np.empty((V, K), dtype=np.int8)
-    s = np.empty((V, K // group), dtype=np.uint16)
-    pick = np.empty((V, K // group), dtype=np.int8)
+    s = np.empty((V, NG), dtype=np.uint16)
+    pick = np.empty((V, NG), dtype=np.int8)
     r = np.ascontiguousarray(np.array(ratios, dtype=np.float64))
-    rc = _load().orc_quantize(_ptr(w), wd, V, K, bits, group, scale_dtype, _ptr(r), len(r),
-                              _ptr(q), _ptr(s), _ptr(pick))
-    _check(rc, "quantize")
+    isz = w.itemsize
+
+    def run(lo, hi):
+        return _load().orc_quantize(_ptr(w) + lo * K * isz, wd, hi - lo, K, bits, group,
+                                    scale_dtype, _ptr(r), len(r), _ptr(q) + lo * K,
+                                    _ptr(s) + lo * NG * 2, _ptr(pick) + lo * NG)
+
+    rcs = _parallel(run, _row_ranges(V, threads)) if V else [
+        _load().orc_quantize(_ptr(w), wd, 0, K, bits, group, scale_dtype, _ptr(r), len(r),
+                             _ptr(q), _ptr(s), _ptr(pick))]
+    for rc in rcs:
+        _check(rc, "quantize")
     return (q, s, pick) if return_pick else (q, s)
 
 
@@ -224,23 +268,37 @@ def _rows_arg(rows, V):
 
 
 def logits(x: np.ndarray, q: np.ndarray, s: np.ndarray, scale_dtype: int, group: int,
-           bias: Optional[np.ndarray] = None, rows=None, x_dtype: Optional[int] = None) -> np.ndarray:
-    """fp64 y[M, rows] = x * dequant(q, s)^T (+ bias), exact products, fp64 sums."""
+           bias: Optional[np.ndarray] = None, rows=None, x_dtype: Optional[int] = None,
+           threads: Optional[int] = None) -> np.ndarray:
+    """fp64 y[M, rows] = x * dequant(q, s)^T (+ bias), exact products, fp64 sums.
+    Each output element is one sequential sum over k; `threads` (default: the
+    host's cores, at most 16) only splits the rows into ranges run side by side."""
     x = np.ascontiguousarray(x)
     q = np.ascontiguousarray(q, dtype=np.int8)
     s = np.ascontiguousarray(s, dtype=np.uint16)
     M, K = x.shape
     V = q.shape[0]
     r, n, rp = _rows_arg(rows, V)
-    y = np.empty((M, n), dtype=np.float64)
     bp = 0
     if bias is not None:
         bias = np.ascontiguousarray(bias, dtype=np.float32)
         bp = _ptr(bias)
-    rc = _load().orc_logits(_ptr(x), _dtype_code(x, x_dtype), M, _ptr(q), _ptr(s), scale_dtype,
-                            V, K, group, bp or None, rp or None, n, _ptr(y))
-    _check(rc, "logits")
-    return y
+    xd = _dtype_code(x, x_dtype)
+    if r is None:
+        r = np.arange(V, dtype=np.int64)
+
+    def run(lo, hi):
+        rr = np.ascontiguousarray(r[lo:hi])
+        y = np.empty((M, hi - lo), dtype=np.float64)
+        rc = _load().orc_logits(_ptr(x), xd, M, _ptr(q), _ptr(s), scale_dtype, V, K, group,
+                                bp or None, _ptr(rr) if hi > lo else None, hi - lo, _ptr(y))
+        _check(rc, "logits")
+        return y
+
+    parts = _parallel(run, _row_ranges(n, threads)) if n else []
+    if not parts:
+        return np.empty((M, 0), dtype=np.float64)
+    return parts[0] if len(parts) == 1 else np.concatenate(parts, axis=1)
 
 
 def embed(q: np.ndarray, s: np.ndarray, scale_dtype: int, group: int, ids,
