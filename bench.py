@@ -4,23 +4,26 @@
 One step = one pass of the per-call hot path over one batch of synthetic input
 on the 151936 x 1024 int4 g64 fp16-scale head at the decode shape: the logits
 at M = 1 and top-8 exact rescoring, in one call (lmhead_logits_topk).  The K
-timed steps give `ms_per_step`.  Each call (logits at M = 1, 32 and 256, the
-separate rescoring, the single logits + rescoring call) is then also timed
-on its own as K back-to-back
-calls between two HIP events, as the metric asks ("each timed separately");
-those give `per_call` and `value`.
-The load-time quantize and pack run once before the timed region and are
-reported separately.
+timed steps give `ms_per_step`.  Each call (logits at every M of the workload,
+16-bit output, the zero-point form, the separate rescoring, the one-call
+decode path, the embedding gather, the unquantized 16-bit control GEMV) is
+then also timed on its own (the metric: "each timed separately"): at least
+200 back-to-back calls between two HIP events (`us`), and the same calls
+replayed from a HIP graph (`us_graph`, no host work between kernels).  All
+calls are prepared once (lmh.PreparedCall), so the host issues them faster
+than the GPU runs them.  The load-time quantize and pack run once before the
+timed region and are reported separately.
 
-Inputs are resident in HBM before timing starts.  Each step reads a different
+Inputs are resident in HBM before timing starts.  Each call reads a different
 copy of the packed head (R copies, >= 1 GB in total) so the 256 MB last-level
 cache cannot serve the weights: the numbers are cold/HBM numbers.
 
 Prints ONE JSON line.  `value` is the mean time of the M = 1 logits call in
 microseconds (lower is better); `per_call` has every call's time, GB/s and
-roofline fraction; `roofline` is the M = 1 kernel's achieved algorithmic bandwidth
-(measured with HIP events on the stream the library launches on) against the
-8 TB/s HBM peak; `cpu_baseline` times the fp64 oracle on the host.
+roofline fraction; `roofline` is the M = 1 kernel's achieved algorithmic
+bandwidth (HIP events on the stream the calls run on) against the 8 TB/s HBM
+peak, with the read-only ceiling measured in the same run (lmhead_stream_read
+over the same bytes); `cpu_baseline` times the fp64 oracle on the host cores.
 """
 from __future__ import annotations
 
@@ -222,22 +225,94 @@ def decode_agreement(args, w, lmh, synth, to_dev, blob, Wref, sdt, dev):
             "topk_set_overlap": round(overlap, 6)}
 
 
+def cpu_oracle_baseline(w, W, Ms, synth, np, budget_s):
+    """The fp64 oracle on the host cores: logits at the first M (one thread and
+    all cores, median of 3) and the quantizer (RTN and MSE clip search, all
+    cores), each on a bounded row sample scaled to the whole head."""
+    import platform
+    import statistics
+
+    import oracle
+
+    od = {"f16": oracle.F16, "bf16": oracle.BF16, "f32": oracle.F32}
+    ratios = oracle.MSE_RATIOS if w.clip == "mse" else oracle.RTN_RATIOS
+    threads = oracle.default_threads()
+    cpu_model = platform.processor() or ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+
+    def med3(fn):
+        ts = []
+        for _ in range(3):
+            c0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - c0)
+        return statistics.median(ts)
+
+    # row samples sized from a probe so that each measurement takes ~budget/8
+    x1 = synth.activations(w, Ms[0])
+    probe = np.ascontiguousarray(W[: min(w.V, 2048)])
+    qp, sp = oracle.quantize(probe, w.bits, w.group, od[w.scale_dtype], ratios, w_dtype=od[w.w_dtype])
+    t_probe = med3(lambda: oracle.logits(x1, qp, sp, od[w.scale_dtype], w.group,
+                                        x_dtype=od[w.x_dtype], threads=1))
+    per_row = t_probe / probe.shape[0]
+    n_rows = int(min(w.V, max(2048, budget_s / 8 / max(per_row, 1e-9))))
+    step = max(1, w.V // n_rows)
+    rows = np.arange(0, w.V, step)
+    Wr = np.ascontiguousarray(W[rows])
+    frac = len(rows) / w.V
+    qo, so = oracle.quantize(Wr, w.bits, w.group, od[w.scale_dtype], ratios, w_dtype=od[w.w_dtype])
+    t1 = med3(lambda: oracle.logits(x1, qo, so, od[w.scale_dtype], w.group, x_dtype=od[w.x_dtype],
+                                    threads=1))
+    tn = med3(lambda: oracle.logits(x1, qo, so, od[w.scale_dtype], w.group, x_dtype=od[w.x_dtype],
+                                    threads=threads))
+    # the quantizer on a smaller sample (RTN; the 5-ratio search)
+    qrows = rows[:: max(1, len(rows) // 4096)] if len(rows) > 4096 else rows
+    Wq = np.ascontiguousarray(W[qrows])
+    qfrac = len(qrows) / w.V
+    t_rtn = med3(lambda: oracle.quantize(Wq, w.bits, w.group, od[w.scale_dtype], oracle.RTN_RATIOS,
+                                         w_dtype=od[w.w_dtype], threads=threads))
+    t_mse = med3(lambda: oracle.quantize(Wq, w.bits, w.group, od[w.scale_dtype], oracle.MSE_RATIOS,
+                                         w_dtype=od[w.w_dtype], threads=threads))
+    return {"value": round(tn / frac * 1e6, 1), "unit": "us/call", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"fp64 oracle logits, M={Ms[0]}, every {step}th of the {w.V} rows "
+                       f"({len(rows)} rows), median of 3 runs on {threads} threads (row ranges "
+                       f"side by side), scaled to one whole call"),
+            "single_thread_us": round(t1 / frac * 1e6, 1),
+            "quantize_rtn_ms": round(t_rtn / qfrac * 1e3, 1),
+            "quantize_mse_ms": round(t_mse / qfrac * 1e3, 1),
+            "quantize_sample": (f"{len(qrows)} rows, median of 3 on {threads} threads, scaled to "
+                                f"the whole head"),
+            "cpu_model": cpu_model, "host_threads_visible": os.cpu_count()}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--calls", type=int, default=200,
+                    help="calls per per-call timing loop (at least 200 whatever --steps is)")
     ap.add_argument("--workload", default=None, help="synthetic workload name (default: the headline)")
     ap.add_argument("--ms", default=None, help="comma-separated M list (default: the workload's)")
     ap.add_argument("--topk", type=int, default=8)
     ap.add_argument("--path", type=int, default=0, help="0 automatic, 1 GEMV, 2 register-fed MFMA, 3 LDS-staged MFMA, 4 activation-resident MFMA")
     ap.add_argument("--hot", action="store_true", help="reuse one copy of the head (cache-hot; labelled)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time only the logits calls of the workload (no 16-bit output, zero-point, "
+                         "top-K, embedding or control entries)")
     ap.add_argument("--agreement", type=int, default=0, metavar="N",
                     help="also report, over N seeded decode states (one activation row each), the "
                          "top-1 agreement with the unquantized 16-bit weight before and after exact "
                          "top-K rescoring, and the top-K set overlap")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=16.0)
     ap.add_argument("--summarize", action="store_true",
                     help="write a profiles/ summary from rocprofv3 CSV files instead of timing")
     ap.add_argument("--stats", help="kernel_stats.csv of a --kernel-trace --stats run")
@@ -269,16 +344,20 @@ def main() -> int:
     Ms = [int(m) for m in args.ms.split(",")] if args.ms else list(w.Ms)
     TD = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
     sdt = TD[w.scale_dtype]
+    ncalls = max(200, args.calls)
 
     def to_dev(a, dt):
         if dt == "bf16":
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
     t0 = time.time()
     W = synth.weight(w)
     Wd = to_dev(W, w.w_dtype)
-    print(f"[bench] {w.name}: weight generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    log(f"{w.name}: weight generated in {time.time() - t0:.1f}s")
 
     # load-time rows: quantize and pack (one warm-up call each, then one timed call)
     ev = lambda: torch.cuda.Event(enable_timing=True)
@@ -315,8 +394,9 @@ def main() -> int:
     e1.record()
     torch.cuda.synchronize()
     qpz_ms = e0.elapsed_time(e1)
+    log(f"load-time kernels done")
 
-    # unquantized 16-bit reference rows for rescoring
+    # unquantized 16-bit reference rows for rescoring (and the control GEMV)
     if w.w_dtype == "f32":
         Wref = Wd.to(torch.float16)
         del Wd
@@ -325,7 +405,7 @@ def main() -> int:
     blob_bytes = blob.numel()
     R = 1 if args.hot else max(2, math.ceil(1e9 / blob_bytes))
     blobs = [blob] + [blob.clone() for _ in range(R - 1)]
-    zblobs = [zblob] + [zblob.clone() for _ in range(R - 1)]
+    zblobs = [zblob] + [zblob.clone() for _ in range(R - 1)] if not args.no_extras else []
     xs = {M: to_dev(synth.activations(w, M), w.x_dtype) for M in Ms}
     outs = {M: torch.empty((M, w.V), dtype=torch.float32, device=dev) for M in Ms}
     wss = {M: lmh.logits_workspace(M, w.K, TD[w.x_dtype], dev) for M in Ms}
@@ -337,157 +417,172 @@ def main() -> int:
     t_top1 = torch.empty((m_rs,), dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
 
-    m_hd = Ms[0]  # the headline call: the decode case
-
-    def call(M, i):
-        lmh.logits(xs[M], blobs[i % R], w.V, w.K, w.bits, w.group, sdt, out=outs[M], workspace=wss[M],
-                   path=args.path)
-
-    def rescore():
-        lmh.topk_rescore(xs[m_rs], Wref, outs[m_rs], args.topk, workspace=tws)
-
-    def one_call(i):
-        # logits (stored) and exact top-K rescoring in one call
-        lmh.logits_topk(xs[m_rs], blobs[i % R], w.V, w.K, w.bits, w.group, sdt, Wref, args.topk,
-                        out=outs[m_rs], workspace=fws, idx=t_idx, val=t_val, top1=t_top1)
-
-    def step(i):
-        # one pass of the per-call hot path at the headline M: logits, then
-        # exact top-K rescoring (one call)
-        one_call(i)
-
-    # ---- the timed region: K steps, synchronised on both sides ----
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t_start, t_end = ev(), ev()
-    t_start.record()
-    for i in range(args.steps):
-        step(args.warmup + i)
-    t_end.record()
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-
-    # ---- each call timed on its own: K back-to-back calls between two events on
-    # the library's stream (torch's current stream), rotating the head copies ----
-    def timed_loop(fn, n):
+    # Every timed call is a prepared call (arguments converted once, see
+    # lmh.PreparedCall), so the host issues calls faster than the GPU runs
+    # them.  Each entry is timed two ways on the stream the calls are bound
+    # to: `us`, back-to-back calls between two HIP events (rotating the head
+    # copies); `us_graph`, the same calls captured once in a HIP graph and
+    # replayed (no host work at all between kernels).
+    def ev_time(calls, n):
         for i in range(min(args.warmup, n)):
-            fn(i)
+            calls[i % len(calls)]()
         torch.cuda.synchronize()
         a_, b_ = ev(), ev()
         a_.record()
         for i in range(n):
-            fn(i)
+            calls[i % len(calls)]()
         b_.record()
         torch.cuda.synchronize()
-        return a_.elapsed_time(b_) / n * 1e3  # us per call
+        return a_.elapsed_time(b_) / n * 1e3
+
+    def graph_time(make_calls, n):
+        gs = torch.cuda.Stream()
+        with torch.cuda.stream(gs):
+            calls = make_calls()
+            for i in range(min(args.warmup, n)):
+                calls[i % len(calls)]()
+        gs.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=gs):
+            for i in range(n):
+                calls[i % len(calls)]()
+        a_, b_ = ev(), ev()
+        reps = 5
+        with torch.cuda.stream(gs):  # replay() launches on the current stream
+            g.replay()
+            gs.synchronize()
+            a_.record(gs)
+            for _ in range(reps):
+                g.replay()
+            b_.record(gs)
+        gs.synchronize()
+        t_ = a_.elapsed_time(b_) / (reps * n) * 1e3
+        del g
+        return t_
+
+    def both(make_calls):
+        return round(ev_time(make_calls(), ncalls), 3), round(graph_time(make_calls, ncalls), 3)
+
+    def prep_logits(M, bl, bits, out, path=None):
+        return lambda: [lmh.prepare_logits(xs[M], b, w.V, w.K, bits, w.group, sdt, out=out,
+                                           workspace=wss[M], path=args.path if path is None else path)
+                        for b in bl]
+
+    def prep_one_call():
+        return [lmh.prepare_logits_topk(xs[m_rs], b, w.V, w.K, w.bits, w.group, sdt, Wref, args.topk,
+                                        t_idx, t_val, t_top1, out=outs[m_rs], workspace=fws)
+                for b in blobs]
+
+    # ---- the timed region: K steps of the per-call hot path at the decode
+    # shape (logits + top-K rescoring in one call), synchronised on both sides ----
+    steps_calls = prep_one_call()
+    for i in range(args.warmup):
+        steps_calls[i % R]()
+    torch.cuda.synchronize()
+    t_start, t_end = ev(), ev()
+    t_start.record()
+    for i in range(args.steps):
+        steps_calls[(args.warmup + i) % R]()
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    log(f"timed region: {total_ms / args.steps * 1e3:.2f} us per step")
 
     def auto_kernel(M):
-        # the library's automatic choice (lmhead_logits), as the library reports it
         names = {lmh.PATH_GEMV: "gemv", lmh.PATH_MFMA: "mfma", lmh.PATH_MFMA_LDS: "mfma_lds",
                  lmh.PATH_MFMA_XRES: "mfma_xres"}
         return names[lmh.auto_path(M, w.K, w.bits, w.group)]
 
     per_call = {}
     for M in Ms:
-        t_us = timed_loop(lambda i, M=M: call(M, i), args.steps)
+        us, usg = both(prep_logits(M, blobs, w.bits, outs[M]))
         B = algorithmic_bytes(M, w.V, w.K, w.bits, w.group)
         F = 2.0 * M * w.V * w.K
-        gbs = B / (t_us * 1e-6) / 1e9
-        tfl = F / (t_us * 1e-6) / 1e12
+        gbs = B / (us * 1e-6) / 1e9
+        tfl = F / (us * 1e-6) / 1e12
         per_call[f"M={M}"] = {
-            "us": round(t_us, 3),
+            "us": us, "us_graph": usg,
             "kernel": {1: "gemv", 2: "mfma", 3: "mfma_lds", 4: "mfma_xres"}.get(args.path, auto_kernel(M)),
             "algorithmic_bytes": B, "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
             "TFLOP/s": round(tfl, 2), "frac_mfma_f16_peak": round(tfl / MFMA_F16_PEAK_TFLOPS, 4),
         }
-    # 16-bit logits (fp16 output: half the output bytes) at every M > 1
-    for M in Ms:
-        if M == 1:
-            continue
-        o16 = torch.empty((M, w.V), dtype=torch.float16, device=dev)
-        t_us = timed_loop(lambda i, M=M, o16=o16: lmh.logits(
-            xs[M], blobs[i % R], w.V, w.K, w.bits, w.group, sdt, out=o16, workspace=wss[M],
-            path=args.path), args.steps)
-        B = algorithmic_bytes(M, w.V, w.K, w.bits, w.group) - M * w.V * 2
-        per_call[f"M={M} y=f16"] = {"us": round(t_us, 3), "algorithmic_bytes": B,
-                                     "GB/s": round(B / (t_us * 1e-6) / 1e9, 1),
-                                     "TFLOP/s": round(2.0 * M * w.V * w.K / (t_us * 1e-6) / 1e12, 2)}
-        del o16
-    # zero-point heads: the same kernels with a per-row, per-group zero point
-    for M in Ms:
-        t_us = timed_loop(lambda i, M=M: lmh.logits(
-            xs[M], zblobs[i % R], w.V, w.K, zbits, w.group, sdt, out=outs[M], workspace=wss[M],
-            path=args.path), args.steps)
-        B = algorithmic_bytes(M, w.V, w.K, w.bits, w.group) + w.V * (w.K // w.group)
-        per_call[f"M={M} zp"] = {"us": round(t_us, 3), "algorithmic_bytes": B,
-                                  "GB/s": round(B / (t_us * 1e-6) / 1e9, 1),
-                                  "TFLOP/s": round(2.0 * M * w.V * w.K / (t_us * 1e-6) / 1e12, 2)}
-    rs_us = timed_loop(lambda i: rescore(), args.steps)
-    per_call[f"top{args.topk}_rescore"] = {"us": round(rs_us, 3), "M": m_rs}
-    fu_us = timed_loop(one_call, args.steps)
-    per_call[f"logits+top{args.topk}_one_call"] = {"us": round(fu_us, 3), "M": m_rs}
-    # input-embedding gather from the same packed blob: one decode token and a
-    # 4096-token prefill, rows in the activation dtype
-    gen = torch.Generator(device="cpu").manual_seed(w.wid)
-    for T in (1, 4096):
-        ids = torch.randint(0, w.V, (T,), generator=gen, dtype=torch.int32).to(dev)
-        eo = torch.empty((T, w.K), dtype=TD[w.x_dtype], device=dev)
-        e_us = timed_loop(lambda i, ids=ids, eo=eo: lmh.embed(
-            ids, blobs[i % R], w.V, w.K, w.bits, w.group, sdt, out=eo), args.steps)
-        eb = T * (w.K * w.bits // 8 + (w.K // w.group) * 2 + w.K * 2 + 4)
-        per_call[f"embed_T={T}"] = {"us": round(e_us, 3), "algorithmic_bytes": eb,
-                                     "GB/s": round(eb / (e_us * 1e-6) / 1e9, 1)}
+        log(f"M={M}: {us:.2f} us (graph {usg:.2f})")
+    if not args.no_extras:
+        # 16-bit logits (fp16 output: half the output bytes) at every M > 1
+        for M in Ms:
+            if M == 1:
+                continue
+            o16 = torch.empty((M, w.V), dtype=torch.float16, device=dev)
+            us, usg = both(prep_logits(M, blobs, w.bits, o16))
+            B = algorithmic_bytes(M, w.V, w.K, w.bits, w.group) - M * w.V * 2
+            per_call[f"M={M} y=f16"] = {"us": us, "us_graph": usg, "algorithmic_bytes": B,
+                                         "GB/s": round(B / (us * 1e-6) / 1e9, 1),
+                                         "TFLOP/s": round(2.0 * M * w.V * w.K / (us * 1e-6) / 1e12, 2)}
+            del o16
+        # zero-point heads: the same kernels with a per-row, per-group zero point
+        for M in Ms:
+            us, usg = both(prep_logits(M, zblobs, zbits, outs[M]))
+            B = algorithmic_bytes(M, w.V, w.K, w.bits, w.group) + w.V * (w.K // w.group)
+            per_call[f"M={M} zp"] = {"us": us, "us_graph": usg, "algorithmic_bytes": B,
+                                      "GB/s": round(B / (us * 1e-6) / 1e9, 1),
+                                      "TFLOP/s": round(2.0 * M * w.V * w.K / (us * 1e-6) / 1e12, 2)}
+        us, usg = both(lambda: [lmh.prepare_topk_rescore(xs[m_rs], Wref, outs[m_rs], args.topk, t_idx,
+                                                         t_val, t_top1, tws)])
+        per_call[f"top{args.topk}_rescore"] = {"us": us, "us_graph": usg, "M": m_rs}
+        us, usg = both(prep_one_call)
+        per_call[f"logits+top{args.topk}_one_call"] = {"us": us, "us_graph": usg, "M": m_rs}
+        # input-embedding gather from the same packed blob: one decode token and a
+        # 4096-token prefill, rows in the activation dtype
+        gen = torch.Generator(device="cpu").manual_seed(w.wid)
+        for T in (1, 4096):
+            ids = torch.randint(0, w.V, (T,), generator=gen, dtype=torch.int32).to(dev)
+            eo = torch.empty((T, w.K), dtype=TD[w.x_dtype], device=dev)
+            us, usg = both(lambda ids=ids, eo=eo: [lmh.prepare_embed(ids, b, w.V, w.K, w.bits, w.group,
+                                                                     sdt, eo) for b in blobs])
+            eb = T * (w.K * w.bits // 8 + (w.K // w.group) * 2 + w.K * 2 + 4)
+            per_call[f"embed_T={T}"] = {"us": us, "us_graph": usg, "algorithmic_bytes": eb,
+                                         "GB/s": round(eb / (us * 1e-6) / 1e9, 1)}
+        # the unquantized 16-bit control GEMV at one activation row (vLLM PR
+        # #48870, review comment, point 1), over rotating copies of the weight
+        RC = 1 if args.hot else max(2, math.ceil(1e9 / (Wref.numel() * 2)))
+        wrefs = [Wref] + [Wref.clone() for _ in range(RC - 1)]
+        x1 = xs[Ms[0]][:1]
+        oc = torch.empty((1, w.V), dtype=torch.float32, device=dev)
+        us, usg = both(lambda: [lmh.prepare_dense_logits(x1, wr, oc) for wr in wrefs])
+        Bc = w.V * w.K * 2 + w.K * 2 + w.V * 4
+        qus = per_call[f"M={Ms[0]}"]["us"] if Ms[0] == 1 else None
+        per_call["control_16bit_gemv_M=1"] = {
+            "us": us, "us_graph": usg, "algorithmic_bytes": Bc, "GB/s": round(Bc / (us * 1e-6) / 1e9, 1),
+            "frac_hbm_peak": round(Bc / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "quantized_speedup": round(us / qus, 3) if qus else None, "weight_copies": RC}
+        del wrefs
 
     agreement = decode_agreement(args, w, lmh, synth, to_dev, blob, Wref, sdt, dev) if args.agreement else None
 
     m1 = per_call[f"M={Ms[0]}"]
     value = m1["us"]
     # the symmetric GEMV without the top-K epilogue (template flags ZP, TK)
-    tr = recorded_traffic(w.name, "gemv_kernel<", ",false,false>") if m1["kernel"] == "gemv" else None
+    tr = recorded_traffic(w.name, "gemv_kernel<", "") if m1["kernel"] == "gemv" else None
     roofline = {
-        "bound": "hbm", "kernel": f"lmh gemv, M={Ms[0]}", "achieved": m1["GB/s"], "peak": HBM_PEAK_GBS,
-        "unit": "GB/s", "frac": m1["frac_hbm_peak"], "traffic": tr["bytes"] if tr else None,
-        "bytes_per_launch": m1["algorithmic_bytes"],
+        "bound": "hbm", "kernel": f"lmh {m1['kernel']}, M={Ms[0]}", "achieved": m1["GB/s"],
+        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": m1["frac_hbm_peak"],
+        "traffic": tr["bytes"] if tr else None, "bytes_per_launch": m1["algorithmic_bytes"],
         "traffic_source": os.path.relpath(traffic_file(w.name), ROOT) if tr else None,
     }
-
-    # a practical ceiling beside the 8 TB/s figure: a device-to-device copy of
-    # one packed head between the rotating copies (identical contents), bytes
-    # read + written per copy over its time
-    if R >= 2:
-        def copy_loop(i):
-            blobs[(i + 1) % R].copy_(blobs[i % R])
-
-        t_copy = timed_loop(copy_loop, 50)
-        copy_gbs = 2.0 * blob_bytes / (t_copy * 1e-6) / 1e9
-        roofline["copy_GBps"] = round(copy_gbs, 1)
-        roofline["frac_of_copy"] = round(m1["GB/s"] / copy_gbs, 4)
+    # the practical read ceiling measured in the same run: a read-only kernel
+    # (lmhead_stream_read) over the same bytes as the packed head, rotating the
+    # same copies, timed the same way
+    sink = torch.empty(1024, dtype=torch.uint8, device=dev)
+    rd_us, rd_usg = both(lambda: [lmh.prepare_stream_read(b, sink) for b in blobs])
+    rd_gbs = blob_bytes / (rd_us * 1e-6) / 1e9
+    roofline["read_ceiling"] = {"GB/s": round(rd_gbs, 1), "us": rd_us, "us_graph": rd_usg,
+                                "bytes": blob_bytes, "frac_of_hbm_peak": round(rd_gbs / HBM_PEAK_GBS, 4)}
+    roofline["frac_of_read_ceiling"] = round(rd_us / value, 4) if Ms[0] == 1 else None
 
     cpu = None
     if not args.no_cpu_baseline:
-        import oracle
-
-        ratios = oracle.MSE_RATIOS if w.clip == "mse" else oracle.RTN_RATIOS
-        od = {"f16": oracle.F16, "bf16": oracle.BF16, "f32": oracle.F32}
-        rows = None
-        if w.K > 2048:  # bound the sample for the widest head
-            rows = np.arange(0, w.V, 8)
-        Wh = W if rows is None else np.ascontiguousarray(W[rows])
-        qo, so = oracle.quantize(Wh, w.bits, w.group, od[w.scale_dtype], ratios, w_dtype=od[w.w_dtype])
-        x1 = synth.activations(w, Ms[0])
-        n, t_cpu = 0, 0.0
-        while n < 50 and (n == 0 or t_cpu < args.cpu_seconds):
-            c0 = time.perf_counter()
-            oracle.logits(x1, qo, so, od[w.scale_dtype], w.group, x_dtype=od[w.x_dtype])
-            t_cpu += time.perf_counter() - c0
-            n += 1
-        frac_rows = 1.0 if rows is None else len(rows) / w.V
-        us_call = t_cpu / n / frac_rows * 1e6
-        cpu = {"value": round(us_call, 1), "unit": "us/call", "cores": 1, "kind": "oracle",
-               "sample": f"fp64 oracle logits, M={Ms[0]}, {'all' if rows is None else len(rows)} of "
-                         f"{w.V} rows, {n} calls, single thread; scaled to one whole call",
-               "host_threads_available": os.cpu_count()}
+        log("cpu baseline (fp64 oracle on the host cores)")
+        cpu = cpu_oracle_baseline(w, W, Ms, synth, np, args.cpu_seconds)
 
     line = {
         "metric": METRIC, "value": value, "unit": "us/call", "n_gpus": 1, "steps": args.steps,
@@ -495,10 +590,11 @@ def main() -> int:
         "higher_is_better": False, "scaling": "weak",
         "vs_baseline": round(value / PAGES_US_M1, 5) if w.name == synth.HEADLINE and Ms[0] == 1 else None,
         "vs_baseline_note": "value / 240 us (fused Marlin on RTX 5080, same head, M=1; context only)",
-        "dtype": "f16", "data": "synthetic",
+        "dtype": "f16" if w.x_dtype == "f16" else "bf16->f16", "data": "synthetic",
         "config": {"workload": w.name, "V": w.V, "K": w.K, "bits": w.bits, "group": w.group,
                    "scale": w.scale_dtype, "x": w.x_dtype, "M": Ms, "topk": args.topk,
-                   "rotating_copies": R, "cache": "hot" if args.hot else "cold"},
+                   "rotating_copies": R, "cache": "hot" if args.hot else "cold",
+                   "calls_per_timing": ncalls},
         "per_call": per_call,
         "load_time": {"quantize_ms": round(quant_ms, 3), "pack_ms": round(pack_ms, 3),
                       "quantize_pack_ms": round(qp_ms, 3),

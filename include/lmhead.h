@@ -245,10 +245,11 @@ int lmhead_embed(const int32_t* ids, int64_t T, const void* packed, int64_t V, i
                  void* stream);
 
 /*
- * lmhead_logits_workspace_bytes -- device workspace that lmhead_logits needs
- *   for M rows of x: 0 for fp16 x; for bf16 x, room for x converted to fp16
- *   with a per-row power-of-two scale (M*K*2 and M*4 bytes, each rounded up
- *   to a multiple of 256).
+ * lmhead_logits_workspace_bytes -- device workspace that lmhead_logits may
+ *   need for M rows of x: 0 for fp16 x; for bf16 x, room for x converted to
+ *   fp16 with a per-row power-of-two scale (M*K*2 and M*4 bytes, each rounded
+ *   up to a multiple of 256), which only the MFMA kernels use (the GEMV,
+ *   M <= 2 by default, converts bf16 rows itself and needs none).
  */
 size_t lmhead_logits_workspace_bytes(int64_t M, int64_t K, int x_dtype);
 
@@ -259,16 +260,18 @@ size_t lmhead_logits_workspace_bytes(int64_t M, int64_t K, int x_dtype);
  *   packed blob.  The codes q enter the arithmetic exactly; each group's
  *   partial sum is accumulated in fp32 and multiplied by its scale in fp32.
  *   x       [M, K] row-major, x_dtype LMH_F16 or LMH_BF16 (bf16 rows are
- *           converted to fp16 with an exact power-of-two row scale first; this
- *           needs the workspace).
+ *           converted to fp16 with an exact power-of-two row scale: inside the
+ *           GEMV, and for the MFMA kernels by a first kernel into the
+ *           workspace).
  *   packed  the blob for (V, K, bits, group, scale_dtype).
  *   bias    [V] fp32 or NULL.
  *   y       [M, ldy] fp32 row-major, ldy >= V; columns V..ldy-1 are not
  *           written.  Needs only 4-byte alignment.
  *   workspace / ws_bytes: at least lmhead_logits_workspace_bytes(M, K, x_dtype)
- *           (may be NULL/0 for fp16 x).
- *   M = 1 and M = 2 run a GEMV with one lane per vocabulary row (all of K
- *   per wave); larger M runs a 16x16x32 fp16 MFMA kernel (its
+ *           when x is bf16 and an MFMA kernel runs (M > 2 by default), else
+ *           ignored (may be NULL/0); a missing or short one is LMH_E_WORKSPACE.
+ *   M = 1 and M = 2 run a GEMV with one lane per vocabulary row (K split
+ *   over up to 8 waves per 64-row block); larger M runs a 16x16x32 fp16 MFMA kernel (its
  *   code unpacking is shared by all activation rows), chosen from
  *   measurements: for K <= 1024 and G >= 64, the activation-resident one
  *   from M = 33 on; otherwise for K <= 1024 the LDS-staged one for
@@ -401,6 +404,16 @@ int lmhead_logits_topk(const void* x, int x_dtype, int64_t M, const void* packed
                        const void* w_ref, int w_dtype, int topk, float* y, int64_t ldy,
                        int32_t* idx_out, float* val_out, int32_t* top1_out, void* workspace,
                        size_t ws_bytes, void* stream);
+
+/*
+ * lmhead_stream_read -- a measurement aid, not part of the logits path: reads
+ *   `bytes` bytes at src (one pass, 16-byte loads, nothing stored except by
+ *   chance into sink) -- the practical HBM read rate a logits kernel that
+ *   reads the same bytes is measured against.  bytes % 16 == 0; src 16-byte
+ *   aligned; sink >= 1024 bytes, 4-byte aligned, contents afterwards
+ *   undefined.  bytes == 0 is a valid empty call.
+ */
+int lmhead_stream_read(const void* src, size_t bytes, void* sink, void* stream);
 
 #ifdef __cplusplus
 }

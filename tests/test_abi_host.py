@@ -86,8 +86,11 @@ def test_logits_validation():
     assert _logits(x=P + 8) == E_ALIGN
     assert _logits(packed=P + 4) == E_ALIGN
     assert _logits(y=P + 2) == E_ALIGN
-    assert _logits(xd=BF16) == E_WS           # bf16 x needs the conversion workspace
-    assert _logits(xd=BF16, ws=P, wsn=16) == E_WS
+    # bf16 x: the MFMA kernels take it converted in the workspace (the GEMV,
+    # M <= 2 by default, converts it itself and needs none)
+    assert _logits(xd=BF16, M=3) == E_WS
+    assert _logits(xd=BF16, path=2) == E_WS
+    assert _logits(xd=BF16, path=3, ws=P, wsn=16) == E_WS
     assert _logits(path=1, M=5) == E_UNSUP   # the GEMV serves M <= 4
     assert _logits(path=5) == E_UNSUP
     # empty requests are valid and launch nothing

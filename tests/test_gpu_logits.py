@@ -112,6 +112,25 @@ def test_invariants_zero_rows_scaling_determinism(path, M):
     assert np.array_equal(y3, 2 * y1), "y(2x) != 2 y(x)"
 
 
+@pytest.mark.parametrize("bits,G,K", [(4, 128, 2048), (4, 128, 3072), (4, 128, 5120), (4, 64, 4096),
+                                      (4, 1024, 3072), (8, 128, 2048), (8, 64, 3072), (8, 2048, 2048)])
+@pytest.mark.parametrize("xdt", ["f16", "bf16"])
+def test_gemv_wide_rows(bits, G, K, xdt):
+    """The GEMV on rows of 2048..5120 columns: waves with 2..5 superchunks of
+    the K split (the two-buffer ring with an even and an odd count, the serial
+    mode of the 3- and 4-row variants), groups inside and across waves."""
+    need_gpu()
+    V = 330
+    sdt = "bf16" if xdt == "bf16" else "f16"
+    q, s, blob = _head(V, K, bits, G, sdt, seed=K + G + bits)
+    for M in (1, 2, 3, 4):
+        x = synth.random_x(M, K, seed=M + 7, dtype=xdt)
+        y = _run(x, xdt, blob, V, K, bits, G, sdt, GEMV)
+        y_or = oracle.logits(x, q, s, OD[sdt], G, x_dtype=OD[xdt])
+        y_abs = abs_terms(x, xdt, q, s, OD[sdt], G)
+        check_logits(y, y_or, y_abs, K, G, what=f"K={K} G={G} bits={bits} M={M} {xdt}")
+
+
 def test_gemv_and_mfma_agree():
     need_gpu()
     V, K, bits, G = 600, 1024, 4, 64

@@ -76,6 +76,7 @@ def lib() -> ctypes.CDLL:
             "lmhead_logits_topk_workspace_bytes": (sz, [i64, i64, i64, i32, i32]),
             "lmhead_logits_topk": (i32, [vp, i32, i64, vp, i64, i64, i32, i64, i32, vp, vp, i32, i32,
                                          vp, i64, vp, vp, vp, vp, sz, vp]),
+            "lmhead_stream_read": (i32, [vp, sz, vp, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -330,6 +331,124 @@ def logits_topk(x: torch.Tensor, packed: torch.Tensor, V: int, K: int, bits: int
         _ptr(w_ref), _DT[w_ref.dtype], topk, _ptr(out), ldy, _ptr(idx), _ptr(val), _ptr(top1),
         _ptr(workspace), workspace.numel(), _stream(x)))
     return idx, val, top1
+
+
+# ---- prepared calls: arguments converted once, for tight decode loops ----------
+
+_raw_lib: Optional[ctypes.CDLL] = None
+
+
+def _raw() -> ctypes.CDLL:
+    """A second handle on the library whose functions carry no argtypes, so a
+    prepared call passes its ready-made ctypes values without conversion."""
+    global _raw_lib
+    if _raw_lib is None:
+        lib()  # raises if the library is missing
+        _raw_lib = ctypes.CDLL(LIB_PATH)
+        for name in ("lmhead_logits_typed", "lmhead_logits_topk", "lmhead_topk_rescore",
+                     "lmhead_embed", "lmhead_dense_logits", "lmhead_stream_read"):
+            getattr(_raw_lib, name).restype = ctypes.c_int
+    return _raw_lib
+
+
+def _cargs(sig, vals):
+    """Python values -> ctypes values of the declared argument types."""
+    return tuple(None if v is None and t is ctypes.c_void_p else t(v) for t, v in zip(sig, vals))
+
+
+class PreparedCall:
+    """One library call whose arguments were checked and converted once.
+    Calling it enqueues the same work again on the stream that was current when
+    it was prepared (no Python-side checks, no allocation); the tensors it
+    refers to are kept alive by the object and must not be resized or freed."""
+
+    def __init__(self, name: str, args: tuple, keep: tuple):
+        self._fn = getattr(_raw(), name)
+        self._name = name
+        self._args = _cargs(getattr(lib(), name).argtypes, args)
+        self._keep = keep
+
+    def __call__(self) -> None:
+        rc = self._fn(*self._args)
+        if rc != LMH_OK:
+            raise LmheadError(self._name, rc)
+
+
+def prepare_logits(x: torch.Tensor, packed: torch.Tensor, V: int, K: int, bits: int, group: int,
+                   scale_dtype: torch.dtype, out: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None, path: int = PATH_AUTO) -> PreparedCall:
+    """lmhead_logits_typed on fixed tensors, as a PreparedCall (see logits)."""
+    _need_cuda(x, packed, bias)
+    if out.stride(-1) != 1:
+        raise ValueError("out must have unit column stride")
+    M = x.shape[0]
+    if workspace is None:
+        workspace = logits_workspace(M, K, x.dtype, x.device)
+    ws_n = 0 if workspace is None else workspace.numel()
+    args = (_ptr(x), _DT[x.dtype], M, _ptr(packed), V, K, bits, group, _DT[scale_dtype], _ptr(bias),
+            _ptr(out), _DT[out.dtype], out.stride(0), _ptr(workspace), ws_n, path, _stream(x))
+    return PreparedCall("lmhead_logits_typed", args, (x, packed, bias, out, workspace))
+
+
+def prepare_logits_topk(x: torch.Tensor, packed: torch.Tensor, V: int, K: int, bits: int,
+                        group: int, scale_dtype: torch.dtype, w_ref: torch.Tensor, topk: int,
+                        idx: torch.Tensor, val: torch.Tensor, top1: torch.Tensor,
+                        bias: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None) -> PreparedCall:
+    """lmhead_logits_topk on fixed tensors, as a PreparedCall (see logits_topk)."""
+    _need_cuda(x, packed, w_ref, bias)
+    M = x.shape[0]
+    if workspace is None:
+        workspace = logits_topk_workspace(M, V, K, x.dtype, topk, x.device)
+    ldy = out.stride(0) if out is not None else 0
+    args = (_ptr(x), _DT[x.dtype], M, _ptr(packed), V, K, bits, group, _DT[scale_dtype], _ptr(bias),
+            _ptr(w_ref), _DT[w_ref.dtype], topk, _ptr(out), ldy, _ptr(idx), _ptr(val), _ptr(top1),
+            _ptr(workspace), workspace.numel(), _stream(x))
+    return PreparedCall("lmhead_logits_topk", args,
+                        (x, packed, w_ref, idx, val, top1, bias, out, workspace))
+
+
+def stream_read(src: torch.Tensor, sink: torch.Tensor) -> None:
+    """One read-only pass over src's bytes (lmhead_stream_read; a measurement aid)."""
+    _need_cuda(src, sink)
+    nb = src.numel() * src.element_size()
+    _check("lmhead_stream_read", lib().lmhead_stream_read(_ptr(src), nb, _ptr(sink), _stream(src)))
+
+
+def prepare_stream_read(src: torch.Tensor, sink: torch.Tensor) -> PreparedCall:
+    _need_cuda(src, sink)
+    nb = src.numel() * src.element_size()
+    return PreparedCall("lmhead_stream_read", (_ptr(src), nb, _ptr(sink), _stream(src)), (src, sink))
+
+
+def prepare_dense_logits(x: torch.Tensor, w: torch.Tensor, out: torch.Tensor) -> PreparedCall:
+    """lmhead_dense_logits on fixed tensors, as a PreparedCall."""
+    _need_cuda(x, w)
+    M, K = x.shape
+    args = (_ptr(x), _DT[x.dtype], M, _ptr(w), _DT[w.dtype], w.shape[0], K, _ptr(out),
+            out.stride(0), _stream(x))
+    return PreparedCall("lmhead_dense_logits", args, (x, w, out))
+
+
+def prepare_topk_rescore(x: torch.Tensor, w_ref: torch.Tensor, y: torch.Tensor, topk: int,
+                         idx: torch.Tensor, val: torch.Tensor, top1: torch.Tensor,
+                         workspace: torch.Tensor) -> PreparedCall:
+    """lmhead_topk_rescore on fixed tensors, as a PreparedCall."""
+    _need_cuda(x, w_ref, y)
+    M, K = x.shape
+    args = (_ptr(x), _DT[x.dtype], M, _ptr(w_ref), _DT[w_ref.dtype], w_ref.shape[0], K, _ptr(y),
+            y.stride(0), topk, _ptr(idx), _ptr(val), _ptr(top1), _ptr(workspace),
+            workspace.numel(), _stream(x))
+    return PreparedCall("lmhead_topk_rescore", args, (x, w_ref, y, idx, val, top1, workspace))
+
+
+def prepare_embed(ids: torch.Tensor, packed: torch.Tensor, V: int, K: int, bits: int, group: int,
+                  scale_dtype: torch.dtype, out: torch.Tensor) -> PreparedCall:
+    """lmhead_embed on fixed tensors, as a PreparedCall."""
+    _need_cuda(ids, packed)
+    args = (_ptr(ids), ids.numel(), _ptr(packed), V, K, bits, group, _DT[scale_dtype], _ptr(out),
+            _DT[out.dtype], out.stride(0), _stream(ids))
+    return PreparedCall("lmhead_embed", args, (ids, packed, out))
 
 
 class QuantizedHead:

@@ -220,22 +220,27 @@ static int logits_impl(const void* x, int x_dtype, int64_t M, const void* packed
     if (y_dtype != F32 && y_dtype != F16 && y_dtype != BF16) return LMH_E_DTYPE;
     if (((uintptr_t)y & (y_dtype == F32 ? 3u : 1u)) != 0) return LMH_E_ALIGN;
     if (bias && ((uintptr_t)bias & 3u) != 0) return LMH_E_ALIGN;
-    const size_t need = lmhead_logits_workspace_bytes(M, K, x_dtype);
-    if (need > 0) {
-        if (!workspace || ws_bytes < need) return LMH_E_WORKSPACE;
-        if (!aligned16(workspace)) return LMH_E_ALIGN;
-    }
     // the MFMA launch has one workgroup per (256 rows, 16..32 activations)
     if ((V + 255) / 256 * ((M + 15) / 16) >= (int64_t(1) << 30)) return LMH_E_UNSUPPORTED;
     const bool gemv_ok = M <= lmh::kGemvMaxM && M * K <= lmh::kGemvMaxMK;
     if (path == 1 && !gemv_ok) return LMH_E_UNSUPPORTED;
     if (path == 4 && !lmh::xres_fits(K)) return LMH_E_UNSUPPORTED;
+    if (path == 0) path = auto_path(M, K, bits, group);
+    // bf16 rows: the GEMV converts them itself; the MFMA kernels take them
+    // converted to fp16 (with a row exponent) in the workspace
+    const bool convert = x_dtype == BF16 && path != 1;
+    if (convert) {
+        const size_t need = lmhead_logits_workspace_bytes(M, K, x_dtype);
+        if (!workspace || ws_bytes < need) return LMH_E_WORKSPACE;
+        if (!aligned16(workspace)) return LMH_E_ALIGN;
+    }
 
     hipStream_t st = (hipStream_t)stream;
     lmh::LogitsArgs a;
     a.x = x;
+    a.x_bf16 = x_dtype == BF16 && path == 1;
     a.xexp = nullptr;
-    if (x_dtype == BF16) {
+    if (convert) {
         _Float16* xh = (_Float16*)workspace;
         int* xe = (int*)((char*)workspace + ((M * K * 2 + 255) / 256) * 256);
         hipError_t e = lmh::launch_x_to_f16((const uint16_t*)x, (int)M, (int)K, xh, xe, st);
@@ -257,7 +262,6 @@ static int logits_impl(const void* x, int x_dtype, int64_t M, const void* packed
     a.zp = wd.zp;
     a.lists = lists;
     a.list_T = list_T;
-    if (path == 0) path = auto_path(M, K, bits, group);
     if (path == 1) return from_hip(lmh::launch_gemv(a, st));
     if (path == 4) return from_hip(lmh::launch_mfma_xres(a, st));
     return from_hip(path == 3 ? lmh::launch_mfma_lds(a, st) : lmh::launch_mfma(a, st));
@@ -407,6 +411,15 @@ int lmhead_logits_topk(const void* x, int x_dtype, int64_t M, const void* packed
     return from_hip(lmh::launch_topk_rescore(x, x_dtype, (int)M, w_ref, w_dtype, V, K, yy, ly, topk,
                                              idx_out, val_out, top1_out, ws + xws,
                                              (hipStream_t)stream));
+}
+
+int lmhead_stream_read(const void* src, size_t bytes, void* sink, void* stream) {
+    if (bytes % 16 != 0 || bytes >= ((size_t)1 << 46)) return LMH_E_SHAPE;
+    if (bytes / 16 / 768 >= ((size_t)1 << 31)) return LMH_E_UNSUPPORTED;
+    if (bytes == 0) return LMH_OK;
+    if (!src || !sink) return LMH_E_NULL;
+    if (!aligned16(src) || ((uintptr_t)sink & 3u) != 0) return LMH_E_ALIGN;
+    return from_hip(lmh::launch_stream_read(src, (int64_t)bytes, sink, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -58,8 +58,9 @@ hipError_t launch_pack(const int8_t* q, const uint16_t* s, const uint8_t* z, int
                        int bits, int64_t G, uint8_t* out, hipStream_t st);
 
 struct LogitsArgs {
-    const void* x;         // [M, K] fp16 (after conversion) row-major
-    const int* xexp;       // [M] power-of-two row exponents, or nullptr
+    const void* x;         // [M, K] row-major: fp16, or bf16 when x_bf16 (GEMV only)
+    int x_bf16;            // the GEMV converts bf16 rows itself (other kernels take fp16)
+    const int* xexp;       // [M] power-of-two row exponents of converted bf16 rows, or nullptr
     const uint8_t* packed; // blob
     const float* bias;     // [V] or nullptr
     void* y;               // [M, ldy] in y_dtype (F32, F16 or BF16)
@@ -74,14 +75,16 @@ struct LogitsArgs {
 
 hipError_t launch_x_to_f16(const uint16_t* x_bf16, int M, int K, _Float16* xh, int* xexp,
                            hipStream_t st);
+// Lane-per-row GEMV (gemv.hip; zero-point heads in gemv_zp.hip).
 hipError_t launch_gemv(const LogitsArgs& a, hipStream_t st);
+hipError_t launch_gemv_zp(const LogitsArgs& a, hipStream_t st);
 hipError_t launch_mfma(const LogitsArgs& a, hipStream_t st);
 // Activation-resident MFMA kernel for large M; needs K <= xres max (xres_fits).
 bool xres_fits(int64_t K);
 hipError_t launch_mfma_xres(const LogitsArgs& a, hipStream_t st);
 hipError_t launch_mfma_lds(const LogitsArgs& a, hipStream_t st);
 // Logits kernel families (gemv, register MFMA, LDS-staged MFMA, activation
-// resident) and the zero-point instantiations of all of them (logits_zp.hip).
+// resident) and the zero-point instantiations of the MFMA ones (logits_zp.hip).
 enum { kFamGemv = 0, kFamMfma = 1, kFamMfmaLds = 2, kFamXres = 3 };
 hipError_t run_family_zp(int family, const LogitsArgs& a, hipStream_t st);
 hipError_t launch_dense(const void* x, int dtype, int M, const void* w, int64_t V, int64_t K,
@@ -100,6 +103,8 @@ hipError_t launch_topk_merge_rescore(const u64* lists, const void* x, int x_dtyp
                                      int64_t ldy, int topk, int T, int32_t* idx, float* val,
                                      int32_t* top1, hipStream_t st);
 int64_t topk_max_v();  // largest row length lmhead_topk_rescore supports
+// Read-only stream over `bytes` (a multiple of 16) at src; sink >= 1 KiB.
+hipError_t launch_stream_read(const void* src, int64_t bytes, void* sink, hipStream_t st);
 
 // Largest M the lane-per-row GEMV accepts when forced, the largest it runs by
 // default (from M = 3 on an MFMA kernel is faster, its unpacking being shared

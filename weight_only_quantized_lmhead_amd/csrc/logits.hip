@@ -1,7 +1,7 @@
 // Fused weight-only-quantized logits: the symmetric instantiations of the
-// kernels in logits_kernels.h, the bf16 -> fp16 activation conversion, the
-// dense control GEMV and the launch entry points (which hand zero-point heads
-// to logits_zp.hip).
+// MFMA kernels in logits_kernels.h, the bf16 -> fp16 activation conversion
+// they take, the dense control GEMV and the MFMA launch entry points (which
+// hand zero-point heads to logits_zp.hip).
 #include "logits_kernels.h"
 
 namespace lmh {
@@ -110,8 +110,6 @@ hipError_t run(int f, const LogitsArgs& a, hipStream_t st) {
     return a.zp ? run_family_zp(f, a, st) : run_family<false>(f, a, st);
 }
 }  // namespace
-
-hipError_t launch_gemv(const LogitsArgs& a, hipStream_t st) { return run(kFamGemv, a, st); }
 
 hipError_t launch_mfma(const LogitsArgs& a, hipStream_t st) { return run(kFamMfma, a, st); }
 

@@ -1,25 +1,15 @@
-// Fused weight-only-quantized logits: y[m,v] = sum_k x[m,k] * q[v,k] * s[v,k/G].
+// Fused weight-only-quantized logits, the MFMA kernels (M > 2):
+// y[m,v] = sum_k x[m,k] * q[v,k] * s[v,k/G].
 //
 // vLLM PR #48870 ("Fused WNA16 GEMM for tied quantized lm_head logits",
 // Purpose and perf table): the logits come straight from the packed codes and
-// scales; the dense weight is never formed.  Review comment, point 1: at one
-// activation row the kernel's time is set by the bytes it reads from HBM.
+// scales; the dense weight is never formed.  The codes enter the MFMA
+// operands exactly (fp16 integers, logits_common.h), each group's MFMA chain
+// starts from zero and is scaled in fp32, so the three kernels below give the
+// same bits as each other.
 //
-// Codes are unpacked exactly into fp16 in registers with the exponent trick:
-// OR-ing a nibble n into the fp16 pattern 0x6400 gives 1024 + n, so one
-// AND-OR per pair of codes plus one packed subtract yields q = n - 8 exactly
-// (int8: a byte permute into 0x64xx gives 1024 + b, minus 1152).  Products
-// with fp16 x are exact in fp32; each group's partial sum is accumulated in
-// fp32 and multiplied by the group scale in fp32 (the scale never touches a
-// 16-bit product).
-//
-// Kernels (which one runs for which M and head is decided in api.hip)
-//   gemv         M <= 4 (and M*K <= 32768).  A lane owns one vocabulary row of
-//                a 64-row block over a contiguous 1/KS of K (KS waves per
-//                block, partial sums added in LDS in wave order).  x is
-//                staged in LDS once per workgroup and read as 16-byte
-//                broadcasts.  Optionally (TK) it also writes each block's
-//                sorted top-K list for the fused decode path.
+// Kernels (which one runs for which M and head is decided in api.hip; the
+// lane-per-row GEMV for one to four rows is in gemv_kernels.h)
 //   mfma         register-fed MFMA.  A wave owns one row block (4 MFMA column
 //                tiles of 16 rows) and MT row tiles of 16 activations; each
 //                16-byte slot load is one 16x16x32 B operand per 32-column
@@ -28,351 +18,17 @@
 //                global-to-LDS loads; 32- or 64-row activation tiles.
 //   mfma_xres    a 64-row activation tile resident in LDS, weights streamed
 //                through a register ring (large M, K <= 1024).
-// (logits.hip adds the bf16 -> fp16 activation conversion and the dense
-// 16-bit control GEMV.)
 //
-// Zero-point heads (the asymmetric layout: unsigned codes n and one 8-bit
-// zero point z per row and group, w = (n - z) * s) use the same kernels with
-// the fixed offset 8 / 128 of the unpacking replaced by the row's z: the
-// fp16 pattern 0xE400 | z is -(1024 + z), so the same single packed add
-// yields n - z exactly.  Each kernel takes ZP as a template flag; the
-// symmetric instantiations are unchanged.
-//
-// This header holds the kernels and their dispatchers; logits.hip
-// instantiates the symmetric ones and logits_zp.hip the zero-point ones (two
-// translation units so that they compile in parallel).
+// Each kernel takes ZP (zero-point heads) as a template flag; the symmetric
+// instantiations are unchanged.  logits.hip instantiates the symmetric
+// kernels and logits_zp.hip the zero-point ones (two translation units so
+// that they compile in parallel).
 #pragma once
 
-#include "lmh_internal.h"
-
-#include <type_traits>
-
-#include <math.h>
+#include "logits_common.h"
 
 namespace lmh {
 namespace {
-
-__device__ __forceinline__ float scale_to_f32(uint16_t b, int sbf16) {
-    return sbf16 ? __uint_as_float((uint32_t)b << 16) : (float)__builtin_bit_cast(_Float16, b);
-}
-
-// (a & mask) | orv in one v_and_or_b32.  Written out because the compiler
-// otherwise splits it into v_and + v_or (gfx9 VOP3 cannot take two literals);
-// the mask comes from an SGPR and orv from a VGPR (one constant-bus read).
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t orv) {
-    uint32_t d;
-    asm volatile("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(mask), "v"(orv));
-    return d;
-}
-
-// Offsets that turn the biased fp16 patterns of the unpacking into signed
-// codes: lo = -(1024 + z) for low nibbles and int8 bytes (1024 + n -> n - z),
-// hi = -(64 + z) for high nibbles ((1024 + 16 n) / 16 -> n - z).  Symmetric
-// heads have the fixed z = 8 (int4) / 128 (int8).
-struct ZC {
-    h2 lo, hi;
-};
-
-template <int BITS>
-__device__ __forceinline__ ZC zc_sym() {
-    constexpr float z = BITS == 4 ? 8.0f : 128.0f;
-    return {{(_Float16)(-1024.0f - z), (_Float16)(-1024.0f - z)},
-            {(_Float16)(-64.0f - z), (_Float16)(-64.0f - z)}};
-}
-
-// Zero point z = byte i of zw (i a compile-time constant after unrolling):
-// the fp16 pattern 0xE400 | z is -(1024 + z) exactly (z < 1024), and adding
-// 960 gives -(64 + z), also exactly.
-__device__ __forceinline__ ZC zc_byte(uint32_t zw, int i) {
-    const h2 lo = __builtin_bit_cast(
-        h2, __builtin_amdgcn_perm(0xE4E4E4E4u, zw, 0x04000400u + (uint32_t)i * 0x00010001u));
-    const h2 k960 = {(_Float16)960.0f, (_Float16)960.0f};
-    return {lo, lo + k960};
-}
-
-// int4 word (8 codes; even columns in the low nibbles of each half-word) ->
-// four fp16 pairs (cols 0,1), (2,3), (4,5), (6,7), exact.  `magic` must hold
-// 0x64006400 (fp16 1024.0 in both halves).
-__device__ __forceinline__ void unpack_i4(uint32_t w, uint32_t magic, const ZC& zc, h2& p0, h2& p1,
-                                          h2& p2, h2& p3) {
-    const uint32_t hi = w >> 8;
-    const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
-    p0 = __builtin_bit_cast(h2, and_or(w, 0x000F000Fu, magic)) + zc.lo;          // 1024+n -> n-z
-    p1 = __builtin_elementwise_fma(__builtin_bit_cast(h2, and_or(w, 0x00F000F0u, magic)), sixteenth,
-                                   zc.hi);                                        // (1024+16n)/16-64-z
-    p2 = __builtin_bit_cast(h2, and_or(hi, 0x000F000Fu, magic)) + zc.lo;
-    p3 = __builtin_elementwise_fma(__builtin_bit_cast(h2, and_or(hi, 0x00F000F0u, magic)), sixteenth,
-                                   zc.hi);
-}
-
-// int8 word (4 codes, byte i = column i) -> two fp16 pairs, exact.
-__device__ __forceinline__ void unpack_i8(uint32_t w, const ZC& zc, h2& p0, h2& p1) {
-    p0 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, w, 0x04010400u)) + zc.lo;
-    p1 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, w, 0x04030402u)) + zc.lo;
-}
-
-__device__ __forceinline__ uint32_t word_of(const uint4& u, int j) {
-    return j == 0 ? u.x : j == 1 ? u.y : j == 2 ? u.z : u.w;
-}
-
-// Logits storage type: fp32, or the 16-bit pattern of fp16 / bf16.
-template <int OUT>
-using YT = typename std::conditional<OUT == F32, float, uint16_t>::type;
-
-// fp32 -> the output type, rounded to nearest even once, from the final fp32
-// value (bias and row exponent already applied).  The value passes through an
-// empty asm first: otherwise the backend may fold the last fp32 add into a
-// mixed-precision fma that rounds only once, which differs from rounding the
-// fp32 result.
-template <int OUT>
-__device__ __forceinline__ YT<OUT> to_out(float v) {
-    if constexpr (OUT == F32) {
-        return v;
-    } else {
-        asm("" : "+v"(v));
-        if constexpr (OUT == F16) {
-            return __builtin_bit_cast(uint16_t, (_Float16)v);
-        } else {
-            uint32_t u = __float_as_uint(v);
-            u += 0x7FFFu + ((u >> 16) & 1u);  // nearest even (finite values)
-            return (uint16_t)(u >> 16);
-        }
-    }
-}
-
-// Four consecutive logits at p (aligned to four elements).
-template <int OUT>
-__device__ __forceinline__ void store4(YT<OUT>* p, f4 v) {
-    if constexpr (OUT == F32) {
-        *(f4*)p = v;
-    } else {
-        const uint32_t lo = (uint32_t)to_out<OUT>(v[0]) | ((uint32_t)to_out<OUT>(v[1]) << 16);
-        const uint32_t hi = (uint32_t)to_out<OUT>(v[2]) | ((uint32_t)to_out<OUT>(v[3]) << 16);
-        *(uint2*)p = make_uint2(lo, hi);
-    }
-}
-
-
-// ---------------------------------------------------------------------------
-// GEMV: one lane per row of a 64-row block.  KS waves share a block, each
-// taking a contiguous 1/KS of the superchunks (KS = 1: all of K, no
-// reduction; KS > 1: the KS partial sums meet in LDS and are added in wave
-// order, so the result does not depend on timing).  Splitting K puts KS times
-// as many loads in flight per row block and gives the launch KS times as many
-// waves, which spreads a ragged number of blocks evenly over the CUs.
-// Superchunks stream through a ring of D register buffers (D = 1 for int4,
-// 2 for int8, whose waves cover twice as many superchunks): a buffer is
-// refilled as soon as it has been consumed, unless the wave's range has no
-// further superchunk (a wave-uniform test; for M > 1 the refill past the end
-// loads the last superchunk again); a ring slot past the end of the range
-// (fewer superchunks than D) loads the last one again and its contribution is
-// dropped.  GPS = groups per
-// superchunk (G <= span); GPS == 1 covers G >= span, the scale of superchunk c
-// then being that of group c / SPG.  With ZP the lane also reads its row's
-// zero point of each group (one byte, beside the scale).
-//
-// TK (top-K epilogue, fp32 logits): the wave that holds a block's final 64
-// logits of activation row m also writes that block's T largest as a sorted
-// list of order codes (value descending, then index ascending; see
-// topk_code), entry j at lists[(m*T + j)*NB + blk] (entry-major, so that the
-// merge reads the lists' heads as one contiguous run): each lane ranks its own code
-// against the 64 codes of the wave (read lane by lane into scalar
-// registers), and the lanes of rank < T store.  Rows past V take codes below
-// every real entry.  y may then be null (logits not stored).
-template <int BITS, int MM, int GPS, int D, int KS, int OUT, bool ZP, bool TK>
-__global__ __launch_bounds__(256) void gemv_kernel(const uint4* __restrict__ wq,
-                                                   const uint16_t* __restrict__ sc,
-                                                   const uint8_t* __restrict__ zq,
-                                                   const h2* __restrict__ xg,
-                                                   const int* __restrict__ xexp,
-                                                   const float* __restrict__ bias,
-                                                   void* __restrict__ y, int64_t ldy, int V, int K,
-                                                   int NB, int NC, int NG, int SPG, int sbf16,
-                                                   u64* __restrict__ lists, int T) {
-    constexpr int SPAN = BITS == 4 ? 128 : 64;
-    constexpr int CPS = SPAN / 32;    // 32-column chunks per superchunk
-    constexpr int CPG = CPS / GPS;    // chunks per group
-    constexpr int NA = MM == 1 ? 4 : (MM == 2 ? 2 : 1);  // independent partial sums per group
-    static_assert(KS == 1 || KS == 2 || KS == 4, "K split over 1, 2 or 4 waves");
-    const int lane = threadIdx.x & 63;
-    // the wave index, as a wave-uniform value the block and K-range arithmetic
-    // runs on the scalar unit (measured: faster at M = 1 and on int8 heads,
-    // slower for two rows of an int4 head, which keep the vector form)
-    const int wv = MM == 1 || BITS == 8 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)
-                                        : threadIdx.x >> 6;
-    const int blk_raw = blockIdx.x * (4 / KS) + wv / KS;
-    const int ks = wv % KS;
-    const bool live = blk_raw < NB;
-    const int blk = live ? blk_raw : NB - 1;
-    const int NCs = NC / KS;      // superchunks per wave
-    const int c0 = ks * NCs;      // first superchunk of this wave
-    const uint4* wp = wq + (int64_t)blk * NC * 256 + lane;
-    const uint16_t* sp = sc + (int64_t)blk * NG * 64 + lane;
-    // zero point of row `lane` in group g: byte (blk*NG + g)*64 + 4*(lane%16) + lane/16
-    const uint8_t* zp = ZP ? zq + (int64_t)blk * NG * 64 + 4 * (lane & 15) + (lane >> 4) : nullptr;
-    const int Kh = K >> 1;
-    const uint32_t magic = 0x64006400u;
-
-    uint4 buf[D][4];
-    uint16_t sb[D][GPS];
-    uint32_t zb[D][GPS];
-    // scale bookkeeping of the prefetch stream when a group spans superchunks
-    // (c0 is a multiple of SPG: the host only splits K on group boundaries)
-    int pf_g = c0 / SPG, pf_left = SPG;
-    const int cend = c0 + NCs;
-    auto load = [&](int p, int c) {
-        const int cc = c < cend ? c : cend - 1;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) buf[p][t] = wp[((int64_t)cc * 4 + t) * 64];
-        if constexpr (GPS > 1) {
-#pragma unroll
-            for (int g = 0; g < GPS; ++g) {
-                sb[p][g] = sp[((int64_t)cc * GPS + g) * 64];
-                if constexpr (ZP) zb[p][g] = zp[((int64_t)cc * GPS + g) * 64];
-            }
-        } else {
-            sb[p][0] = sp[(int64_t)pf_g * 64];
-            if constexpr (ZP) zb[p][0] = zp[(int64_t)pf_g * 64];
-            if (--pf_left == 0 && pf_g + 1 < NG) {
-                ++pf_g;
-                pf_left = SPG;
-            }
-        }
-    };
-
-    // int8: the first weight loads go out before x is staged, so the two
-    // round trips to memory overlap (151936 x 1024 int8 g128: M = 2 29.5
-    // against 34.2 us; for int4 it doubles the registers for no gain)
-    constexpr bool kEarly = BITS == 8;
-    if constexpr (kEarly) {
-#pragma unroll
-        for (int p = 0; p < D; ++p) load(p, c0 + p);
-    }
-    // x (all M rows, all of K) is staged once per workgroup in LDS; every lane
-    // then reads the same 16 bytes at a time (an LDS broadcast).
-    extern __shared__ uint4 xs_raw[];
-    const h2* x = (const h2*)xs_raw;
-    {
-        const uint4* src = (const uint4*)xg;
-        const int n16 = MM * K / 8;
-        for (int i = threadIdx.x; i < n16; i += 256) xs_raw[i] = src[i];
-    }
-    __syncthreads();
-    if (KS == 1 && blk_raw >= NB) return;  // wave-uniform; no barriers below when KS == 1
-
-    float acc[MM];
-#pragma unroll
-    for (int m = 0; m < MM; ++m) acc[m] = 0.0f;
-    if constexpr (!kEarly) {
-#pragma unroll
-        for (int p = 0; p < D; ++p) load(p, c0 + p);
-    }
-    for (int cb = c0; cb < cend; cb += D) {
-#pragma unroll
-        for (int p = 0; p < D; ++p) {
-            const int c = cb + p;
-            const int cl = c < cend ? c : cend - 1;
-            float part[MM][GPS][NA];
-#pragma unroll
-            for (int m = 0; m < MM; ++m)
-#pragma unroll
-                for (int g = 0; g < GPS; ++g)
-#pragma unroll
-                    for (int a = 0; a < NA; ++a) part[m][g][a] = 0.0f;
-            const int xc = cl * (SPAN / 2);  // half2 index of the superchunk's first column
-            ZC zc[GPS];
-#pragma unroll
-            for (int g = 0; g < GPS; ++g) zc[g] = ZP ? zc_byte(zb[p][g], 0) : zc_sym<BITS>();
-#pragma unroll
-            for (int j = 0; j < CPS; ++j) {
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    h2 p0, p1, p2, p3;
-                    if constexpr (BITS == 4) {
-                        unpack_i4(word_of(buf[p][t], j), magic, zc[j / CPG], p0, p1, p2, p3);
-                    } else {
-                        unpack_i8(word_of(buf[p][t], 2 * j), zc[j / CPG], p0, p1);
-                        unpack_i8(word_of(buf[p][t], 2 * j + 1), zc[j / CPG], p2, p3);
-                    }
-                    const int xi = xc + 16 * j + 4 * t;  // columns span*c + 32j + 8t
-#pragma unroll
-                    for (int m = 0; m < MM; ++m) {
-                        const uint4 xv = *(const uint4*)(x + m * Kh + xi);
-                        float a = part[m][j / CPG][t % NA];
-                        a = __builtin_amdgcn_fdot2(p0, __builtin_bit_cast(h2, xv.x), a, false);
-                        a = __builtin_amdgcn_fdot2(p1, __builtin_bit_cast(h2, xv.y), a, false);
-                        a = __builtin_amdgcn_fdot2(p2, __builtin_bit_cast(h2, xv.z), a, false);
-                        a = __builtin_amdgcn_fdot2(p3, __builtin_bit_cast(h2, xv.w), a, false);
-                        part[m][j / CPG][t % NA] = a;
-                    }
-                }
-            }
-            const bool real = c < cend;
-#pragma unroll
-            for (int g = 0; g < GPS; ++g) {
-                const float sv = real ? scale_to_f32(sb[p][g], sbf16) : 0.0f;
-#pragma unroll
-                for (int m = 0; m < MM; ++m) {
-                    float q = part[m][g][0];
-#pragma unroll
-                    for (int a = 1; a < NA; ++a) q += part[m][g][a];
-                    acc[m] = fmaf(sv, q, acc[m]);
-                }
-            }
-            // (the forced M = 2..4 variants keep the unconditional clamped
-            // load: the branch costs them registers)
-            if (MM > 1 || c + D < cend) load(p, c + D);
-        }
-    }
-    if constexpr (KS > 1) {
-        __shared__ float red[4][MM][64];
-#pragma unroll
-        for (int m = 0; m < MM; ++m) red[wv][m][lane] = acc[m];
-        __syncthreads();
-        if (ks != 0) return;
-#pragma unroll
-        for (int m = 0; m < MM; ++m) {
-            float r = red[wv][m][lane];
-#pragma unroll
-            for (int k = 1; k < KS; ++k) r += red[wv + k][m][lane];
-            acc[m] = r;
-        }
-    }
-    const int v = blk * 64 + lane;
-    if constexpr (!TK) {
-        if (live && v < V) {
-            const float b = bias ? bias[v] : 0.0f;
-#pragma unroll
-            for (int m = 0; m < MM; ++m) {
-                float r = acc[m];
-                if (xexp) r = ldexpf(r, xexp[m]);
-                ((YT<OUT>*)y)[(int64_t)m * ldy + v] = to_out<OUT>(r + b);
-            }
-        }
-    } else {
-        static_assert(OUT == F32, "the top-K epilogue ranks fp32 logits");
-        if (!live) return;  // wave-uniform: every lane of the wave takes part below
-        const float b = (bias && v < V) ? bias[v] : 0.0f;
-#pragma unroll
-        for (int m = 0; m < MM; ++m) {
-            float r = acc[m];
-            if (xexp) r = ldexpf(r, xexp[m]);
-            r = r + b;
-            if (y && v < V) ((float*)y)[(int64_t)m * ldy + v] = r;
-            const u64 c = v < V ? topk_code(r, v) : (u64)(64 - lane);
-            const uint32_t chi = (uint32_t)(c >> 32), clo = (uint32_t)c;
-            int rank = 0;
-#pragma unroll
-            for (int j = 0; j < 64; ++j) {
-                const u64 cj = ((u64)(uint32_t)__builtin_amdgcn_readlane((int)chi, j) << 32) |
-                               (uint32_t)__builtin_amdgcn_readlane((int)clo, j);
-                rank += cj > c;
-            }
-            if (rank < T) lists[((int64_t)m * T + rank) * NB + blk] = c;
-        }
-    }
-}
-
 // ---------------------------------------------------------------------------
 // MFMA kernel.  A workgroup = 4 waves = 4 row blocks (256 vocabulary rows) x
 // MT*16 activation rows (grid.y tiles M).  For each superchunk the workgroup
@@ -1271,82 +927,6 @@ __global__ __launch_bounds__(64 * xres_waves<NT_>(), 1) void mfma_xres_kernel(
 }
 
 
-inline int gps_of(int bits, int64_t G) {
-    const int span = span_of(bits);
-    return G >= span ? 1 : span / (int)G;
-}
-
-// Regions of the blob: codes, then scales, then (zero-point heads) zero points.
-template <int BITS>
-struct Regions {
-    const uint4* wq;
-    const uint16_t* sc;
-    const uint8_t* zq;
-    Regions(const LogitsArgs& a, bool zp) {
-        const int64_t vpad = (a.V + 63) / 64 * 64;
-        const int64_t wbytes = vpad * a.K * BITS / 8;
-        wq = (const uint4*)a.packed;
-        sc = (const uint16_t*)(a.packed + wbytes);
-        zq = zp ? a.packed + wbytes + vpad * (a.K / a.G) * 2 : nullptr;
-    }
-};
-
-template <int BITS, int MM, int OUT, bool ZP>
-hipError_t gemv_dispatch_gps(const LogitsArgs& a, int gps, hipStream_t st) {
-    // ring depth: measured on the 151936-row heads at M = 1 (int8 g128: 29.2
-    // against 32.0 us with D = 1; int4 loses with D = 2, its registers double;
-    // the forced M = 2..4 variants keep D = 1 for the same reason)
-    constexpr int D = BITS == 8 && MM == 1 ? 2 : 1;
-    const int NB = (int)((a.V + 63) / 64);
-    const int NC = (int)(a.K / span_of(BITS));
-    const int NG = (int)(a.K / a.G);
-    const int SPG = gps == 1 ? (int)(a.G / span_of(BITS)) : 1;
-    const Regions<BITS> rg(a, ZP);
-    const size_t lds = (size_t)MM * a.K * 2;
-    // split K over KS waves when every wave still gets at least 2 superchunks
-    // and the split falls on group boundaries
-    auto splits = [&](int ks) { return NC % (2 * ks) == 0 && (NC / ks) % SPG == 0; };
-    const int KS = splits(4) ? 4 : splits(2) ? 2 : 1;
-    // the top-K epilogue: fp32 logits, one activation row (its only user)
-    constexpr bool kTK = OUT == F32 && MM == 1;
-    const bool tk = kTK && a.lists != nullptr;
-#define LMH_GEMV_TK(G_, KS_, TK_)                                                                  \
-    hipLaunchKernelGGL((gemv_kernel<BITS, MM, G_, D, KS_, OUT, ZP, TK_>), dim3((NB * KS_ + 3) / 4), \
-                       dim3(256), lds, st, rg.wq, rg.sc, rg.zq, (const h2*)a.x, a.xexp, a.bias,    \
-                       a.y, a.ldy, (int)a.V, (int)a.K, NB, NC, NG, SPG, a.scale_bf16, a.lists,    \
-                       a.list_T)
-#define LMH_GEMV(G_, KS_)                                                                          \
-    do {                                                                                           \
-        if constexpr (kTK) {                                                                       \
-            if (tk) LMH_GEMV_TK(G_, KS_, true);                                                    \
-            else LMH_GEMV_TK(G_, KS_, false);                                                      \
-        } else {                                                                                   \
-            LMH_GEMV_TK(G_, KS_, false);                                                           \
-        }                                                                                          \
-    } while (0)
-#define LMH_GEMV_KS(G_) \
-    if (KS == 4) LMH_GEMV(G_, 4); else if (KS == 2) LMH_GEMV(G_, 2); else LMH_GEMV(G_, 1)
-    if (gps == 1) { LMH_GEMV_KS(1); }
-    else if constexpr (BITS == 8) { LMH_GEMV_KS(2); }
-    else if (gps == 2) { LMH_GEMV_KS(2); }
-    else { LMH_GEMV_KS(4); }
-#undef LMH_GEMV_KS
-#undef LMH_GEMV
-#undef LMH_GEMV_TK
-    return hipGetLastError();
-}
-
-template <int BITS, int OUT, bool ZP>
-hipError_t gemv_dispatch(const LogitsArgs& a, hipStream_t st) {
-    const int gps = gps_of(BITS, a.G);
-    switch (a.M) {
-    case 1: return gemv_dispatch_gps<BITS, 1, OUT, ZP>(a, gps, st);
-    case 2: return gemv_dispatch_gps<BITS, 2, OUT, ZP>(a, gps, st);
-    case 3: return gemv_dispatch_gps<BITS, 3, OUT, ZP>(a, gps, st);
-    default: return gemv_dispatch_gps<BITS, 4, OUT, ZP>(a, gps, st);
-    }
-}
-
 template <int BITS, int MT, int OUT, bool ZP>
 hipError_t mfma_dispatch_mt(const LogitsArgs& a, hipStream_t st) {
     const int NB = (int)((a.V + 63) / 64);
@@ -1470,7 +1050,6 @@ hipError_t run_family(int f, const LogitsArgs& a, hipStream_t st) {
     default: return a.bits == 4 ? FN<4, BF16, ZP>(a, st) : FN<8, BF16, ZP>(a, st);                \
     }
     switch (f) {
-    case kFamGemv: LMH_BY_BITS_OUT(gemv_dispatch)
     case kFamMfma: LMH_BY_BITS_OUT(mfma_dispatch)
     case kFamMfmaLds: LMH_BY_BITS_OUT(mfma_lds_dispatch)
     default: LMH_BY_BITS_OUT(xres_dispatch)
@@ -1480,3 +1059,4 @@ hipError_t run_family(int f, const LogitsArgs& a, hipStream_t st) {
 
 }  // namespace
 }  // namespace lmh
+
