@@ -99,7 +99,8 @@ enum {
     LMH_E_ALIGN = 4,       /* a pointer is not 16-byte aligned */
     LMH_E_UNSUPPORTED = 5, /* a valid request this build does not implement */
     LMH_E_WORKSPACE = 6,   /* workspace missing or smaller than required */
-    LMH_E_HIP = 7          /* the HIP runtime reported an error */
+    LMH_E_HIP = 7,         /* the HIP runtime reported an error */
+    LMH_E_SCRATCH = 8      /* more than the allocation-free entry point's scratch */
 };
 
 enum { LMH_F32 = 0, LMH_F16 = 1, LMH_BF16 = 2 };
@@ -404,6 +405,28 @@ int lmhead_logits_topk(const void* x, int x_dtype, int64_t M, const void* packed
                        const void* w_ref, int w_dtype, int topk, float* y, int64_t ldy,
                        int32_t* idx_out, float* val_out, int32_t* top1_out, void* workspace,
                        size_t ws_bytes, void* stream);
+
+/*
+ * lmhead_logits_topk_noalloc -- lmhead_logits_topk for callers that cannot
+ *   allocate device memory: code under HIP graph capture, tight serving
+ *   loops, harnesses that forbid hipMalloc.  Same arguments, result and
+ *   rules as lmhead_logits_topk, without the workspace: the call uses a
+ *   16 MiB scratch array inside the library instead (one per GPU, held until
+ *   the process ends; its device address is looked up on the call's first use
+ *   of a device, which must be the current device).  Calls no hipMalloc,
+ *   hipFree or other allocating routine.  A call whose working set -- the
+ *   workspace bytes it actually uses, i.e. the lmhead_logits_topk workspace
+ *   without the logits region when y is given or the fused one-row path runs
+ *   -- exceeds the scratch returns LMH_E_SCRATCH before any launch.  The
+ *   scratch keeps the last call's contents (none of it needs clearing); every
+ *   call on one GPU shares it, so calls that may overlap on one GPU (other
+ *   streams, other host threads) race and must be serialised by the caller.
+ */
+int lmhead_logits_topk_noalloc(const void* x, int x_dtype, int64_t M, const void* packed,
+                               int64_t V, int64_t K, int bits, int64_t group, int scale_dtype,
+                               const float* bias, const void* w_ref, int w_dtype, int topk,
+                               float* y, int64_t ldy, int32_t* idx_out, float* val_out,
+                               int32_t* top1_out, void* stream);
 
 /*
  * lmhead_stream_read -- a measurement aid, not part of the logits path: reads

@@ -18,7 +18,7 @@ import weight_only_quantized_lmhead_amd as lmh
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "lmhead.h")
 
-OK, E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_UNSUP, E_WS, E_HIP = range(8)
+OK, E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_UNSUP, E_WS, E_HIP, E_SCRATCH = range(9)
 F32, F16, BF16 = 0, 1, 2
 P = 0x10000  # a fake, 16-byte-aligned non-null address: never dereferenced on these paths
 
@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     L = lmh.lib()
-    for s in range(8):
+    for s in range(9):
         assert L.lmhead_status_string(s).startswith(b"LMH_")
     assert b"unknown" in L.lmhead_status_string(99)
 
@@ -334,3 +334,28 @@ def test_auto_path_validation():
     assert _auto(1, K=192) == (E_SHAPE, -1)
     assert _auto(1, K=384, G=96) == (E_UNSUP, -1)
     assert lmh.lib().lmhead_logits_auto_path(1, 1024, 4, 64, None) == E_NULL
+
+
+def test_logits_topk_noalloc_validation():
+    """The allocation-free decode entry validates like lmhead_logits_topk and
+    refuses, before any HIP call, a working set beyond its 16 MiB scratch."""
+    L = lmh.lib()
+
+    def call(**kw):
+        a = dict(x=P, xd=F16, M=1, packed=P, V=151936, K=1024, bits=4, G=64, sd=F16, bias=None,
+                 w=P, wd=F16, topk=8, y=P, ldy=151936)
+        a.update(kw)
+        return L.lmhead_logits_topk_noalloc(a["x"], a["xd"], a["M"], a["packed"], a["V"], a["K"],
+                                            a["bits"], a["G"], a["sd"], a["bias"], a["w"], a["wd"],
+                                            a["topk"], a["y"], a["ldy"], P, P, P, None)
+    assert call(bits=3) == E_UNSUP
+    assert call(topk=0) == E_SHAPE
+    assert call(topk=65) == E_SHAPE
+    assert call(xd=F32) == E_DTYPE
+    assert call(wd=7) == E_DTYPE
+    assert call(x=None) == E_NULL
+    assert call(packed=P + 4) == E_ALIGN
+    assert call(M=0) == OK
+    # 64 rows of 200000 logits kept in the scratch (no y): 51 MB > 16 MiB
+    assert call(M=64, V=200000, K=128, y=None, ldy=0) == E_SCRATCH
+    assert L.lmhead_status_string(E_SCRATCH).decode().startswith("LMH_E_SCRATCH")

@@ -77,6 +77,8 @@ def lib() -> ctypes.CDLL:
             "lmhead_logits_topk": (i32, [vp, i32, i64, vp, i64, i64, i32, i64, i32, vp, vp, i32, i32,
                                          vp, i64, vp, vp, vp, vp, sz, vp]),
             "lmhead_stream_read": (i32, [vp, sz, vp, vp]),
+            "lmhead_logits_topk_noalloc": (i32, [vp, i32, i64, vp, i64, i64, i32, i64, i32, vp, vp,
+                                                 i32, i32, vp, i64, vp, vp, vp, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -449,6 +451,22 @@ def prepare_embed(ids: torch.Tensor, packed: torch.Tensor, V: int, K: int, bits:
     args = (_ptr(ids), ids.numel(), _ptr(packed), V, K, bits, group, _DT[scale_dtype], _ptr(out),
             _DT[out.dtype], out.stride(0), _stream(ids))
     return PreparedCall("lmhead_embed", args, (ids, packed, out))
+
+
+def logits_topk_noalloc(x: torch.Tensor, packed: torch.Tensor, V: int, K: int, bits: int,
+                        group: int, scale_dtype: torch.dtype, w_ref: torch.Tensor, topk: int,
+                        idx: torch.Tensor, val: torch.Tensor, top1: torch.Tensor,
+                        bias: Optional[torch.Tensor] = None,
+                        out: Optional[torch.Tensor] = None) -> None:
+    """logits_topk without a workspace -- lmhead_logits_topk_noalloc (the
+    library's own scratch; nothing is allocated, the outputs are given)."""
+    _need_cuda(x, packed, w_ref, bias)
+    M = x.shape[0]
+    ldy = out.stride(0) if out is not None else 0
+    _check("lmhead_logits_topk_noalloc", lib().lmhead_logits_topk_noalloc(
+        _ptr(x), _DT[x.dtype], M, _ptr(packed), V, K, bits, group, _DT[scale_dtype], _ptr(bias),
+        _ptr(w_ref), _DT[w_ref.dtype], topk, _ptr(out), ldy, _ptr(idx), _ptr(val), _ptr(top1),
+        _stream(x)))
 
 
 class QuantizedHead:

@@ -7,6 +7,8 @@
 #include "lmhead.h"
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 namespace {
 
@@ -32,6 +34,37 @@ int check_layout(int64_t V, int64_t K, int bits, int64_t G) {
 
 int from_hip(hipError_t e) { return e == hipSuccess ? LMH_OK : LMH_E_HIP; }
 
+// Scratch of lmhead_logits_topk_noalloc, for callers that cannot allocate: a
+// file-scope device array (each GPU the library runs on holds its own copy
+// until the process ends).  Its device address is looked up once per device
+// (hipGetSymbolAddress, with that device current) and only that address is
+// passed to kernels: in host code the array's name is not a device address.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_of_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return LMH_E_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return LMH_E_UNSUPPORTED;
+    void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            void* q = nullptr;
+            if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return LMH_E_HIP;
+            g_scratch_addr[dev].store(q, std::memory_order_release);
+            p = q;
+        }
+    }
+    *out = p;
+    return LMH_OK;
+}
+
 // A `bits` argument: the code width, optionally with LMH_ZP (zero-point form).
 struct Width {
     int bits;
@@ -53,6 +86,9 @@ const char* lmhead_status_string(int status) {
     case LMH_E_UNSUPPORTED: return "LMH_E_UNSUPPORTED: combination not implemented";
     case LMH_E_WORKSPACE: return "LMH_E_WORKSPACE: workspace missing or too small";
     case LMH_E_HIP: return "LMH_E_HIP: the HIP runtime reported an error";
+    case LMH_E_SCRATCH:
+        return "LMH_E_SCRATCH: the call needs more than the 16 MiB scratch of the "
+               "allocation-free entry point";
     default: return "unknown lmhead status";
     }
 }
@@ -359,11 +395,14 @@ size_t lmhead_logits_topk_workspace_bytes(int64_t M, int64_t V, int64_t K, int x
                     topk_lists_region(M, V, topk) + round256(M * V * 4));
 }
 
-int lmhead_logits_topk(const void* x, int x_dtype, int64_t M, const void* packed, int64_t V,
-                       int64_t K, int bits, int64_t group, int scale_dtype, const float* bias,
-                       const void* w_ref, int w_dtype, int topk, float* y, int64_t ldy,
-                       int32_t* idx_out, float* val_out, int32_t* top1_out, void* workspace,
-                       size_t ws_bytes, void* stream) {
+// lmhead_logits_topk on a given workspace.  `exact`: the workspace may be
+// the exact bytes this call uses (the logits region only when y is NULL on the
+// unfused path); otherwise it must hold lmhead_logits_topk_workspace_bytes.
+static int logits_topk_impl(const void* x, int x_dtype, int64_t M, const void* packed, int64_t V,
+                            int64_t K, int bits, int64_t group, int scale_dtype, const float* bias,
+                            const void* w_ref, int w_dtype, int topk, float* y, int64_t ldy,
+                            int32_t* idx_out, float* val_out, int32_t* top1_out, void* workspace,
+                            size_t ws_bytes, void* stream, bool exact, size_t* need_out = nullptr) {
     int rc = check_layout(V, K, bits & ~LMH_ZP, group);
     if (rc != LMH_OK) return rc;
     if (x_dtype != F16 && x_dtype != BF16) return LMH_E_DTYPE;
@@ -381,10 +420,6 @@ int lmhead_logits_topk(const void* x, int x_dtype, int64_t M, const void* packed
     if (((uintptr_t)w_ref & 3u) != 0 || (y && ((uintptr_t)y & 3u) != 0) ||
         (bias && ((uintptr_t)bias & 3u) != 0))
         return LMH_E_ALIGN;
-    const size_t need = lmhead_logits_topk_workspace_bytes(M, V, K, x_dtype, topk);
-    if (!workspace || ws_bytes < need) return LMH_E_WORKSPACE;
-    if (!aligned16(workspace)) return LMH_E_ALIGN;
-    char* ws = (char*)workspace;
     const int64_t xws = round256((int64_t)lmhead_logits_workspace_bytes(M, K, x_dtype));
     const int64_t tws = topk_lists_region(M, V, topk);
     // one activation row through the GEMV: its epilogue writes each 64-row
@@ -392,7 +427,18 @@ int lmhead_logits_topk(const void* x, int x_dtype, int64_t M, const void* packed
     // (no separate pass over the logits; y is stored only when given)
     // (the GEMV's top-K epilogue exists for one activation row only)
     const bool gemv_one = M == 1 && K <= lmh::kGemvMaxMK;
-    if (gemv_one && lmh::topk_fused_ok(V, topk)) {
+    const bool fused = gemv_one && lmh::topk_fused_ok(V, topk);
+    const size_t need =
+        exact ? (size_t)(xws + tws + (fused || y ? 0 : round256(M * V * 4)))
+              : lmhead_logits_topk_workspace_bytes(M, V, K, x_dtype, topk);
+    if (need_out) {
+        *need_out = need;
+        return LMH_OK;
+    }
+    if (!workspace || ws_bytes < need) return LMH_E_WORKSPACE;
+    if (!aligned16(workspace)) return LMH_E_ALIGN;
+    char* ws = (char*)workspace;
+    if (fused) {
         const int T = (int)(topk + 1 <= V ? topk + 1 : V);
         lmh::u64* lists = (lmh::u64*)(ws + xws);
         rc = logits_impl(x, x_dtype, M, packed, V, K, bits, group, scale_dtype, bias, y, F32, ldy,
@@ -411,6 +457,37 @@ int lmhead_logits_topk(const void* x, int x_dtype, int64_t M, const void* packed
     return from_hip(lmh::launch_topk_rescore(x, x_dtype, (int)M, w_ref, w_dtype, V, K, yy, ly, topk,
                                              idx_out, val_out, top1_out, ws + xws,
                                              (hipStream_t)stream));
+}
+
+int lmhead_logits_topk(const void* x, int x_dtype, int64_t M, const void* packed, int64_t V,
+                       int64_t K, int bits, int64_t group, int scale_dtype, const float* bias,
+                       const void* w_ref, int w_dtype, int topk, float* y, int64_t ldy,
+                       int32_t* idx_out, float* val_out, int32_t* top1_out, void* workspace,
+                       size_t ws_bytes, void* stream) {
+    return logits_topk_impl(x, x_dtype, M, packed, V, K, bits, group, scale_dtype, bias, w_ref,
+                            w_dtype, topk, y, ldy, idx_out, val_out, top1_out, workspace, ws_bytes,
+                            stream, false);
+}
+
+int lmhead_logits_topk_noalloc(const void* x, int x_dtype, int64_t M, const void* packed,
+                               int64_t V, int64_t K, int bits, int64_t group, int scale_dtype,
+                               const float* bias, const void* w_ref, int w_dtype, int topk,
+                               float* y, int64_t ldy, int32_t* idx_out, float* val_out,
+                               int32_t* top1_out, void* stream) {
+    // validation and the bytes this call needs, before any HIP call
+    size_t need = 0;
+    int rc = logits_topk_impl(x, x_dtype, M, packed, V, K, bits, group, scale_dtype, bias, w_ref,
+                              w_dtype, topk, y, ldy, idx_out, val_out, top1_out, nullptr, 0, stream,
+                              true, &need);
+    if (rc != LMH_OK) return rc;
+    if (M == 0 || V == 0) return LMH_OK;
+    if (need > kScratchBytes) return LMH_E_SCRATCH;
+    void* ws = nullptr;
+    rc = scratch_of_current_device(&ws);
+    if (rc != LMH_OK) return rc;
+    return logits_topk_impl(x, x_dtype, M, packed, V, K, bits, group, scale_dtype, bias, w_ref,
+                            w_dtype, topk, y, ldy, idx_out, val_out, top1_out, ws, kScratchBytes,
+                            stream, true);
 }
 
 int lmhead_stream_read(const void* src, size_t bytes, void* sink, void* stream) {
