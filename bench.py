@@ -49,8 +49,9 @@ def algorithmic_bytes(M, V, K, bits, G):
 
 # Sources whose change invalidates a recorded traffic measurement of the
 # logits kernels.
-TRAFFIC_SOURCES = ["weight_only_quantized_lmhead_amd/csrc/logits.hip",
-                   "weight_only_quantized_lmhead_amd/csrc/logits_kernels.h",
+TRAFFIC_SOURCES = ["weight_only_quantized_lmhead_amd/csrc/gemv.hip",
+                   "weight_only_quantized_lmhead_amd/csrc/gemv_kernels.h",
+                   "weight_only_quantized_lmhead_amd/csrc/logits_common.h",
                    "weight_only_quantized_lmhead_amd/csrc/lmh_internal.h",
                    "weight_only_quantized_lmhead_amd/build.py"]
 
@@ -101,7 +102,9 @@ def _short_kernel(name: str) -> str:
                 for t, v in re.findall(r"L([ib])(\d+)E", targs + "E")]
         return f"{base}<{','.join(vals)}>"
     name = name.replace("void ", "").replace("lmh::(anonymous namespace)::", "")
-    return name.split("(")[0][:60]
+    name = name.split("(")[0]
+    return (name.replace(" ", "") if name.startswith(("gemv_", "mfma_", "quant_", "embed_", "topk_"))
+            else name[:60])
 
 
 def summarize(args) -> int:
@@ -148,19 +151,27 @@ def summarize(args) -> int:
             return vals
 
         fv, wv = per_kernel(args.fetch, "FETCH_SIZE"), per_kernel(args.write, "WRITE_SIZE")
-        # the largest copy dispatches are the packed-head clones: blob bytes each
-        copy_f = max(fv["__amd_rocclr_copyBuffer"])
-        copy_w = max(wv["__amd_rocclr_copyBuffer"])
-        kf, kw = blob / 1024 / copy_f, blob / 1024 / copy_w
+        # reads: the read-only stream kernel reads exactly the packed head once
+        # per dispatch (and writes nothing); writes: the copies that clone the
+        # zero-point packed head (their written bytes are that head's size)
+        head = lmh.packed_bytes(w.V, w.K, w.bits, w.group)
+        rd = [v for k, v in fv.items() if k.startswith("stream_read_kernel")][0]
+        copy_f = statistics.mean(rd)
+        kf = head / 1024 / copy_f
+        clones = [v for v in wv["__amd_rocclr_copyBuffer"] if abs(v * 1024 / blob - 1) < 0.03]
+        copy_w = statistics.mean(clones) if clones else float("nan")
+        kw = blob / 1024 / copy_w if clones else 1.0
         t = ["## HBM traffic (rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE)\n",
-             f"Calibration: the copy kernel that clones the {blob}-byte zero-point packed head reads "
-             f"FETCH_SIZE = {copy_f:.1f} KiB and WRITE_SIZE = {copy_w:.1f} KiB per dispatch, so "
-             f"bytes read = FETCH_SIZE x {kf:.5f} x 1024 and bytes written = WRITE_SIZE x {kw:.5f} x 1024.\n",
+             f"Calibration: the read-only stream kernel (lmhead_stream_read over the {head}-byte packed "
+             f"head) reads FETCH_SIZE = {copy_f:.1f} KiB per dispatch, and the copies that clone the "
+             f"{blob}-byte zero-point packed head write WRITE_SIZE = {copy_w:.1f} KiB, so bytes read = "
+             f"FETCH_SIZE x {kf:.5f} x 1024 and bytes written = WRITE_SIZE x {kw:.5f} x 1024.\n",
              "| kernel | dispatches | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | read (B) | written (B) | total (B) |",
              "|---|---|---|---|---|---|---|"]
         recs = []
         for k in sorted(fv):
-            if not k.startswith(("gemv_kernel", "mfma", "topk", "quant_", "embed_")):
+            if not k.startswith(("gemv_kernel", "mfma", "topk", "quant_", "embed_", "stream_read",
+                                 "dense_kernel", "x_to_f16")):
                 continue
             f_ = statistics.mean(fv[k])
             w_ = statistics.mean(wv.get(k, [0.0]))
@@ -297,8 +308,9 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--calls", type=int, default=200,
-                    help="calls per per-call timing loop (at least 200 whatever --steps is)")
+    ap.add_argument("--calls", type=int, default=None,
+                    help="calls per per-call timing loop (default 200 whatever --steps is; "
+                         "profiled runs may ask for fewer)")
     ap.add_argument("--workload", default=None, help="synthetic workload name (default: the headline)")
     ap.add_argument("--ms", default=None, help="comma-separated M list (default: the workload's)")
     ap.add_argument("--topk", type=int, default=8)
@@ -344,7 +356,7 @@ def main() -> int:
     Ms = [int(m) for m in args.ms.split(",")] if args.ms else list(w.Ms)
     TD = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
     sdt = TD[w.scale_dtype]
-    ncalls = max(200, args.calls)
+    ncalls = 200 if args.calls is None else max(1, args.calls)
 
     def to_dev(a, dt):
         if dt == "bf16":
@@ -561,8 +573,11 @@ def main() -> int:
 
     m1 = per_call[f"M={Ms[0]}"]
     value = m1["us"]
-    # the symmetric GEMV without the top-K epilogue (template flags ZP, TK)
-    tr = recorded_traffic(w.name, "gemv_kernel<", "") if m1["kernel"] == "gemv" else None
+    # the symmetric GEMV without the top-K epilogue (template flags ZP, TK, and
+    # the activation source: 0 fp16 through the scalar unit, 2 bf16 converted)
+    xm = "2" if w.x_dtype == "bf16" else "0"
+    tr = (recorded_traffic(w.name, "gemv_kernel<", f",false,false,{xm}>")
+          if m1["kernel"] == "gemv" else None)
     roofline = {
         "bound": "hbm", "kernel": f"lmh {m1['kernel']}, M={Ms[0]}", "achieved": m1["GB/s"],
         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": m1["frac_hbm_peak"],

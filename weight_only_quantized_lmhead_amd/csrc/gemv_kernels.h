@@ -76,14 +76,18 @@ __device__ __forceinline__ void unpack_i4_free(uint32_t w, uint32_t magic, const
                                    sixteenth, zc.hi);
 }
 
-// An ordering point for the scheduler: `r` counts as rewritten here, after
-// `dep` is available, so nothing computed from r can move above the
-// instruction that produced dep.  Used to unpack and read one 32-column chunk
-// at a time (the scheduler otherwise unpacks every code of a superchunk first
-// and keeps them all live).
+// Ordering points for the scheduler (empty volatile statements keep their
+// order among themselves): order_after makes `r` count as rewritten after
+// `dep` is available, so nothing computed from r moves above it; used_here
+// makes `v` count as read at this point, so its computation cannot sink below
+// it.  Together they run one 32-column chunk at a time -- its code words
+// unpacked after the previous chunk's dot products, its dot products before
+// the next chunk's unpacking (the scheduler otherwise unpacks every code of a
+// superchunk first, or sinks the dot products, and keeps everything live).
 __device__ __forceinline__ void order_after(uint32_t& r, float dep) {
     asm volatile("" : "+v"(r) : "v"(dep));
 }
+__device__ __forceinline__ void used_here(float v) { asm volatile("" ::"v"(v)); }
 
 // Largest |x| of eight bf16 values, as bits (the order of non-negative bf16
 // bit patterns is the order of their values).
@@ -232,6 +236,10 @@ __attribute__((amdgpu_waves_per_eu(gemv_occupancy<MM, XM, NCB>()))) void gemv_ke
         float dep = acc[0];
 #pragma unroll
         for (int j = 0; j < CPS; ++j) {
+            // LDS-staged x: its reads for this chunk pass the same ordering
+            // point (the scalar loads of XM = 0 need none)
+            uint32_t xo = (uint32_t)(xc + 16 * j) * 4u;  // byte offset of the chunk's x
+            if constexpr (XM != 0) order_after(xo, dep);
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 h2 p0, p1, p2, p3;
@@ -250,7 +258,9 @@ __attribute__((amdgpu_waves_per_eu(gemv_occupancy<MM, XM, NCB>()))) void gemv_ke
                 const int xi = xc + 16 * j + 4 * t;  // columns span*c + 32j + 8t
 #pragma unroll
                 for (int m = 0; m < MM; ++m) {
-                    const uint4 xv = *(const uint4*)((XM == 0 ? xh : xl) + m * Kh + xi);
+                    const uint4 xv =
+                        XM == 0 ? *(const uint4*)(xh + m * Kh + xi)
+                                : *(const uint4*)((const char*)xl + xo + 16u * t + 2u * (uint32_t)(m * K));
                     float a = part[m][j / CPG][t % NA];
                     a = __builtin_amdgcn_fdot2(p0, __builtin_bit_cast(h2, xv.x), a, false);
                     a = __builtin_amdgcn_fdot2(p1, __builtin_bit_cast(h2, xv.y), a, false);
@@ -259,6 +269,10 @@ __attribute__((amdgpu_waves_per_eu(gemv_occupancy<MM, XM, NCB>()))) void gemv_ke
                     part[m][j / CPG][t % NA] = a;
                 }
             }
+#pragma unroll
+            for (int m = 0; m < MM; ++m)
+#pragma unroll
+                for (int a = 0; a < NA; ++a) used_here(part[m][j / CPG][a]);
         }
 #pragma unroll
         for (int g = 0; g < GPS; ++g) {
@@ -290,6 +304,7 @@ __attribute__((amdgpu_waves_per_eu(gemv_occupancy<MM, XM, NCB>()))) void gemv_ke
         load(A, c0);
         if constexpr (XM != 0) stage_x();
         gs = scale_to_f32(A.s[0], sbf16);
+#pragma unroll 1
         for (int c = c0; c < cend; ++c) {
             if (c > c0) load(A, c);
             compute(A, c);
@@ -300,6 +315,7 @@ __attribute__((amdgpu_waves_per_eu(gemv_occupancy<MM, XM, NCB>()))) void gemv_ke
         if constexpr (XM != 0) stage_x();
         gs = scale_to_f32(A.s[0], sbf16);
         int c = c0;
+#pragma unroll 1
         for (; c + 1 < cend; c += 2) {
             load(B, c + 1);
             compute(A, c);

@@ -8,27 +8,52 @@ namespace lmh {
 namespace {
 
 // ---------------------------------------------------------------------------
-// bf16 x -> fp16 x * 2^-e, one workgroup per row.
+// bf16 x -> fp16 x * 2^-e, one workgroup per row: max |x| of the row (16-byte
+// loads; the order of non-negative bf16 bit patterns is the order of their
+// values), e such that max |x| * 2^-e lies in [2^14, 2^15), then every
+// element rounded once to fp16 (the same conversion the GEMV does in LDS).
 __global__ __launch_bounds__(256) void x_to_f16_kernel(const uint16_t* __restrict__ xb, int K,
                                                        _Float16* __restrict__ xh,
                                                        int* __restrict__ xexp) {
-    __shared__ float red[4];
+    __shared__ uint32_t red[4];
     const int m = blockIdx.x;
-    const uint16_t* row = xb + (int64_t)m * K;
-    float amax = 0.0f;
-    for (int k = threadIdx.x; k < K; k += 256) amax = fmaxf(amax, fabsf(__uint_as_float((uint32_t)row[k] << 16)));
-    for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+    const int P = K >> 3;  // 16-byte pieces per row (K is a multiple of 64)
+    const uint4* row = (const uint4*)(xb + (int64_t)m * K);
+    uint32_t mx = 0;
+    for (int i = threadIdx.x; i < P; i += 256) {
+        const uint4 v = row[i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t w = word_of(v, j);
+            mx = max(mx, max(w & 0x7FFFu, (w >> 16) & 0x7FFFu));
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
     __syncthreads();
-    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    mx = max(max(red[0], red[1]), max(red[2], red[3]));
+    const float amax = __uint_as_float(mx << 16);
     int e = 0;
     if (amax > 0.0f) {
         int E;
         frexpf(amax, &E);  // amax = f * 2^E, f in [0.5, 1)
         e = E - 15;        // amax * 2^-e in [2^14, 2^15)
     }
-    for (int k = threadIdx.x; k < K; k += 256)
-        xh[(int64_t)m * K + k] = (_Float16)ldexpf(__uint_as_float((uint32_t)row[k] << 16), -e);
+    uint4* out = (uint4*)(xh + (int64_t)m * K);
+    for (int i = threadIdx.x; i < P; i += 256) {
+        const uint4 v = row[i];
+        uint32_t o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t w = word_of(v, j);
+            const _Float16 lo = (_Float16)ldexpf(__uint_as_float(w << 16), -e);
+            const _Float16 hi = (_Float16)ldexpf(__uint_as_float(w & 0xFFFF0000u), -e);
+            o[j] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+                   ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+        }
+        out[i] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
     if (threadIdx.x == 0) xexp[m] = e;
 }
 // ---------------------------------------------------------------------------
