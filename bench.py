@@ -192,6 +192,74 @@ def summarize(args) -> int:
     return 0
 
 
+SQ_PASSES = [
+    ["SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS",
+     "SQ_ACTIVE_INST_VMEM", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_WAIT_INST_ANY", "SQ_WAIT_ANY",
+     "GRBM_GUI_ACTIVE"],
+    ["SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_VMEM_RD", "SQ_INSTS_VMEM_WR",
+     "SQ_INSTS_SALU", "SQ_LDS_BANK_CONFLICT", "SQ_WAVES", "GRBM_GUI_ACTIVE"],
+]
+
+
+def summarize_sq(args) -> int:
+    """Write a profiles/ summary of SQ counters per logits kernel from the
+    counter_collection.csv files of the SQ_PASSES runs (--sq, one per pass)."""
+    import csv
+    import statistics
+
+    vals = {}  # (kernel, grid) -> counter -> [values]
+    for path in args.sq:
+        for r in csv.DictReader(open(path)):
+            k = _short_kernel(r["Kernel_Name"])
+            if not k.startswith(("gemv_kernel", "mfma", "stream_read")):
+                continue
+            key = f"{k} grid {r['Grid_Size']}"
+            vals.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    out = [f"# SQ counters of the logits kernels ({args.workload or 'headline'} head), one MI355X\n",
+           "Commands (from the repository root; `export TMPDIR=/tmp` first):\n", "```"]
+    out += args.cmd
+    out += ["```\n",
+            "Per-dispatch means over every dispatch of a kernel (one kernel per M; the grid says which). "
+            "Derived columns, with the kernel's GPU cycles = GRBM_GUI_ACTIVE / 8 (the counter is summed "
+            "over the 8 XCDs) and 1024 SIMDs: MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (cycles x 1024) "
+            "(matches 16 cycles per 16x16x32 fp16 MFMA x SQ_INSTS_MFMA); VALU busy = 4 x (SQ_INSTS_VALU - "
+            "SQ_INSTS_MFMA) / (cycles x 1024) (a wave64 VALU instruction holds its SIMD 4 cycles); LDS "
+            "and VMEM active = SQ_ACTIVE_INST_* / SQ_WAVE_CYCLES; wait = SQ_WAIT_INST_ANY / "
+            "SQ_WAVE_CYCLES; VALU/MFMA = non-MFMA VALU instructions per MFMA; bank conflicts per LDS "
+            "instruction.\n",
+            "| kernel | MFMA busy | VALU busy | LDS active | VMEM active | wait | VALU/MFMA | LDS instr/MFMA | bank conflicts/LDS instr | waves |",
+            "|---|---|---|---|---|---|---|---|---|---|"]
+    for key in sorted(vals):
+        c = {n: statistics.mean(v) for n, v in vals[key].items()}
+        g = lambda n: c.get(n, float("nan"))
+        # GRBM_GUI_ACTIVE is summed over the 8 XCDs, the MFMA busy cycles over
+        # the 1024 SIMDs; SQ_INSTS_VALU counts MFMA instructions too, and one
+        # VALU instruction of a wave occupies its SIMD for 4 cycles
+        gpu_cycles = g("GRBM_GUI_ACTIVE") / 8
+        busy = g("SQ_VALU_MFMA_BUSY_CYCLES") / (gpu_cycles * 1024)
+        mf = g("SQ_INSTS_MFMA")
+        valu_busy = (g("SQ_INSTS_VALU") - mf) * 4 / (gpu_cycles * 1024)
+        wc = g("SQ_WAVE_CYCLES")
+        out.append(f"| `{key}` | {busy:.1%} | {valu_busy:.1%} | "
+                   f"{g('SQ_ACTIVE_INST_LDS') / wc:.1%} | {g('SQ_ACTIVE_INST_VMEM') / wc:.1%} | "
+                   f"{g('SQ_WAIT_INST_ANY') / wc:.1%} | "
+                   f"{(g('SQ_INSTS_VALU') - mf) / mf if mf else float('nan'):.2f} | "
+                   f"{g('SQ_INSTS_LDS') / mf if mf else float('nan'):.2f} | "
+                   f"{g('SQ_LDS_BANK_CONFLICT') / max(g('SQ_INSTS_LDS'), 1):.2f} | {g('SQ_WAVES'):.0f} |")
+    out.append("\nRaw means:\n")
+    out.append("| kernel | " + " | ".join(sorted({n for v in vals.values() for n in v})) + " |")
+    names = sorted({n for v in vals.values() for n in v})
+    out.append("|---|" + "---|" * len(names))
+    for key in sorted(vals):
+        out.append(f"| `{key}` | " + " | ".join(
+            f"{statistics.mean(vals[key][n]):.4g}" if n in vals[key] else "" for n in names) + " |")
+    text = "\n".join(out) + "\n"
+    with open(args.out, "w") as fh:
+        fh.write(text)
+    print(text)
+    return 0
+
+
 def decode_agreement(args, w, lmh, synth, to_dev, blob, Wref, sdt, dev):
     """Top-1 agreement of the quantized head with the unquantized 16-bit weight
     (lmhead_dense_logits: exact 16-bit products, fp32 sums) over N seeded
@@ -332,9 +400,15 @@ def main() -> int:
     ap.add_argument("--write", help="counter_collection.csv of a --pmc WRITE_SIZE run")
     ap.add_argument("--out", help="summary file to write")
     ap.add_argument("--cmd", action="append", default=[], help="command line to record (repeatable)")
+    ap.add_argument("--summarize-sq", action="store_true",
+                    help="write a profiles/ summary of SQ counters (--sq files) instead of timing")
+    ap.add_argument("--sq", action="append", default=[],
+                    help="counter_collection.csv of one SQ_PASSES run (repeatable)")
     args = ap.parse_args()
     if args.summarize:
         return summarize(args)
+    if args.summarize_sq:
+        return summarize_sq(args)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the head would be "
