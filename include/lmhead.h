@@ -275,8 +275,9 @@ size_t lmhead_logits_workspace_bytes(int64_t M, int64_t K, int x_dtype);
  *   over up to 8 waves per 64-row block); larger M runs a 16x16x32 fp16 MFMA kernel (its
  *   code unpacking is shared by all activation rows), chosen from
  *   measurements: for K <= 1024 and G >= 64, the activation-resident one
- *   from M = 33 on; otherwise for K <= 1024 the LDS-staged one for
- *   M = 17..32 and for int8 heads, else the register-fed one; for K > 1024,
+ *   from M = 33 on (int4 heads: from M = 17 on); otherwise for K <= 1024 the
+ *   LDS-staged one for M = 17..32 and for int8 heads, else the register-fed
+ *   one; for K > 1024,
  *   the register-fed one for
  *   M = 25..32, else the LDS-staged one (see lmhead_logits_path).  Every
  *   MFMA kernel runs the same per-group MFMA chains and fp32 scale FMAs in
@@ -297,8 +298,9 @@ int lmhead_logits(const void* x, int x_dtype, int64_t M, const void* packed, int
  *   loaded straight into registers (any M), 3 = the MFMA kernel with every
  *   operand staged in LDS by direct global-to-LDS loads (any M; 32 or 64
  *   activation rows per workgroup), 4 = the activation-resident MFMA kernel
- *   (a 64-row activation tile held in LDS for the workgroup's life, weights
- *   streamed through registers; K <= 1024, else LMH_E_UNSUPPORTED).  All
+ *   (a 32-row (M <= 32) or 64-row activation tile held in LDS for the
+ *   workgroup's life, weights streamed through registers; K <= 1024, else
+ *   LMH_E_UNSUPPORTED).  All
  *   kernels compute the same function; this entry point exists to test and
  *   time each of them on the same shapes.
  */

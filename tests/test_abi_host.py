@@ -307,14 +307,16 @@ def _auto(M, K=1024, bits=4, G=64):
 
 def test_auto_path_choice():
     # the automatic kernel choice, host only: the GEMV for one or two rows, the
-    # activation-resident kernel beyond 32 rows when the tile fits (K <= 1024,
-    # G >= 64), the LDS-staged kernel for 17..32 rows and for int8 heads, and
-    # the register-fed kernel for 3..16 rows of an int4 head
+    # activation-resident kernel when the tile fits (K <= 1024, G >= 64)
+    # beyond 32 rows, and from 17 rows on for int4 heads; the LDS-staged
+    # kernel for int8 heads up to 32 rows, and the register-fed kernel for
+    # 3..16 rows of an int4 head
     GEMV, MFMA, LDS, XRES = (lmh.PATH_GEMV, lmh.PATH_MFMA, lmh.PATH_MFMA_LDS,
                              lmh.PATH_MFMA_XRES)
-    for M, want in [(1, GEMV), (2, GEMV), (3, MFMA), (16, MFMA), (17, LDS), (32, LDS),
+    for M, want in [(1, GEMV), (2, GEMV), (3, MFMA), (16, MFMA), (17, XRES), (32, XRES),
                     (33, XRES), (64, XRES), (256, XRES), (65535, XRES)]:
         assert _auto(M) == (OK, want), M
+    assert _auto(24, G=32) == (OK, LDS)               # 32-column groups: no resident tile
     for M, want in [(1, GEMV), (2, GEMV), (3, LDS), (32, LDS), (33, XRES), (256, XRES)]:
         assert _auto(M, bits=8, G=128) == (OK, want), M
     assert _auto(256, G=32) == (OK, LDS)              # 32-column groups: no resident tile

@@ -220,18 +220,21 @@ size_t lmhead_logits_workspace_bytes(int64_t M, int64_t K, int x_dtype) {
 //   - when K <= 1024 and G >= 64, the activation-resident kernel from 33
 //     rows on (int4 M = 33..64: 29-33 us against 38-42 for the LDS-staged
 //     kernel's 64-row tiles; M = 96..256 6-10 % faster; int8 M = 40..256:
-//     0-14 % faster; with 32-column groups it runs out of registers);
-//   - when K <= 1024: the LDS-staged kernel for 17..32 rows (int4: 25-28
-//     us against 30-32 activation-resident) and for every M >= 3 on int8
-//     heads (int8 2..32 rows: 15-25 % faster than activation-resident),
-//     else the register-fed kernel (3..16 rows on int4 heads; the
-//     LDS-staged one is 4-6 % slower there);
+//     0-14 % faster; with 32-column groups it runs out of registers), and
+//     on int4 heads from 17 rows on (its 32-row tile: 7.6-7.8 us against
+//     8.3-9.2 on the 50304 x 512 g64 head, within 3 % of the LDS-staged
+//     kernel on the 151936 x 1024 g64 and g128 heads);
+//   - when K <= 1024: the LDS-staged kernel for 17..32 rows on the other
+//     heads and for every M >= 3 on int8 heads (int8 3..32 rows: 4-8 %
+//     faster than the activation-resident kernel's 32-row tile), else the
+//     register-fed kernel (3..16 rows on int4 heads; the LDS-staged one is
+//     2-15 % slower there);
 //   - when K > 1024: the register-fed kernel for 25..32 rows (3 % faster),
 //     else the LDS-staged one (3..24 rows: 1.5-3 % faster; beyond 32 rows
 //     the register-fed kernel would read the weights once per 32 rows).
 static int auto_path(int64_t M, int64_t K, int bits, int64_t group) {
     if (M <= lmh::kGemvAutoMaxM && M <= lmh::kGemvMaxM && M * K <= lmh::kGemvMaxMK) return 1;
-    if (M > 32 && lmh::xres_fits(K) && group >= 64) return 4;
+    if (M > 16 && lmh::xres_fits(K) && group >= 64 && (M > 32 || bits == 4)) return 4;
     const bool narrow = K <= 1024;
     const bool lds = narrow ? (M > 16 || bits == 8) : !(M > 24 && M <= 32);
     return lds ? 3 : 2;

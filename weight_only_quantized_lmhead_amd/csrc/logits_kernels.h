@@ -600,13 +600,15 @@ constexpr int xres_waves() { return NT_ == 4 ? 8 : 16; }
 
 // SB: the scale type as a template flag (0 fp16, 1 bf16), so that the per-step
 // scale conversion is one instruction per scale and carries no select.
-template <int BITS, int GPS, int D, bool TR, int OUT, bool ZP, int NT_, int SB>
+// MT_: activation tiles of 16 rows resident in LDS (4: a 64-row tile, 2: a
+// 32-row tile for M <= 32, half the LDS).
+template <int BITS, int GPS, int D, bool TR, int OUT, bool ZP, int NT_, int SB, int MT_>
 __global__ __launch_bounds__(64 * xres_waves<NT_>(), 1) void mfma_xres_kernel(
     const uint4* __restrict__ wq, const uint16_t* __restrict__ sc, const uint8_t* __restrict__ zq,
     const _Float16* __restrict__ x,
     const int* __restrict__ xexp, const float* __restrict__ bias, void* __restrict__ y,
     int64_t ldy, int V, int K, int M, int NB, int NC, int NG, int SPG, int NMT, int VRX) {
-    constexpr int MT = 4, NT = NT_, ROWS = 64;
+    constexpr int MT = MT_, NT = NT_, ROWS = 16 * MT_;
     constexpr int WAVES = xres_waves<NT_>(), NTH = 64 * WAVES;
     constexpr int PARTS = 4 / NT;  // a row block's 64 columns in PARTS units of 16 NT
     constexpr int SPAN = BITS == 4 ? 128 : 64;
@@ -626,13 +628,6 @@ __global__ __launch_bounds__(64 * xres_waves<NT_>(), 1) void mfma_xres_kernel(
     // piece p of row m sits at p ^ (m & 15)
     constexpr int PP = kXresMaxK / 8;
     const int P = K / 8;                       // 16-byte pieces per row
-    for (int i = threadIdx.x; i < ROWS * P; i += NTH) {
-        const int m = i / P, p = i - m * P;
-        const int mr = min(m0 + m, M - 1);     // rows past M: any valid row, never stored
-        xs[m * PP + (p ^ (m & 15))] = *(const uint4*)(x + (int64_t)mr * K + p * 8);
-    }
-    if (xexp && threadIdx.x < ROWS) xe_s[threadIdx.x] = xexp[min(m0 + (int)threadIdx.x, M - 1)];
-    __syncthreads();
 
     const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, t = lane >> 4;
@@ -655,7 +650,6 @@ __global__ __launch_bounds__(64 * xres_waves<NT_>(), 1) void mfma_xres_kernel(
     const int nunit = (rb1 - rb0) * PARTS;
     const int nblk = nunit > wv ? (nunit - wv + WAVES - 1) / WAVES : 0;
     const int nsteps = nblk * NC;
-    if (nsteps == 0) return;
 
     // ring stage: the NT slots, and per group and column tile the scales of the
     // lane's vocabulary rows: row 16 nt + r (one 2-byte load), or with TR the
@@ -685,6 +679,24 @@ __global__ __launch_bounds__(64 * xres_waves<NT_>(), 1) void mfma_xres_kernel(
         }
     };
 
+    // the ring's first steps are requested before the activation tile is
+    // staged, so that their latency overlaps the staging (where the ring's
+    // registers fit beside the staging loop's without spilling: the 32-row
+    // tile, and the symmetric int4 fp32-output kernels)
+    constexpr bool kEarly = MT_ == 2 || (BITS == 4 && !ZP && OUT == F32);
+    if (kEarly && nsteps > 0) {
+#pragma unroll
+        for (int p = 0; p < D; ++p) load(p, p);
+    }
+    for (int i = threadIdx.x; i < ROWS * P; i += NTH) {
+        const int m = i / P, p = i - m * P;
+        const int mr = min(m0 + m, M - 1);     // rows past M: any valid row, never stored
+        xs[m * PP + (p ^ (m & 15))] = *(const uint4*)(x + (int64_t)mr * K + p * 8);
+    }
+    if (xexp && threadIdx.x < ROWS) xe_s[threadIdx.x] = xexp[min(m0 + (int)threadIdx.x, M - 1)];
+    __syncthreads();
+    if (nsteps == 0) return;
+
     f4 acc[MT][NT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -692,8 +704,10 @@ __global__ __launch_bounds__(64 * xres_waves<NT_>(), 1) void mfma_xres_kernel(
         for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = (f4){0.f, 0.f, 0.f, 0.f};
     const uint32_t magic = 0x64006400u;
 
+    if constexpr (!kEarly) {
 #pragma unroll
-    for (int p = 0; p < D; ++p) load(p, p);
+        for (int p = 0; p < D; ++p) load(p, p);
+    }
     int ci = 0, cc = 0;  // block index within the wave's list, superchunk of step s
     for (int sb = 0; sb < nsteps; sb += D) {
 #pragma unroll
@@ -853,7 +867,7 @@ __global__ __launch_bounds__(64 * xres_waves<NT_>(), 1) void mfma_xres_kernel(
                         for (int nt = 0; nt < NT; ++nt)
                             yrow[16 * nt] = to_out<OUT>(acc[mt][nt][e] + bv[nt]);
                     };
-                    if (M - m0 >= 64) {
+                    if (M - m0 >= ROWS) {
 #pragma unroll
                         for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
@@ -987,7 +1001,7 @@ hipError_t mfma_lds_dispatch(const LogitsArgs& a, hipStream_t st) {
     return mfma_lds_dispatch_mt<BITS, 4, 2, 4, OUT, ZP>(a, st);
 }
 
-template <int BITS, int D, bool TR, int OUT, bool ZP, int NT_>
+template <int BITS, int D, bool TR, int OUT, bool ZP, int NT_, int MT_>
 hipError_t mfma_xres_dispatch_d(const LogitsArgs& a, hipStream_t st) {
     const int NB = (int)((a.V + 63) / 64);
     const int NC = (int)(a.K / span_of(BITS));
@@ -995,12 +1009,12 @@ hipError_t mfma_xres_dispatch_d(const LogitsArgs& a, hipStream_t st) {
     const int gps = gps_of(BITS, a.G);
     const int SPG = gps == 1 ? (int)(a.G / span_of(BITS)) : 1;
     const Regions<BITS> rg(a, ZP);
-    const int NMT = (a.M + 63) / 64;
+    const int NMT = (a.M + 16 * MT_ - 1) / (16 * MT_);
     // one workgroup per CU: per XCD, NMT activation tiles x VRX vocabulary ranges
     const int VRX = NMT >= 32 ? 1 : 32 / NMT;
     const dim3 grid((unsigned)(8 * NMT * VRX));
 #define LMH_XRES_SB(G_, SB_)                                                                      \
-    hipLaunchKernelGGL((mfma_xres_kernel<BITS, G_, D, TR, OUT, ZP, NT_, SB_>), grid,             \
+    hipLaunchKernelGGL((mfma_xres_kernel<BITS, G_, D, TR, OUT, ZP, NT_, SB_, MT_>), grid,        \
                        dim3(64 * xres_waves<NT_>()), 0, st,                                       \
                        rg.wq, rg.sc, rg.zq,                                                       \
                        (const _Float16*)a.x, a.xexp, a.bias, a.y, a.ldy, (int)a.V, (int)a.K, a.M, \
@@ -1028,16 +1042,20 @@ hipError_t mfma_dispatch(const LogitsArgs& a, hipStream_t st) {
     return mfma_dispatch_mt<BITS, 2, OUT, ZP>(a, st);
 }
 
-// int4: results as activation rows x single vocabulary columns, a 3-deep ring;
-// int8: transposed results (4 contiguous vocabulary columns per lane, one
-// 4-element store) with a 2-deep ring -- the fastest of the variants that fit
-// in 256 VGPRs on the 151936 x 1024 heads
+// int4: results as activation rows x single vocabulary columns; int8:
+// transposed results (4 contiguous vocabulary columns per lane, one 4-element
+// store); both with a 2-deep ring -- the fastest of the variants that fit in
+// 128 VGPRs (16 waves) on the 151936 x 1024 heads.  Up to 32 activation rows:
+// a 32-row tile and 16-column units (NT = 1), which spread a head's columns
+// over the 16 waves of a CU in 2-3 units each instead of 1-2.
 template <int BITS, int OUT, bool ZP>
 hipError_t xres_dispatch(const LogitsArgs& a, hipStream_t st) {
-    // (zero-point int4 heads: a 2-deep ring, which leaves room for the zero
-    // point words without spilling)
-    if constexpr (BITS == 4) return mfma_xres_dispatch_d<4, 2, false, OUT, ZP, 2>(a, st);
-    else return mfma_xres_dispatch_d<8, 2, true, OUT, ZP, 2>(a, st);
+    if (a.M <= 32) {
+        if constexpr (BITS == 4) return mfma_xres_dispatch_d<4, 2, false, OUT, ZP, 1, 2>(a, st);
+        else return mfma_xres_dispatch_d<8, 2, true, OUT, ZP, 1, 2>(a, st);
+    }
+    if constexpr (BITS == 4) return mfma_xres_dispatch_d<4, 2, false, OUT, ZP, 2, 4>(a, st);
+    else return mfma_xres_dispatch_d<8, 2, true, OUT, ZP, 2, 4>(a, st);
 }
 
 // The kernel family `f` for the head's code width and the output type.
