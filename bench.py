@@ -580,6 +580,7 @@ def main() -> int:
         return names[lmh.auto_path(M, w.K, w.bits, w.group)]
 
     per_call = {}
+    csink = torch.empty(lmh.MFMA_CEILING_SINK, dtype=torch.float32, device=dev)
     for M in Ms:
         us, usg = both(prep_logits(M, blobs, w.bits, outs[M]))
         B = algorithmic_bytes(M, w.V, w.K, w.bits, w.group)
@@ -593,6 +594,23 @@ def main() -> int:
             "TFLOP/s": round(tfl, 2), "frac_mfma_f16_peak": round(tfl / MFMA_F16_PEAK_TFLOPS, 4),
         }
         log(f"M={M}: {us:.2f} us (graph {usg:.2f})")
+        if M > 2 and per_call[f"M={M}"]["kernel"] != "gemv":
+            # the practical MFMA ceiling for the same flops on the same grid
+            # shape (lmhead_mfma_ceiling: MFMA chains alone, then with 2 and 4
+            # independent fp32 FMAs per MFMA -- a G-column group's scale FMAs
+            # are 128 / G per MFMA)
+            rounds = max(1, round(F / lmh.mfma_ceiling_flops(1)))
+            cf = lmh.mfma_ceiling_flops(rounds)
+            mc = {}
+            for nv in (0, 2, 4):
+                cu, cug = both(lambda nv=nv: [lmh.prepare_mfma_ceiling(rounds, nv, csink)])
+                mc[nv] = cu
+            ctf = cf / (mc[0] * 1e-6) / 1e12
+            per_call[f"M={M}"]["mfma_ceiling"] = {
+                "rounds": rounds, "flops": cf, "us": mc[0], "TFLOP/s": round(ctf, 2),
+                "frac_of_mfma_f16_peak": round(ctf / MFMA_F16_PEAK_TFLOPS, 4),
+                "us_with_2_fma_per_mfma": mc[2], "us_with_4_fma_per_mfma": mc[4],
+                "kernel_frac_of_ceiling": round(tfl / ctf, 4)}
     if not args.no_extras:
         # 16-bit logits (fp16 output: half the output bytes) at every M > 1
         for M in Ms:

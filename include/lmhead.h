@@ -440,6 +440,23 @@ int lmhead_logits_topk_noalloc(const void* x, int x_dtype, int64_t M, const void
  */
 int lmhead_stream_read(const void* src, size_t bytes, void* sink, void* stream);
 
+/*
+ * lmhead_mfma_ceiling -- a measurement aid, not part of the logits path: the
+ *   practical rate of the 16x16x32 fp16 MFMA (the instruction of the MFMA
+ *   logits kernels) on a grid of one 16-wave workgroup per CU, each wave
+ *   running `rounds` rounds of 8 independent MFMA chains on register
+ *   operands (no memory traffic), and with valu_per_mfma = 2 or 4 as many
+ *   independent fp32 FMAs beside each MFMA (the scale FMAs of a G-column
+ *   group are 128 / G per MFMA) -- how much the VALU work of a kernel adds
+ *   to its MFMA time.  rounds in [1, 2^31 - 1] (else LMH_E_SHAPE);
+ *   valu_per_mfma 0, 2 or 4 (else LMH_E_UNSUPPORTED); sink (device, not
+ *   NULL) receives one float per thread, 256 * 1024 floats, contents
+ *   undefined.  lmhead_mfma_ceiling_mfmas(rounds) is the number of MFMAs one
+ *   call issues (each 16 * 16 * 32 * 2 flops), 0 for rounds out of range.
+ */
+int lmhead_mfma_ceiling(int64_t rounds, int valu_per_mfma, float* sink, void* stream);
+int64_t lmhead_mfma_ceiling_mfmas(int64_t rounds);
+
 #ifdef __cplusplus
 }
 #endif

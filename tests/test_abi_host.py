@@ -361,3 +361,21 @@ def test_logits_topk_noalloc_validation():
     # 64 rows of 200000 logits kept in the scratch (no y): 51 MB > 16 MiB
     assert call(M=64, V=200000, K=128, y=None, ldy=0) == E_SCRATCH
     assert L.lmhead_status_string(E_SCRATCH).decode().startswith("LMH_E_SCRATCH")
+
+
+def test_measurement_aids_validation():
+    """The ceiling kernels' entry points reject bad arguments before any HIP
+    call, and report the MFMA count of a ceiling call."""
+    L = lmh.lib()
+    E_SHAPE, E_UNSUP, E_NULL = 2, 5, 1
+    assert L.lmhead_stream_read(None, 17, None, None) == E_SHAPE
+    assert L.lmhead_stream_read(None, 0, None, None) == OK
+    assert L.lmhead_stream_read(None, 16, None, None) == E_NULL
+    assert L.lmhead_mfma_ceiling(0, 0, None, None) == E_SHAPE
+    assert L.lmhead_mfma_ceiling(1 << 31, 0, None, None) == E_SHAPE
+    assert L.lmhead_mfma_ceiling(10, 3, None, None) == E_UNSUP
+    assert L.lmhead_mfma_ceiling(10, 2, None, None) == E_NULL
+    # 256 workgroups x 16 waves x 8 MFMAs per round
+    assert L.lmhead_mfma_ceiling_mfmas(10) == 10 * 8 * 16 * 256
+    assert L.lmhead_mfma_ceiling_mfmas(0) == 0
+    assert lmh.mfma_ceiling_flops(3) == 3 * 8 * 16 * 256 * 16 * 16 * 32 * 2

@@ -77,6 +77,8 @@ def lib() -> ctypes.CDLL:
             "lmhead_logits_topk": (i32, [vp, i32, i64, vp, i64, i64, i32, i64, i32, vp, vp, i32, i32,
                                          vp, i64, vp, vp, vp, vp, sz, vp]),
             "lmhead_stream_read": (i32, [vp, sz, vp, vp]),
+            "lmhead_mfma_ceiling": (i32, [i64, i32, vp, vp]),
+            "lmhead_mfma_ceiling_mfmas": (i64, [i64]),
             "lmhead_logits_topk_noalloc": (i32, [vp, i32, i64, vp, i64, i64, i32, i64, i32, vp, vp,
                                                  i32, i32, vp, i64, vp, vp, vp, vp]),
         }
@@ -348,7 +350,8 @@ def _raw() -> ctypes.CDLL:
         lib()  # raises if the library is missing
         _raw_lib = ctypes.CDLL(LIB_PATH)
         for name in ("lmhead_logits_typed", "lmhead_logits_topk", "lmhead_topk_rescore",
-                     "lmhead_embed", "lmhead_dense_logits", "lmhead_stream_read"):
+                     "lmhead_embed", "lmhead_dense_logits", "lmhead_stream_read",
+                     "lmhead_mfma_ceiling"):
             getattr(_raw_lib, name).restype = ctypes.c_int
     return _raw_lib
 
@@ -421,6 +424,23 @@ def prepare_stream_read(src: torch.Tensor, sink: torch.Tensor) -> PreparedCall:
     _need_cuda(src, sink)
     nb = src.numel() * src.element_size()
     return PreparedCall("lmhead_stream_read", (_ptr(src), nb, _ptr(sink), _stream(src)), (src, sink))
+
+
+MFMA_CEILING_SINK = 256 * 1024  # floats lmhead_mfma_ceiling's sink receives
+
+
+def prepare_mfma_ceiling(rounds: int, valu_per_mfma: int, sink: torch.Tensor) -> PreparedCall:
+    """lmhead_mfma_ceiling (a measurement aid) on a fixed sink, as a PreparedCall."""
+    _need_cuda(sink)
+    if sink.dtype != torch.float32 or sink.numel() < MFMA_CEILING_SINK:
+        raise ValueError(f"sink must be a float32 GPU tensor of at least {MFMA_CEILING_SINK} elements")
+    return PreparedCall("lmhead_mfma_ceiling", (int(rounds), int(valu_per_mfma), _ptr(sink), _stream(sink)),
+                        (sink,))
+
+
+def mfma_ceiling_flops(rounds: int) -> int:
+    """Flops of one lmhead_mfma_ceiling call with `rounds` rounds."""
+    return int(lib().lmhead_mfma_ceiling_mfmas(int(rounds))) * 16 * 16 * 32 * 2
 
 
 def prepare_dense_logits(x: torch.Tensor, w: torch.Tensor, out: torch.Tensor) -> PreparedCall:

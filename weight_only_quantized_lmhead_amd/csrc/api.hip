@@ -502,4 +502,16 @@ int lmhead_stream_read(const void* src, size_t bytes, void* sink, void* stream) 
     return from_hip(lmh::launch_stream_read(src, (int64_t)bytes, sink, (hipStream_t)stream));
 }
 
+int64_t lmhead_mfma_ceiling_mfmas(int64_t rounds) {
+    if (rounds < 1 || rounds > 0x7FFFFFFF) return 0;
+    return rounds * 8 * 16 * (int64_t)lmh::mfma_ceiling_grid();
+}
+
+int lmhead_mfma_ceiling(int64_t rounds, int valu_per_mfma, float* sink, void* stream) {
+    if (rounds < 1 || rounds > 0x7FFFFFFF) return LMH_E_SHAPE;
+    if (valu_per_mfma != 0 && valu_per_mfma != 2 && valu_per_mfma != 4) return LMH_E_UNSUPPORTED;
+    if (!sink) return LMH_E_NULL;
+    return from_hip(lmh::launch_mfma_ceiling((int)rounds, valu_per_mfma, sink, (hipStream_t)stream));
+}
+
 }  // extern "C"

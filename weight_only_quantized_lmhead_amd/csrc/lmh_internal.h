@@ -105,6 +105,11 @@ hipError_t launch_topk_merge_rescore(const u64* lists, const void* x, int x_dtyp
 int64_t topk_max_v();  // largest row length lmhead_topk_rescore supports
 // Read-only stream over `bytes` (a multiple of 16) at src; sink >= 1 KiB.
 hipError_t launch_stream_read(const void* src, int64_t bytes, void* sink, hipStream_t st);
+// MFMA ceiling: mfma_ceiling_grid() workgroups of 16 waves, `rounds` rounds of
+// 8 MFMAs per wave, valu_per_mfma (0, 2 or 4) fp32 FMAs per MFMA; sink holds
+// one float per thread.
+int mfma_ceiling_grid();
+hipError_t launch_mfma_ceiling(int rounds, int valu_per_mfma, float* sink, hipStream_t st);
 
 // Largest M the lane-per-row GEMV accepts when forced, the largest it runs by
 // default (from M = 3 on an MFMA kernel is faster, its unpacking being shared

@@ -1,9 +1,17 @@
-// Read-only HBM stream: the practical read ceiling the logits kernels are
-// measured against (a measurement aid, not part of the logits path).  Each
-// workgroup reads one contiguous run of 768 16-byte words (12 KiB), one load
-// per thread per step; the best of the shapes measured on MI355X for a cold
-// 83 MB buffer (5.9 TB/s, against 5.3-5.7 for fewer, longer-lived
-// workgroups or a grid-stride loop).
+// Measurement aids, not part of the logits path: the practical ceilings the
+// logits kernels are measured against.
+//
+// Read-only HBM stream.  Each workgroup reads one contiguous run of 768
+// 16-byte words (12 KiB), one load per thread per step; the best of the
+// shapes measured on MI355X for a cold 83 MB buffer (5.9 TB/s, against
+// 5.3-5.7 for fewer, longer-lived workgroups or a grid-stride loop).
+//
+// MFMA issue.  One workgroup of 16 waves per CU (the activation-resident
+// kernel's shape); every wave runs `rounds` rounds of 8 independent
+// v_mfma_f32_16x16x32_f16 chains on register operands, and with NV > 0 also
+// NV independent fp32 FMAs per MFMA (the scale FMAs of a G-column group cost
+// 128 / G per MFMA), so that the time of MFMA work alone and of MFMA work
+// with a given VALU share is measured on the same grid.
 #include "lmh_internal.h"
 
 namespace lmh {
@@ -26,7 +34,57 @@ __global__ __launch_bounds__(kStreamThreads) void stream_read_kernel(const uint4
     if (acc == 0x9E3779B9u) sink[threadIdx.x] = acc;
 }
 
+constexpr int kCeilWaves = 16;
+
+template <int NV>
+__global__ __launch_bounds__(64 * kCeilWaves, 1) void mfma_ceiling_kernel(int rounds,
+                                                                          float* __restrict__ sink) {
+    const int lane = threadIdx.x & 63;
+    h8 a, b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        a[i] = (_Float16)(float)((lane + i) & 7);
+        b[i] = (_Float16)(float)((3 * lane + i) & 7);
+    }
+    f4 acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = (f4){0.f, 0.f, 0.f, 0.f};
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = (float)(lane + i);
+    const float c = 0.5f + (float)(lane & 1), d = 1.0f;
+    for (int it = 0; it < rounds; ++it) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[i], 0, 0, 0);
+#pragma unroll
+            for (int k = 0; k < NV; ++k) {
+                float& r = v[(i * NV + k) & 15];
+                r = __builtin_fmaf(r, c, d);
+            }
+        }
+    }
+    float t = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t += acc[i][0] + acc[i][1] + acc[i][2] + acc[i][3];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) t += v[i];
+    sink[(int64_t)blockIdx.x * 64 * kCeilWaves + threadIdx.x] = t;
+}
+
 }  // namespace
+
+int mfma_ceiling_grid() { return 256; }
+
+hipError_t launch_mfma_ceiling(int rounds, int valu_per_mfma, float* sink, hipStream_t st) {
+    const dim3 grid((unsigned)mfma_ceiling_grid()), block(64 * kCeilWaves);
+    switch (valu_per_mfma) {
+    case 0: hipLaunchKernelGGL(mfma_ceiling_kernel<0>, grid, block, 0, st, rounds, sink); break;
+    case 2: hipLaunchKernelGGL(mfma_ceiling_kernel<2>, grid, block, 0, st, rounds, sink); break;
+    default: hipLaunchKernelGGL(mfma_ceiling_kernel<4>, grid, block, 0, st, rounds, sink); break;
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_stream_read(const void* src, int64_t bytes, void* sink, hipStream_t st) {
     const int64_t n16 = bytes / 16;
