@@ -393,6 +393,8 @@ def main() -> int:
                          "top-1 agreement with the unquantized 16-bit weight before and after exact "
                          "top-K rescoring, and the top-K set overlap")
     ap.add_argument("--cpu-seconds", type=float, default=16.0)
+    ap.add_argument("--record", metavar="PATH",
+                    help="also write the JSON line, with the command that made it, as a markdown file")
     ap.add_argument("--summarize", action="store_true",
                     help="write a profiles/ summary from rocprofv3 CSV files instead of timing")
     ap.add_argument("--stats", help="kernel_stats.csv of a --kernel-trace --stats run")
@@ -713,6 +715,18 @@ def main() -> int:
     if agreement is not None:
         line["agreement"] = agreement
     print(json.dumps(line), flush=True)
+    if args.record:
+        argv, skip = [], False
+        for a in sys.argv[1:]:
+            if skip:
+                skip = False
+            elif a == "--record":
+                skip = True
+            elif not a.startswith("--record="):
+                argv.append(a)
+        with open(args.record, "w") as f:
+            f.write(f"# bench.py line: {w.name}\n\nCommand (from the repository root): "
+                    f"`python3 bench.py {' '.join(argv)}`\n\n```json\n{json.dumps(line)}\n```\n")
     return 0
 
 
