@@ -382,7 +382,7 @@ def main() -> int:
     ap.add_argument("--workload", default=None, help="synthetic workload name (default: the headline)")
     ap.add_argument("--ms", default=None, help="comma-separated M list (default: the workload's)")
     ap.add_argument("--topk", type=int, default=8)
-    ap.add_argument("--path", type=int, default=0, help="0 automatic, 1 GEMV, 2 register-fed MFMA, 3 LDS-staged MFMA, 4 activation-resident MFMA")
+    ap.add_argument("--path", type=int, default=0, help="0 automatic, 1 GEMV, 2 register-fed MFMA, 3 LDS-staged MFMA, 4 activation-resident MFMA, 5 split-K MFMA")
     ap.add_argument("--hot", action="store_true", help="reuse one copy of the head (cache-hot; labelled)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
@@ -578,7 +578,7 @@ def main() -> int:
 
     def auto_kernel(M):
         names = {lmh.PATH_GEMV: "gemv", lmh.PATH_MFMA: "mfma", lmh.PATH_MFMA_LDS: "mfma_lds",
-                 lmh.PATH_MFMA_XRES: "mfma_xres"}
+                 lmh.PATH_MFMA_XRES: "mfma_xres", lmh.PATH_MFMA_SPLITK: "mfma_splitk"}
         return names[lmh.auto_path(M, w.K, w.bits, w.group)]
 
     per_call = {}
@@ -591,7 +591,8 @@ def main() -> int:
         tfl = F / (us * 1e-6) / 1e12
         per_call[f"M={M}"] = {
             "us": us, "us_graph": usg,
-            "kernel": {1: "gemv", 2: "mfma", 3: "mfma_lds", 4: "mfma_xres"}.get(args.path, auto_kernel(M)),
+            "kernel": {1: "gemv", 2: "mfma", 3: "mfma_lds", 4: "mfma_xres",
+                       5: "mfma_splitk"}.get(args.path, auto_kernel(M)),
             "algorithmic_bytes": B, "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
             "TFLOP/s": round(tfl, 2), "frac_mfma_f16_peak": round(tfl / MFMA_F16_PEAK_TFLOPS, 4),
         }

@@ -274,7 +274,8 @@ size_t lmhead_logits_workspace_bytes(int64_t M, int64_t K, int x_dtype);
  *   M = 1 and M = 2 run a GEMV with one lane per vocabulary row (K split
  *   over up to 8 waves per 64-row block); larger M runs a 16x16x32 fp16 MFMA kernel (its
  *   code unpacking is shared by all activation rows), chosen from
- *   measurements: for K <= 1024 and G >= 64, the activation-resident one
+ *   measurements: for M = 3..16 and K <= 2048 the split-K one (path 5);
+ *   beyond, for K <= 1024 and G >= 64, the activation-resident one
  *   from M = 33 on (int4 heads: from M = 17 on); otherwise for K <= 1024 the
  *   LDS-staged one for M = 17..32 and for int8 heads, else the register-fed
  *   one; for K > 1024,
@@ -300,7 +301,13 @@ int lmhead_logits(const void* x, int x_dtype, int64_t M, const void* packed, int
  *   activation rows per workgroup), 4 = the activation-resident MFMA kernel
  *   (a 32-row (M <= 32) or 64-row activation tile held in LDS for the
  *   workgroup's life, weights streamed through registers; K <= 1024, else
- *   LMH_E_UNSUPPORTED).  All
+ *   LMH_E_UNSUPPORTED), 5 = the split-K MFMA kernel (a 64-row block split
+ *   along K over up to 8 waves, every load of a wave issued up front, the
+ *   waves' partial tiles added in wave order through LDS; M <= 16, else
+ *   LMH_E_UNSUPPORTED).  Paths 2-4 give bit-identical results; path 5 adds
+ *   the same per-group products and scale FMAs, but its K partial sums
+ *   associate differently (as the GEMV's do), so it agrees with them to
+ *   within fp32 rounding.  All
  *   kernels compute the same function; this entry point exists to test and
  *   time each of them on the same shapes.
  */

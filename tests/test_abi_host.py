@@ -92,7 +92,8 @@ def test_logits_validation():
     assert _logits(xd=BF16, path=2) == E_WS
     assert _logits(xd=BF16, path=3, ws=P, wsn=16) == E_WS
     assert _logits(path=1, M=5) == E_UNSUP   # the GEMV serves M <= 4
-    assert _logits(path=5) == E_UNSUP
+    assert _logits(path=6) == E_UNSUP
+    assert _logits(path=5, M=17) == E_UNSUP  # the split-K kernel serves M <= 16
     # empty requests are valid and launch nothing
     assert _logits(M=0) == OK
     assert _logits(V=0) == OK
@@ -295,7 +296,7 @@ def test_zero_point_validation():
     assert _logits(bits=4 | ZP, M=0) == OK
     assert _logits(bits=8 | ZP, G=64, V=0) == OK
     assert _logits(bits=3 | ZP) == E_UNSUP
-    assert _logits(bits=4 | ZP, path=5) == E_UNSUP
+    assert _logits(bits=4 | ZP, path=6) == E_UNSUP
     assert L.lmhead_embed(P, 0, P, 128, 128, 4 | ZP, 64, F16, P, F16, 128, None) == OK
 
 
@@ -307,18 +308,20 @@ def _auto(M, K=1024, bits=4, G=64):
 
 def test_auto_path_choice():
     # the automatic kernel choice, host only: the GEMV for one or two rows, the
-    # activation-resident kernel when the tile fits (K <= 1024, G >= 64)
-    # beyond 32 rows, and from 17 rows on for int4 heads; the LDS-staged
-    # kernel for int8 heads up to 32 rows, and the register-fed kernel for
-    # 3..16 rows of an int4 head
-    GEMV, MFMA, LDS, XRES = (lmh.PATH_GEMV, lmh.PATH_MFMA, lmh.PATH_MFMA_LDS,
-                             lmh.PATH_MFMA_XRES)
-    for M, want in [(1, GEMV), (2, GEMV), (3, MFMA), (16, MFMA), (17, XRES), (32, XRES),
+    # split-K kernel for 3..16 rows when K <= 2048, the activation-resident
+    # kernel when the tile fits (K <= 1024, G >= 64) beyond 32 rows, and from
+    # 17 rows on for int4 heads; the LDS-staged kernel for int8 heads of
+    # 17..32 rows
+    GEMV, MFMA, LDS, XRES, SPLITK = (lmh.PATH_GEMV, lmh.PATH_MFMA, lmh.PATH_MFMA_LDS,
+                                     lmh.PATH_MFMA_XRES, lmh.PATH_MFMA_SPLITK)
+    for M, want in [(1, GEMV), (2, GEMV), (3, SPLITK), (16, SPLITK), (17, XRES), (32, XRES),
                     (33, XRES), (64, XRES), (256, XRES), (65535, XRES)]:
         assert _auto(M) == (OK, want), M
     assert _auto(24, G=32) == (OK, LDS)               # 32-column groups: no resident tile
-    for M, want in [(1, GEMV), (2, GEMV), (3, LDS), (32, LDS), (33, XRES), (256, XRES)]:
+    for M, want in [(1, GEMV), (2, GEMV), (3, SPLITK), (16, SPLITK), (17, LDS), (32, LDS),
+                    (33, XRES), (256, XRES)]:
         assert _auto(M, bits=8, G=128) == (OK, want), M
+    assert _auto(8, K=2048, bits=8, G=2048) == (OK, SPLITK)
     assert _auto(256, G=32) == (OK, LDS)              # 32-column groups: no resident tile
     assert _auto(256, K=2048) == (OK, LDS)            # the 64-row tile of K > 1024 exceeds LDS
     for M, want in [(2, GEMV), (3, LDS), (24, LDS), (25, MFMA), (32, MFMA), (33, LDS)]:

@@ -12,6 +12,7 @@ from gpu_common import DEV, OD, TD, abs_terms, bits16, check_logits, gpu, need_g
 pytestmark = gpu
 
 GEMV, MFMA, LDS, XRES = lmh.PATH_GEMV, lmh.PATH_MFMA, lmh.PATH_MFMA_LDS, lmh.PATH_MFMA_XRES
+SPLITK = lmh.PATH_MFMA_SPLITK
 
 
 def _head(V, K, bits, G, sdt, seed, zero_rows=()):
@@ -45,7 +46,8 @@ CASES = [  # bits, G, K
 @pytest.mark.parametrize("bits,G,K", CASES)
 @pytest.mark.parametrize("xdt,sdt", [("f16", "f16"), ("bf16", "bf16"), ("f16", "bf16")])
 @pytest.mark.parametrize("path,Ms", [(GEMV, (1, 2, 3, 4)), (MFMA, (1, 5, 16, 17, 40, 67)),
-                                     (LDS, (1, 5, 64, 65, 130)), (XRES, (1, 7, 64, 65, 130))])
+                                     (LDS, (1, 5, 64, 65, 130)), (XRES, (1, 7, 64, 65, 130)),
+                                     (SPLITK, (1, 3, 9, 16))])
 def test_logits_small_vs_oracle(bits, G, K, xdt, sdt, path, Ms):
     need_gpu()
     V = 64 * 5 + 37
@@ -61,7 +63,7 @@ def test_logits_small_vs_oracle(bits, G, K, xdt, sdt, path, Ms):
 
 
 @pytest.mark.parametrize("path,M", [(GEMV, 1), (GEMV, 3), (MFMA, 8), (MFMA, 33), (LDS, 20), (LDS, 70),
-                                    (XRES, 3), (XRES, 29), (XRES, 70)])
+                                    (XRES, 3), (XRES, 29), (XRES, 70), (SPLITK, 5), (SPLITK, 13)])
 def test_bias_and_row_stride(path, M):
     need_gpu()
     V, K, bits, G = 200, 512, 4, 64
@@ -75,7 +77,7 @@ def test_bias_and_row_stride(path, M):
 
 
 @pytest.mark.parametrize("bits,G", [(4, 64), (4, 128), (8, 128), (8, 32)])
-@pytest.mark.parametrize("path", [GEMV, MFMA, LDS, XRES])
+@pytest.mark.parametrize("path", [GEMV, MFMA, LDS, XRES, SPLITK])
 def test_one_hot_exposes_layout(bits, G, path):
     """x = e_k gives y[v] = q[v,k] * s[v, k/G] exactly (one exact product): any
     misplaced nibble, byte, slot or scale shows up bit for bit."""
@@ -96,7 +98,7 @@ def test_one_hot_exposes_layout(bits, G, path):
 
 
 @pytest.mark.parametrize("path,M", [(GEMV, 1), (GEMV, 4), (MFMA, 16), (MFMA, 64), (LDS, 64), (LDS, 128),
-                                    (XRES, 64), (XRES, 200)])
+                                    (XRES, 64), (XRES, 200), (SPLITK, 11), (SPLITK, 16)])
 def test_invariants_zero_rows_scaling_determinism(path, M):
     need_gpu()
     V, K, bits, G = 320, 512, 4, 64
@@ -161,6 +163,29 @@ def test_mfma_kernels_bit_identical(bits, G):
         assert np.array_equal(a, c), f"M={M} (activation-resident)"
 
 
+@pytest.mark.parametrize("bits,G,K", [(4, 32, 512), (4, 64, 1024), (4, 256, 1024), (4, 128, 3072),
+                                      (4, 64, 768), (4, 128, 384), (8, 64, 320), (8, 64, 512),
+                                      (8, 128, 2048), (8, 1024, 1024)])
+def test_splitk_agrees_with_mfma_kernels(bits, G, K):
+    """The split-K kernel adds the same exact per-group products and fp32
+    scale FMAs as the other MFMA kernels, only its K partial sums associate
+    differently: per element within the fp32 summation bound of the oracle
+    and within a few fp32 ulps of max|y| of the register-fed kernel; splits
+    of 1, 2, 4 and 8 waves (superchunk counts 4..48), one- and two-buffer
+    loads, one to sixteen rows, a ragged vocabulary tail."""
+    need_gpu()
+    V = 64 * 7 + 29
+    q, s, blob = _head(V, K, bits, G, "f16", seed=61 + G + K)
+    for M in (1, 3, 9, 16):
+        x = synth.random_x(M, K, seed=70 + M)
+        a = _run(x, "f16", blob, V, K, bits, G, "f16", MFMA)
+        b = _run(x, "f16", blob, V, K, bits, G, "f16", SPLITK)
+        y_or = oracle.logits(x, q, s, oracle.F16, G, x_dtype=oracle.F16)
+        y_abs = abs_terms(x, "f16", q, s, oracle.F16, G)
+        check_logits(b, y_or, y_abs, K, G, what=f"split-K M={M}")
+        assert np.abs(a - b).max() <= 1e-5 * np.abs(a).max(), f"M={M}"
+
+
 def test_bf16_activations_large_and_small_rows():
     """bf16 rows far outside the fp16 range (and tiny ones) are handled by the
     power-of-two row scale."""
@@ -172,7 +197,7 @@ def test_bf16_activations_large_and_small_rows():
     xf[1] *= 1e-6
     xf[2, 5] = 3e4
     x = synth.to_bf16_bits(xf)
-    for path in (GEMV, MFMA, LDS, XRES):
+    for path in (GEMV, MFMA, LDS, XRES, SPLITK):
         y = _run(x, "bf16", blob, V, K, bits, G, "bf16", path)
         y_or = oracle.logits(x, q, s, oracle.BF16, G, x_dtype=oracle.BF16)
         y_abs = abs_terms(x, "bf16", q, s, oracle.BF16, G)
@@ -195,7 +220,7 @@ def _ulp16(y: np.ndarray, odt: str) -> np.ndarray:
 
 @pytest.mark.parametrize("odt", ["f16", "bf16"])
 @pytest.mark.parametrize("path,M", [(GEMV, 1), (GEMV, 3), (MFMA, 5), (MFMA, 17), (LDS, 20), (LDS, 70),
-                                    (XRES, 20), (XRES, 40), (XRES, 130)])
+                                    (XRES, 20), (XRES, 40), (XRES, 130), (SPLITK, 9), (SPLITK, 16)])
 @pytest.mark.parametrize("bits,G", [(4, 64), (8, 128)])
 def test_16bit_logits_output(odt, path, M, bits, G):
     """16-bit logits are the fp32 result rounded once to nearest even (bit-exact

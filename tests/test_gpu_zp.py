@@ -18,6 +18,7 @@ pytestmark = gpu
 ZP = lmh.ZP
 QR = {4: 15, 8: 255}
 GEMV, MFMA, LDS, XRES = lmh.PATH_GEMV, lmh.PATH_MFMA, lmh.PATH_MFMA_LDS, lmh.PATH_MFMA_XRES
+SPLITK = lmh.PATH_MFMA_SPLITK
 
 
 def _weights(V, K, wdt, seed, zero_rows=()):
@@ -177,7 +178,7 @@ CASES = [  # bits, G, K
 @pytest.mark.parametrize("bits,G,K", CASES)
 @pytest.mark.parametrize("xdt,sdt", [("f16", "f16"), ("bf16", "bf16")])
 @pytest.mark.parametrize("path,Ms", [(GEMV, (1, 2, 4)), (MFMA, (1, 5, 17, 40)),
-                                     (LDS, (3, 33, 65)), (XRES, (7, 65, 130))])
+                                     (LDS, (3, 33, 65)), (XRES, (7, 65, 130)), (SPLITK, (3, 9, 16))])
 def test_logits_zp_vs_oracle(bits, G, K, xdt, sdt, path, Ms):
     need_gpu()
     V = 64 * 5 + 37
@@ -194,7 +195,7 @@ def test_logits_zp_vs_oracle(bits, G, K, xdt, sdt, path, Ms):
 
 
 @pytest.mark.parametrize("bits,G", [(4, 64), (4, 128), (8, 128), (8, 32)])
-@pytest.mark.parametrize("path", [GEMV, MFMA, LDS, XRES])
+@pytest.mark.parametrize("path", [GEMV, MFMA, LDS, XRES, SPLITK])
 def test_logits_zp_one_hot_exposes_layout(bits, G, path):
     """x = e_k gives y[v] = (n[v,k] - z[v,k/G]) * s[v,k/G] exactly: a misplaced
     zero-point byte shows up bit for bit."""
@@ -226,7 +227,7 @@ def test_fixed_zero_point_is_the_symmetric_head_bit_for_bit(bits, G):
     z = np.full((V, K // G), zc, dtype=np.uint8)
     sym = torch.from_numpy(oracle.pack(q, s, bits, G)).to(DEV)
     zpb = torch.from_numpy(oracle.pack_zp(n, s, z, bits, G)).to(DEV)
-    for path, M in [(GEMV, 1), (GEMV, 3), (MFMA, 9), (LDS, 40), (XRES, 100)]:
+    for path, M in [(GEMV, 1), (GEMV, 3), (MFMA, 9), (LDS, 40), (XRES, 100), (SPLITK, 15)]:
         x = to_dev(synth.random_x(M, K, seed=M), "f16")
         ys = lmh.logits(x, sym, V, K, bits, G, torch.float16, path=path)
         yz = lmh.logits(x, zpb, V, K, bits | ZP, G, torch.float16, path=path)
@@ -244,7 +245,7 @@ def test_mfma_kernels_agree_bit_for_bit_zp(bits, G):
         assert np.array_equal(ys[0], ys[1]) and np.array_equal(ys[0], ys[2]), f"M={M}"
 
 
-@pytest.mark.parametrize("path,M", [(GEMV, 2), (MFMA, 8), (LDS, 20), (XRES, 70)])
+@pytest.mark.parametrize("path,M", [(GEMV, 2), (MFMA, 8), (LDS, 20), (XRES, 70), (SPLITK, 12)])
 def test_logits_zp_bias_stride_and_16bit_output(path, M):
     need_gpu()
     V, K, bits, G = 200, 512, 4, 64

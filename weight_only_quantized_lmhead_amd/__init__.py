@@ -29,7 +29,7 @@ LIB_PATH = os.path.join(_HERE, "liblmhead.so")
 LMH_OK = 0
 _DT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 _CLIP = {"rtn": 0, "mse": 1}
-PATH_AUTO, PATH_GEMV, PATH_MFMA, PATH_MFMA_LDS, PATH_MFMA_XRES = 0, 1, 2, 3, 4
+PATH_AUTO, PATH_GEMV, PATH_MFMA, PATH_MFMA_LDS, PATH_MFMA_XRES, PATH_MFMA_SPLITK = 0, 1, 2, 3, 4, 5
 ZP = 0x10  # LMH_ZP: OR'd into `bits`, selects the zero-point form
 
 _lib: Optional[ctypes.CDLL] = None

@@ -214,6 +214,15 @@ size_t lmhead_logits_workspace_bytes(int64_t M, int64_t K, int x_dtype) {
 // The automatic kernel choice (path 0), from sweeps over M = 2..256 on the
 // 151936 x 1024 int4 g64 and int8 g128 heads and the 248064 x 5120 int4 g128
 // head:
+//   - the split-K MFMA kernel for 3..16 rows when K <= 2048 (us against the
+//     best of the other kernels, M = 3 / 8 / 16: 151936 x 1024 int4 g64
+//     18.9 / 18.0 / 20.9 vs 21.4 / 22.5 / 23.1; g128 16.7 / 17.5 / 20.3 vs
+//     20.2 / 21.2 / 21.9; int8 g128 29.8 / 29.9 / 32.1 vs 32.5 / 32.4 /
+//     33.4; 50304 x 512 g64 5.3 / 5.6 / 6.1 vs 6.9 / 7.2 / 7.4; 151936 x
+//     2048 int8 per-row 54.0 / 56.4 / 61.8 vs 60.5 / 61.6 / 63.9); with
+//     K = 5120 its two-buffer ring needs 132 registers and it loses from
+//     M = 8 (144.7 vs 135.2), and with 32 rows (104 registers, 70 KiB of
+//     LDS: half the waves) it loses to the activation-resident kernel;
 //   - the GEMV for one or two activation rows (at M = 2 against the best MFMA
 //     kernel: int4 K = 1024 20.3 vs 20.8 us, int4 K = 5120 133 vs 141 us,
 //     int8 K = 1024 29.5 vs 31.6 us);
@@ -234,6 +243,7 @@ size_t lmhead_logits_workspace_bytes(int64_t M, int64_t K, int x_dtype) {
 //     the register-fed kernel would read the weights once per 32 rows).
 static int auto_path(int64_t M, int64_t K, int bits, int64_t group) {
     if (M <= lmh::kGemvAutoMaxM && M <= lmh::kGemvMaxM && M * K <= lmh::kGemvMaxMK) return 1;
+    if (M <= 16 && K <= 2048) return 5;
     if (M > 16 && lmh::xres_fits(K) && group >= 64 && (M > 32 || bits == 4)) return 4;
     const bool narrow = K <= 1024;
     const bool lds = narrow ? (M > 16 || bits == 8) : !(M > 24 && M <= 32);
@@ -251,7 +261,7 @@ static int logits_impl(const void* x, int x_dtype, int64_t M, const void* packed
     if (x_dtype != F16 && x_dtype != BF16) return LMH_E_DTYPE;
     if (scale_dtype != F16 && scale_dtype != BF16) return LMH_E_DTYPE;
     if (M < 0 || M > 65535) return LMH_E_SHAPE;
-    if (path < 0 || path > 4) return LMH_E_UNSUPPORTED;
+    if (path < 0 || path > 5) return LMH_E_UNSUPPORTED;
     if (M == 0 || V == 0) return LMH_OK;
     if (y && ldy < V) return LMH_E_SHAPE;
     if (!x || !packed || (!y && !lists)) return LMH_E_NULL;
@@ -264,6 +274,7 @@ static int logits_impl(const void* x, int x_dtype, int64_t M, const void* packed
     const bool gemv_ok = M <= lmh::kGemvMaxM && M * K <= lmh::kGemvMaxMK;
     if (path == 1 && !gemv_ok) return LMH_E_UNSUPPORTED;
     if (path == 4 && !lmh::xres_fits(K)) return LMH_E_UNSUPPORTED;
+    if (path == 5 && M > lmh::kSplitkMaxM) return LMH_E_UNSUPPORTED;
     if (path == 0) path = auto_path(M, K, bits, group);
     // bf16 rows: the GEMV converts them itself; the MFMA kernels take them
     // converted to fp16 (with a row exponent) in the workspace
@@ -303,6 +314,7 @@ static int logits_impl(const void* x, int x_dtype, int64_t M, const void* packed
     a.list_T = list_T;
     if (path == 1) return from_hip(lmh::launch_gemv(a, st));
     if (path == 4) return from_hip(lmh::launch_mfma_xres(a, st));
+    if (path == 5) return from_hip(lmh::launch_mfma_splitk(a, st));
     return from_hip(path == 3 ? lmh::launch_mfma_lds(a, st) : lmh::launch_mfma(a, st));
 }
 

@@ -83,6 +83,10 @@ hipError_t launch_mfma(const LogitsArgs& a, hipStream_t st);
 bool xres_fits(int64_t K);
 hipError_t launch_mfma_xres(const LogitsArgs& a, hipStream_t st);
 hipError_t launch_mfma_lds(const LogitsArgs& a, hipStream_t st);
+// Split-K MFMA kernel for M <= 16 (splitk.hip; zero-point heads in splitk_zp.hip).
+constexpr int kSplitkMaxM = 16;
+hipError_t launch_mfma_splitk(const LogitsArgs& a, hipStream_t st);
+hipError_t launch_mfma_splitk_zp(const LogitsArgs& a, hipStream_t st);
 // Logits kernel families (gemv, register MFMA, LDS-staged MFMA, activation
 // resident) and the zero-point instantiations of the MFMA ones (logits_zp.hip).
 enum { kFamGemv = 0, kFamMfma = 1, kFamMfmaLds = 2, kFamXres = 3 };
