@@ -204,7 +204,7 @@ def quantize(w: np.ndarray, bits: int, group: int, scale_dtype: int,
              ratios: Sequence[float] = RTN_RATIOS, w_dtype: Optional[int] = None,
              return_pick: bool = False, threads: Optional[int] = None):
     """(q int8 [V,K], s uint16 [V,K/G]) per the page's quantize_int4_rows, generalised
-    to int8 (qmax 127, qmin -128) and fp16/bf16 scales; readings R1-R4, R7.
+    to int8 (qmax 127, qmin -128) and fp16/bf16 scales; readings R1-R4 and R7 of the list at the top of lmh_oracle.c.
     Rows are quantized independently, so `threads` (default: the host's cores,
     at most 16) only splits the rows into ranges run side by side."""
     w = np.ascontiguousarray(w)
@@ -338,7 +338,7 @@ def dense_logits(x: np.ndarray, w: np.ndarray, rows=None, x_dtype: Optional[int]
 def quantize_asym(w: np.ndarray, bits: int, group: int, scale_dtype: int,
                   w_dtype: Optional[int] = None):
     """(n uint8 [V,K], s uint16 [V,K/G], z uint8 [V,K/G]) with w ~ (n - z) * s:
-    per-group min/max round to nearest with zero exactly representable (R21)."""
+    per-group min/max round to nearest with zero exactly representable (reading R21 of lmh_oracle.c)."""
     w = np.ascontiguousarray(w)
     V, K = w.shape
     n = np.empty((V, K), dtype=np.uint8)

@@ -34,8 +34,8 @@
  * -O2 -ffp-contract=off, never -ffast-math); fp64 sums are sequential in
  * ascending index order.  Everything is single-threaded and unblocked.
  *
- * Readings of the pages that are not stated there (each also recorded in the
- * design notes):
+ * Readings of the pages that are not stated there (referred to below, in
+ * oracle/__init__.py and in the tests by these tags):
  *   R1 an all-zero group gets scale 0 and q = 0 (the page clamps the scale to
  *      1e-8 instead; the logits are 0 either way);
  *   R2 the scale floor is 1e-8f for bf16 scales and 2^-24 (smallest fp16

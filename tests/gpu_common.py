@@ -2,7 +2,7 @@
 
 Acceptance for logits (fp32 output vs the fp64 oracle):
   * whole call:  max |y - y_or| <= 1e-3 * max |y_or|
-  * per row m:   max_v |y - y_or| <= 5e-4 * max_v |y_or[m, :]|   (reading R6)
+  * per row m:   max_v |y - y_or| <= 5e-4 * max_v |y_or[m, :]|   (the pages' per-row relative difference, normalised by that row's largest oracle logit)
   * argmax identical on rows whose oracle top1 - top2 margin exceeds 1e-3
   * per element: |y - y_or| <= gamma * sum_k |x q s| with
       gamma = (K + K/G + 16) * 2^-24,

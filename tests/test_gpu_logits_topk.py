@@ -4,7 +4,7 @@ The single call must give exactly what the two separate calls give
 (lmhead_logits, then lmhead_topk_rescore): the same indices in the same
 order, bit-identical rescored values, top-1 and scattered logits, with or
 without the logits stored.  The selection itself is checked against the
-oracle's top-K of the GPU's own logits (reading R5)."""
+oracle's top-K of the GPU's own logits (reading R5 of oracle/lmh_oracle.c: value descending, then index ascending)."""
 import numpy as np
 import pytest
 import torch

@@ -1,7 +1,7 @@
 """GPU top-K exact rescoring and the dense 16-bit control GEMV against the oracle.
 
 Top-K: the selected indices and their order must equal the oracle's selection on
-the GPU's own logits (bit-exact, reading R5); rescored values must lie within the
+the GPU's own logits (bit-exact, reading R5 of oracle/lmh_oracle.c); rescored values must lie within the
 fp32 summation bound gamma_K * sum_k |x w| of the fp64 dot product; the top-1 must
 equal the oracle's argmax of the scattered row wherever that is unambiguous."""
 import numpy as np

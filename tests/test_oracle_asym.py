@@ -2,7 +2,7 @@
 oracle.quantize_asym, the packed form pack_zp/unpack_zp, logits_zp and
 embed_zp (w ~ (n - z) * s with unsigned codes n and a per-group zero point z;
 the module page's kernel subtracts a fixed 8 from every nibble, the asymmetric
-checkpoint on the other page has a per-group value there; reading R21).
+checkpoint on the other page has a per-group value there; reading R21 of oracle/lmh_oracle.c).
 
 None of these re-types the oracle's formula.  They check:
   * a known answer: groups built on an exact grid (k - z0) * s0 that include

@@ -1,5 +1,5 @@
 """Pins for the oracle's quantizer (page "radiance_lmhead_int4.py": docstring "How"
-paragraph, module constants, quantize_int4_rows; readings R1-R4, R7).
+paragraph, module constants, quantize_int4_rows; readings R1-R4 and R7 of oracle/lmh_oracle.c).
 
 None of these re-types the oracle's formula.  They check what the pages and the
 mathematics fix:

@@ -1,4 +1,4 @@
-"""Exact pins of the quantizer's scale form and scale floor (readings R7 and R2).
+"""Exact pins of the quantizer's scale form and scale floor (readings R7 and R2 of oracle/lmh_oracle.c).
 
 Page "radiance_lmhead_int4.py", ``quantize_int4_rows``: the group scale is the
 fp32 product of amax with the ratio r / QMAX (a Python double quotient, cast to

@@ -1,5 +1,5 @@
 """Pins for the oracle's top-K selection and exact rescoring (vLLM PR #48870, review
-comment point 2; reading R5: value descending then index ascending; the top-1 is
+comment point 2; reading R5 of oracle/lmh_oracle.c: value descending then index ascending; the top-1 is
 the first maximum of the scattered vector)."""
 import numpy as np
 import pytest
