@@ -272,18 +272,18 @@ size_t lmhead_logits_workspace_bytes(int64_t M, int64_t K, int x_dtype);
  *           when x is bf16 and an MFMA kernel runs (M > 2 by default), else
  *           ignored (may be NULL/0); a missing or short one is LMH_E_WORKSPACE.
  *   M = 1 and M = 2 run a GEMV with one lane per vocabulary row (K split
- *   over up to 8 waves per 64-row block); larger M runs a 16x16x32 fp16 MFMA kernel (its
- *   code unpacking is shared by all activation rows), chosen from
- *   measurements: for M = 3..16 and K <= 2048 the split-K one (path 5);
- *   beyond, for K <= 1024 and G >= 64, the activation-resident one
- *   from M = 33 on (int4 heads: from M = 17 on); otherwise for K <= 1024 the
- *   LDS-staged one for M = 17..32 and for int8 heads, else the register-fed
- *   one; for K > 1024,
- *   the register-fed one for
- *   M = 25..32, else the LDS-staged one (see lmhead_logits_path).  Every
- *   MFMA kernel runs the same per-group MFMA chains and fp32 scale FMAs in
- *   the same order, so they give bit-identical results.  The result does not
- *   depend on the stream or on other calls.
+ *   over up to 8 waves per 64-row block); larger M runs a 16x16x32 fp16 MFMA
+ *   kernel (its code unpacking is shared by all activation rows), chosen
+ *   from measurements: for M = 3..16 and K <= 2048 the split-K one (path 5);
+ *   beyond, for K <= 1024 and G >= 64, the activation-resident one from
+ *   M = 33 on (int4 heads: from M = 17 on), else the LDS-staged one; for
+ *   K > 1024 the register-fed one for M = 25..32, else the LDS-staged one
+ *   (see lmhead_logits_path).  The register-fed, LDS-staged and
+ *   activation-resident kernels run the same per-group MFMA chains and fp32
+ *   scale FMAs in the same order, so they give bit-identical results; the
+ *   split-K kernel and the GEMV add the same exact terms in another
+ *   association (within fp32 rounding of them).  The result does not depend
+ *   on the stream, on timing or on other calls.
  *   Zero-point heads (bits | LMH_ZP) run the same kernels with each row's
  *   per-group zero point subtracted from its codes while they are unpacked
  *   (n - z is exact in fp16), so the arithmetic is otherwise the same.
