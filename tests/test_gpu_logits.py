@@ -186,6 +186,27 @@ def test_splitk_agrees_with_mfma_kernels(bits, G, K):
         assert np.abs(a - b).max() <= 1e-5 * np.abs(a).max(), f"M={M}"
 
 
+@pytest.mark.parametrize("V,K,bits,G", [(1, 128, 4, 64), (63, 128, 4, 32), (65, 256, 4, 128),
+                                        (130, 384, 4, 128), (200, 64, 8, 32), (64, 128, 8, 128)])
+def test_splitk_small_heads_and_dead_waves(V, K, bits, G):
+    """Split-K on heads of one to a few row blocks: K splits of 1, 2 and 4
+    waves (several blocks per workgroup, most waves finding no block), a
+    ragged last block, bias and a padded row stride, fp32 and fp16 output."""
+    need_gpu()
+    q, s, blob = _head(V, K, bits, G, "f16", seed=V + K)
+    bias = synth.random_weight((1, V), 1.0, 3)[0]
+    for M in (1, 2, 7, 16):
+        x = synth.random_x(M, K, seed=M + V)
+        y = _run(x, "f16", blob, V, K, bits, G, "f16", SPLITK, bias=bias, ldy=V + 5)
+        y_or = oracle.logits(x, q, s, oracle.F16, G, x_dtype=oracle.F16, bias=bias)
+        check_logits(y, y_or, abs_terms(x, "f16", q, s, oracle.F16, G), K, G, what=f"M={M}",
+                     bias=bias)
+        y16 = lmh.logits(to_dev(x, "f16"), blob, V, K, bits, G, torch.float16, path=SPLITK,
+                         bias=torch.from_numpy(bias).to(DEV), out_dtype=torch.float16)
+        torch.cuda.synchronize()
+        assert torch.equal(y16.cpu(), torch.from_numpy(np.ascontiguousarray(y)).half()), f"fp16 M={M}"
+
+
 def test_bf16_activations_large_and_small_rows():
     """bf16 rows far outside the fp16 range (and tiny ones) are handled by the
     power-of-two row scale."""
