@@ -141,7 +141,9 @@ size_t lmhead_packed_bytes(int64_t V, int64_t K, int bits, int64_t group);
  *   q_out  [V, K] int8 row-major (the code q itself, not biased).
  *   s_out  [V, K/G] 16-bit scale bit patterns, scale_dtype LMH_F16 / LMH_BF16.
  *   clip   LMH_CLIP_RTN or LMH_CLIP_MSE.
- *   Shape rules: G % 32 == 0 and K % G == 0 (the packing span is not needed).
+ *   Shape rules: G % 32 == 0 and K % G == 0 (the packing span is not needed);
+ *   V * K < 2^40 (else LMH_E_SHAPE); ceil(V/64) * (K/G) <= 2^26 - 32 (one
+ *   wavefront per 64 rows and group; else LMH_E_UNSUPPORTED).
  *   A scale that overflows the scale type is a precondition violation.
  */
 int lmhead_quantize(const void* w, int w_dtype, int64_t V, int64_t K, int bits, int64_t group,
@@ -216,7 +218,8 @@ int lmhead_pack_zp(const uint8_t* n, const void* s, const uint8_t* z, int64_t V,
  *   for lmhead_pack.  With bits | LMH_ZP the arithmetic is that of
  *   lmhead_quantize_zp and the blob the zero-point one (clip must be
  *   LMH_CLIP_RTN, else LMH_E_UNSUPPORTED).  rows == 0 is a valid empty call.
- *   Deterministic.
+ *   ceil(rows/64) * (K / max(G, span)) <= 2^26 - 32 (one wavefront per 64
+ *   rows and superchunk or group; else LMH_E_UNSUPPORTED).  Deterministic.
  */
 int lmhead_quantize_pack(const void* w, int w_dtype, int64_t ldw, int64_t V, int64_t K, int bits,
                          int64_t group, int scale_dtype, int clip, int64_t row0, int64_t rows,

@@ -120,6 +120,10 @@ def test_quantize_pack_validation():
     assert q(None, F32, 4, 128, 4, 64, F16, 0, P, P, None) == E_NULL
     assert q(P + 4, F32, 4, 128, 4, 64, F16, 0, P, P, None) == E_ALIGN
     assert q(P, F32, 0, 128, 4, 64, F16, 0, P, P, None) == OK
+    # one wavefront per 64 rows and group, at most 2^26 - 32 of them (the
+    # grid's work-item count fits 32 bits); None pointers: nothing launches
+    assert q(None, F32, 64 * (2**21 - 1), 1024, 4, 32, F16, 0, P, P, None) == E_NULL
+    assert q(None, F32, 64 * 2**21, 1024, 4, 32, F16, 0, P, P, None) == E_UNSUP
     pk = L.lmhead_pack
     assert pk(P, P, 4, 100, 4, 64, P, None) == E_SHAPE
     assert pk(None, P, 4, 128, 4, 64, P, None) == E_NULL
@@ -153,6 +157,10 @@ def test_fused_quantize_pack_validation():
     assert qp(out=P + 4) == E_ALIGN
     assert qp(w=None, rows=0, row0=64) == OK          # empty chunk: nothing launched
     assert qp(V=0, rows=0) == OK
+    # at most 2^26 - 32 wavefronts (64 rows x one 128-column superchunk each)
+    big = 64 * (2**23 - 4)
+    assert qp(w=None, V=big, rows=big, K=1024, ldw=1024) == E_NULL
+    assert qp(w=None, V=64 * 2**23, rows=64 * 2**23, K=1024, ldw=1024) == E_UNSUP
 
 
 def test_dense_and_topk_validation():

@@ -66,6 +66,13 @@ int scratch_of_current_device(void** out) {
 }
 
 // A `bits` argument: the code width, optionally with LMH_ZP (zero-point form).
+// Quantizer launches: one wavefront per unit, four per workgroup, the
+// workgroup count rounded up to a multiple of 8; the grid's work-item count
+// must fit the dispatch packet's 32-bit size.
+bool quant_grid_fits(int64_t units) {
+    return ((units + 3) / 4 + 7) / 8 * 8 * 256 < (int64_t(1) << 32);
+}
+
 struct Width {
     int bits;
     bool zp;
@@ -112,6 +119,7 @@ static int quantize_impl(const void* w, int w_dtype, int64_t V, int64_t K, int b
     if (clip != LMH_CLIP_RTN && clip != LMH_CLIP_MSE) return LMH_E_UNSUPPORTED;
     if (V < 0 || K < 1 || group < 32 || group % 32 != 0 || K % group != 0) return LMH_E_SHAPE;
     if (V * K >= (int64_t(1) << 40)) return LMH_E_SHAPE;
+    if (!quant_grid_fits((V + 63) / 64 * (K / group))) return LMH_E_UNSUPPORTED;
     if (V == 0) return LMH_OK;
     if (!w || !q_out || !s_out || (zp && !z_out)) return LMH_E_NULL;
     if (!aligned16(w) || !aligned16(q_out)) return LMH_E_ALIGN;
@@ -149,11 +157,11 @@ int lmhead_quantize_pack(const void* w, int w_dtype, int64_t ldw, int64_t V, int
     if (rows % 64 != 0 && row0 + rows != V) return LMH_E_SHAPE;
     if (ldw < K || ldw % 8 != 0) return LMH_E_SHAPE;
     if (rows == 0) return LMH_OK;
-    if (!w || !packed_out) return LMH_E_NULL;
-    if (!aligned16(w) || !aligned16(packed_out)) return LMH_E_ALIGN;
     // one wavefront per (64-row block, superchunk or group), four per workgroup
     const int64_t units = (rows + 63) / 64 * (K / std::max<int64_t>(group, lmh::span_of(bits)));
-    if ((units + 3) / 4 >= (int64_t(1) << 31)) return LMH_E_UNSUPPORTED;
+    if (!quant_grid_fits(units)) return LMH_E_UNSUPPORTED;
+    if (!w || !packed_out) return LMH_E_NULL;
+    if (!aligned16(w) || !aligned16(packed_out)) return LMH_E_ALIGN;
     return from_hip(lmh::launch_quantize_pack(w, w_dtype, ldw, V, K, bits, group, scale_dtype,
                                               clip == LMH_CLIP_MSE ? 5 : 1, wd.zp, row0, rows,
                                               (uint8_t*)packed_out, (hipStream_t)stream));

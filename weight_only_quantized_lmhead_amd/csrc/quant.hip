@@ -401,12 +401,26 @@ __device__ __forceinline__ int64_t zp_offset(int64_t b, int NG, int g, int r) {
     return (b * NG + g) * 64 + 4 * (r & 15) + (r >> 4);
 }
 
+// The unit (one wave's work) of this thread.  The launch's workgroups are
+// dealt round-robin to the 8 XCDs, so the work is numbered for XCD x to take
+// the contiguous run of workgroups [x per, (x + 1) per), per = grid / 8 (the
+// grid is a multiple of 8; workgroups past the work find unit >= nunits).  In
+// codes mode a workgroup writes 4 groups' scales of each of its 64 rows, only
+// part of the row's scale line; its neighbour writes the next part.  On one
+// XCD the parts meet in that XCD's L2 and go to HBM as whole lines; dealt to
+// two XCDs they would leave two L2s as two partial lines.
+__device__ __forceinline__ int64_t quant_unit() {
+    const int64_t per = gridDim.x >> 3;
+    const int64_t wg = (int64_t)(blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    return wg * 4 + (threadIdx.x >> 6);
+}
+
 template <int WDT, int BITS, int GT, bool PACKED, bool ASYM>
 __global__ __launch_bounds__(256, 2) void
 quant_held_kernel(
     const QuantArgs a) {
 #pragma clang fp contract(off)
-    const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t unit = quant_unit();
     if (unit >= a.nunits) return;
     const int r = threadIdx.x & 63;
     const int64_t b = a.blk0 + unit / a.upb;
@@ -463,7 +477,7 @@ quant_held_kernel(
 template <int WDT, int BITS, bool PACKED, bool ASYM>
 __global__ __launch_bounds__(256, 2) void quant_stream_kernel(const QuantArgs a) {
 #pragma clang fp contract(off)
-    const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t unit = quant_unit();
     if (unit >= a.nunits) return;
     const int r = threadIdx.x & 63;
     const int64_t b = a.blk0 + unit / a.upb;
@@ -530,7 +544,7 @@ void launch_q3(const QuantArgs& a, dim3 grid, hipStream_t st) {
 template <bool PACKED>
 hipError_t launch_q(const QuantArgs& a, int w_dtype, int bits, hipStream_t st) {
     if (a.nunits <= 0) return hipSuccess;
-    const dim3 grid((unsigned)((a.nunits + 3) / 4));
+    const dim3 grid((unsigned)(((a.nunits + 3) / 4 + 7) / 8 * 8));  // a multiple of 8: quant_unit
 #define LMH_Q_CASE(WDT)                                                                 \
     if (a.asym) {                                                                       \
         if (bits == 4) launch_q3<WDT, 4, PACKED, true>(a, grid, st);                    \
