@@ -579,7 +579,8 @@ def main() -> int:
     def auto_kernel(M):
         names = {lmh.PATH_GEMV: "gemv", lmh.PATH_MFMA: "mfma", lmh.PATH_MFMA_LDS: "mfma_lds",
                  lmh.PATH_MFMA_XRES: "mfma_xres", lmh.PATH_MFMA_SPLITK: "mfma_splitk"}
-        return names[lmh.auto_path(M, w.K, w.bits, w.group)]
+        xdt = torch.bfloat16 if w.x_dtype == "bf16" else torch.float16
+        return names[lmh.auto_path(M, w.K, w.bits, w.group, xdt)]
 
     per_call = {}
     csink = torch.empty(lmh.MFMA_CEILING_SINK, dtype=torch.float32, device=dev)

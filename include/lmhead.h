@@ -274,10 +274,12 @@ size_t lmhead_logits_workspace_bytes(int64_t M, int64_t K, int x_dtype);
  *   workspace / ws_bytes: at least lmhead_logits_workspace_bytes(M, K, x_dtype)
  *           when x is bf16 and an MFMA kernel runs (M > 2 by default), else
  *           ignored (may be NULL/0); a missing or short one is LMH_E_WORKSPACE.
- *   M = 1 and M = 2 run a GEMV with one lane per vocabulary row (K split
- *   over up to 8 waves per 64-row block); larger M runs a 16x16x32 fp16 MFMA
+ *   M = 1 runs a GEMV with one lane per vocabulary row (K split over up to 8
+ *   waves per 64-row block), and so does M = 2 with bf16 x or K > 2048;
+ *   larger M (and two fp16 rows of K <= 2048) runs a 16x16x32 fp16 MFMA
  *   kernel (its code unpacking is shared by all activation rows), chosen
- *   from measurements: for M = 3..16 and K <= 2048 the split-K one (path 5);
+ *   from measurements: for M = 2 (fp16 x) and 3..16 with K <= 2048 the
+ *   split-K one (path 5);
  *   beyond, for K <= 1024 and G >= 64, the activation-resident one from
  *   M = 33 on (int4 heads: from M = 17 on), else the LDS-staged one; for
  *   K > 1024 the register-fed one for M = 25..32, else the LDS-staged one
@@ -320,14 +322,20 @@ int lmhead_logits_path(const void* x, int x_dtype, int64_t M, const void* packed
                        void* stream);
 
 /*
- * lmhead_logits_auto_path -- the kernel lmhead_logits (path 0) runs for a
- *   head of the given shape, as a lmhead_logits_path number (1..4), in *path.
- *   Host only: no device work, no GPU needed.  M >= 1; K, bits (4 or 8,
- *   optionally | LMH_ZP) and group as for lmhead_logits.  Returns LMH_OK,
- *   LMH_E_NULL (path NULL), LMH_E_SHAPE or LMH_E_UNSUPPORTED (invalid shape
- *   or width, as lmhead_logits would report); *path is written only on
- *   LMH_OK.  The choice depends on M, K, the code width and G only.
+ * lmhead_logits_auto_path_x -- the kernel lmhead_logits (path 0) runs for a
+ *   head of the given shape and activation type, as a lmhead_logits_path
+ *   number (1..5), in *path.  Host only: no device work, no GPU needed.
+ *   M >= 1; K, bits (4 or 8, optionally | LMH_ZP), group and x_dtype (LMH_F16
+ *   or LMH_BF16) as for lmhead_logits.  Returns LMH_OK, LMH_E_NULL (path
+ *   NULL), LMH_E_SHAPE, LMH_E_DTYPE or LMH_E_UNSUPPORTED (invalid shape,
+ *   type or width, as lmhead_logits would report); *path is written only on
+ *   LMH_OK.  The choice depends on M, K, the code width, G and, at M = 2
+ *   only, on x_dtype (bf16 rows stay on the GEMV, which needs no workspace).
  */
+int lmhead_logits_auto_path_x(int64_t M, int64_t K, int bits, int64_t group, int x_dtype,
+                              int* path);
+
+/* lmhead_logits_auto_path -- lmhead_logits_auto_path_x for fp16 activations. */
 int lmhead_logits_auto_path(int64_t M, int64_t K, int bits, int64_t group, int* path);
 
 /*

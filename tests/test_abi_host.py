@@ -11,6 +11,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import oracle
 import weight_only_quantized_lmhead_amd as lmh
@@ -315,20 +316,28 @@ def _auto(M, K=1024, bits=4, G=64):
 
 
 def test_auto_path_choice():
-    # the automatic kernel choice, host only: the GEMV for one or two rows, the
-    # split-K kernel for 3..16 rows when K <= 2048, the activation-resident
+    # the automatic kernel choice, host only: the GEMV for one row (and two bf16
+    # rows, or two rows of K > 2048), the split-K kernel for two fp16 rows and
+    # for 3..16 rows when K <= 2048, the activation-resident
     # kernel when the tile fits (K <= 1024, G >= 64) beyond 32 rows, and from
     # 17 rows on for int4 heads; the LDS-staged kernel for int8 heads of
     # 17..32 rows
     GEMV, MFMA, LDS, XRES, SPLITK = (lmh.PATH_GEMV, lmh.PATH_MFMA, lmh.PATH_MFMA_LDS,
                                      lmh.PATH_MFMA_XRES, lmh.PATH_MFMA_SPLITK)
-    for M, want in [(1, GEMV), (2, GEMV), (3, SPLITK), (16, SPLITK), (17, XRES), (32, XRES),
+    for M, want in [(1, GEMV), (2, SPLITK), (3, SPLITK), (16, SPLITK), (17, XRES), (32, XRES),
                     (33, XRES), (64, XRES), (256, XRES), (65535, XRES)]:
         assert _auto(M) == (OK, want), M
     assert _auto(24, G=32) == (OK, LDS)               # 32-column groups: no resident tile
-    for M, want in [(1, GEMV), (2, GEMV), (3, SPLITK), (16, SPLITK), (17, LDS), (32, LDS),
+    for M, want in [(1, GEMV), (2, SPLITK), (3, SPLITK), (16, SPLITK), (17, LDS), (32, LDS),
                     (33, XRES), (256, XRES)]:
         assert _auto(M, bits=8, G=128) == (OK, want), M
+    # the activation type matters at two rows only: bf16 rows stay on the GEMV
+    # (no workspace); lmhead_logits_auto_path is the fp16 case
+    for M, want in [(1, GEMV), (2, GEMV), (3, SPLITK), (40, XRES)]:
+        assert lmh.auto_path(M, 1024, 4, 64, torch.bfloat16) == want, M
+    for M in (1, 2, 3, 16, 40):
+        assert lmh.auto_path(M, 1024, 4, 64, torch.float16) == _auto(M)[1]
+    assert _auto(2, K=4096, G=128) == (OK, GEMV)       # K > 2048: two rows stay on the GEMV
     assert _auto(8, K=2048, bits=8, G=2048) == (OK, SPLITK)
     assert _auto(256, G=32) == (OK, LDS)              # 32-column groups: no resident tile
     assert _auto(256, K=2048) == (OK, LDS)            # the 64-row tile of K > 1024 exceeds LDS
@@ -347,6 +356,10 @@ def test_auto_path_validation():
     assert _auto(1, K=192) == (E_SHAPE, -1)
     assert _auto(1, K=384, G=96) == (E_UNSUP, -1)
     assert lmh.lib().lmhead_logits_auto_path(1, 1024, 4, 64, None) == E_NULL
+    out = ctypes.c_int(-1)
+    assert lmh.lib().lmhead_logits_auto_path_x(1, 1024, 4, 64, F32, ctypes.byref(out)) == E_DTYPE
+    assert lmh.lib().lmhead_logits_auto_path_x(2, 1024, 4, 64, BF16, None) == E_NULL
+    assert out.value == -1
 
 
 def test_logits_topk_noalloc_validation():

@@ -69,6 +69,7 @@ def lib() -> ctypes.CDLL:
             "lmhead_logits_typed": (i32, [vp, i32, i64, vp, i64, i64, i32, i64, i32, vp, vp, i32, i64,
                                           vp, sz, i32, vp]),
             "lmhead_logits_auto_path": (i32, [i64, i64, i32, i64, vp]),
+            "lmhead_logits_auto_path_x": (i32, [i64, i64, i32, i64, i32, vp]),
             "lmhead_dense_logits": (i32, [vp, i32, i64, vp, i32, i64, i64, vp, i64, vp]),
             "lmhead_topk_workspace_bytes": (sz, [i64, i64, i32]),
             "lmhead_topk_rescore": (i32, [vp, i32, i64, vp, i32, i64, i64, vp, i64, i32, vp, vp,
@@ -233,11 +234,12 @@ def embed(ids: torch.Tensor, packed: torch.Tensor, V: int, K: int, bits: int, gr
     return out
 
 
-def auto_path(M: int, K: int, bits: int, group: int) -> int:
-    """The kernel lmhead_logits runs for this shape (PATH_GEMV .. PATH_MFMA_XRES); host only."""
+def auto_path(M: int, K: int, bits: int, group: int, x_dtype: torch.dtype = torch.float16) -> int:
+    """The kernel lmhead_logits runs for this shape and activation type
+    (PATH_GEMV .. PATH_MFMA_SPLITK); host only."""
     out = ctypes.c_int(0)
-    _check("lmhead_logits_auto_path",
-           lib().lmhead_logits_auto_path(M, K, bits, group, ctypes.byref(out)))
+    _check("lmhead_logits_auto_path_x",
+           lib().lmhead_logits_auto_path_x(M, K, bits, group, _DT[x_dtype], ctypes.byref(out)))
     return out.value
 
 

@@ -231,9 +231,13 @@ size_t lmhead_logits_workspace_bytes(int64_t M, int64_t K, int x_dtype) {
 //     K = 5120 its two-buffer ring needs 132 registers and it loses from
 //     M = 8 (144.7 vs 135.2), and with 32 rows (104 registers, 70 KiB of
 //     LDS: half the waves) it loses to the activation-resident kernel;
-//   - the GEMV for one or two activation rows (at M = 2 against the best MFMA
-//     kernel: int4 K = 1024 20.3 vs 20.8 us, int4 K = 5120 133 vs 141 us,
-//     int8 K = 1024 29.5 vs 31.6 us);
+//   - the GEMV for one activation row, and for two bf16 rows or two rows of
+//     K > 2048 (it converts bf16 rows itself, with no workspace; at M = 2,
+//     int4 K = 5120: 133 vs 141 us for the best MFMA kernel); two fp16 rows
+//     of K <= 2048 run the split-K kernel (M = 2, us, alternated twice:
+//     151936 x 1024 int4 g64 16.0-16.1 vs 17.1-17.2 for the GEMV, int8 g128
+//     28.4-28.5 vs 29.8-29.9, 151936 x 2048 int8 per-row 52.9-53.1 vs
+//     55.8-55.9, 50304 x 512 g64 5.66-5.68 vs 6.35-6.40);
 //   - when K <= 1024 and G >= 64, the activation-resident kernel from 33
 //     rows on (int4 M = 33..64: 29-33 us against 38-42 for the LDS-staged
 //     kernel's 64-row tiles; M = 96..256 6-10 % faster; int8 M = 40..256:
@@ -249,8 +253,9 @@ size_t lmhead_logits_workspace_bytes(int64_t M, int64_t K, int x_dtype) {
 //   - when K > 1024: the register-fed kernel for 25..32 rows (3 % faster),
 //     else the LDS-staged one (3..24 rows: 1.5-3 % faster; beyond 32 rows
 //     the register-fed kernel would read the weights once per 32 rows).
-static int auto_path(int64_t M, int64_t K, int bits, int64_t group) {
-    if (M <= lmh::kGemvAutoMaxM && M <= lmh::kGemvMaxM && M * K <= lmh::kGemvMaxMK) return 1;
+static int auto_path(int64_t M, int64_t K, int bits, int64_t group, bool x_bf16) {
+    if (M <= lmh::kGemvAutoMaxM && M <= lmh::kGemvMaxM && M * K <= lmh::kGemvMaxMK)
+        return M == 2 && !x_bf16 && K <= 2048 ? 5 : 1;
     if (M <= 16 && K <= 2048) return 5;
     if (M > 16 && lmh::xres_fits(K) && group >= 64 && (M > 32 || bits == 4)) return 4;
     const bool narrow = K <= 1024;
@@ -283,7 +288,7 @@ static int logits_impl(const void* x, int x_dtype, int64_t M, const void* packed
     if (path == 1 && !gemv_ok) return LMH_E_UNSUPPORTED;
     if (path == 4 && !lmh::xres_fits(K)) return LMH_E_UNSUPPORTED;
     if (path == 5 && M > lmh::kSplitkMaxM) return LMH_E_UNSUPPORTED;
-    if (path == 0) path = auto_path(M, K, bits, group);
+    if (path == 0) path = auto_path(M, K, bits, group, x_dtype == BF16);
     // bf16 rows: the GEMV converts them itself; the MFMA kernels take them
     // converted to fp16 (with a row exponent) in the workspace
     const bool convert = x_dtype == BF16 && path != 1;
@@ -326,14 +331,20 @@ static int logits_impl(const void* x, int x_dtype, int64_t M, const void* packed
     return from_hip(path == 3 ? lmh::launch_mfma_lds(a, st) : lmh::launch_mfma(a, st));
 }
 
-int lmhead_logits_auto_path(int64_t M, int64_t K, int bits_arg, int64_t group, int* path) {
+int lmhead_logits_auto_path_x(int64_t M, int64_t K, int bits_arg, int64_t group, int x_dtype,
+                              int* path) {
     if (!path) return LMH_E_NULL;
     const Width wd = width_of(bits_arg);
     const int rc = check_layout(1, K, wd.bits, group);
     if (rc != LMH_OK) return rc;
+    if (x_dtype != F16 && x_dtype != BF16) return LMH_E_DTYPE;
     if (M < 1 || M > 65535) return LMH_E_SHAPE;
-    *path = auto_path(M, K, wd.bits, group);
+    *path = auto_path(M, K, wd.bits, group, x_dtype == BF16);
     return LMH_OK;
+}
+
+int lmhead_logits_auto_path(int64_t M, int64_t K, int bits_arg, int64_t group, int* path) {
+    return lmhead_logits_auto_path_x(M, K, bits_arg, group, F16, path);
 }
 
 int lmhead_logits(const void* x, int x_dtype, int64_t M, const void* packed, int64_t V, int64_t K,
