@@ -67,6 +67,12 @@ def sources_sha() -> str:
 
 
 def traffic_file(workload: str) -> str:
+    """The committed counter summary of a workload: logits_<workload>_... for
+    the headline head, hotpath_<workload>_... for the others."""
+    for kind in ("logits", "hotpath"):
+        f = os.path.join(ROOT, "profiles", f"{kind}_{workload}_hbm_traffic.md")
+        if os.path.exists(f):
+            return f
     return os.path.join(ROOT, "profiles", f"logits_{workload}_hbm_traffic.md")
 
 
