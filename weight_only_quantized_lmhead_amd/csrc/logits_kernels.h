@@ -577,8 +577,8 @@ void mfma_lds_kernel(
 // (NT = 2: half a block, so 32 accumulator registers and 4 waves per SIMD to
 // hide each other's latency); each wave streams its units' weight slots and
 // scales through a D-deep register ring (loads past its last step are clamped
-// to that step and their contribution dropped, so every load is
-// unconditional and the wait counts stay exact), reads its A operands from
+// to that step, so every load is unconditional and the wait counts stay
+// exact; what those steps add is never stored), reads its A operands from
 // the resident tile, and stores a unit's 64 x 16 NT results as soon as its
 // last superchunk is done.  The workgroups of one XCD cover NMT activation
 // tiles times VRX vocabulary ranges with the NMT tiles of a range side by
@@ -732,15 +732,18 @@ __global__ __launch_bounds__(64 * xres_waves<NT_>(), 1) void mfma_xres_kernel(
                         }
                         bop[nt][jj] = (h8){p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
                     }
+                    // (a step past the wave's last is not masked: the last
+                    // real step ends a unit, whose results are stored and
+                    // whose accumulators are cleared, so what such a step
+                    // adds is never stored)
                     if constexpr (TR) {
                         const uint2 sw = sbuf[p][g][nt];
-                        sv[nt] = real ? (f4){scale_to_f32((uint16_t)sw.x, SB),
-                                             scale_to_f32((uint16_t)(sw.x >> 16), SB),
-                                             scale_to_f32((uint16_t)sw.y, SB),
-                                             scale_to_f32((uint16_t)(sw.y >> 16), SB)}
-                                      : (f4){0.f, 0.f, 0.f, 0.f};
+                        sv[nt] = (f4){scale_to_f32((uint16_t)sw.x, SB),
+                                      scale_to_f32((uint16_t)(sw.x >> 16), SB),
+                                      scale_to_f32((uint16_t)sw.y, SB),
+                                      scale_to_f32((uint16_t)(sw.y >> 16), SB)};
                     } else {
-                        const float v1 = real ? scale_to_f32(sbuf[p][g][nt], SB) : 0.0f;
+                        const float v1 = scale_to_f32(sbuf[p][g][nt], SB);
                         sv[nt] = (f4){v1, v1, v1, v1};
                     }
                 }
