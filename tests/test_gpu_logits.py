@@ -1,4 +1,4 @@
-"""GPU logits (GEMV and the three MFMA kernels) against the fp64 oracle on small heads
+"""GPU logits (GEMV and the four MFMA kernels) against the fp64 oracle on small heads
 that still span several row blocks, several superchunks per wave and a ragged tail."""
 import numpy as np
 import pytest
