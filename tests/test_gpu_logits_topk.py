@@ -98,8 +98,9 @@ def _dev_head(V, K, bits, G, seed, zp=False, zero=False):
     return Wd.half(), blob, bb
 
 
-@pytest.mark.parametrize("V,topk", [(5, 4), (64, 8), (65, 16), (64 * 256, 16), (64 * 256 + 1, 1),
-                                    (64 * 4096, 8), (64 * 4096 + 3, 8), (3000, 17)])
+@pytest.mark.parametrize("V,topk", [(1, 1), (2, 1), (5, 4), (64, 8), (65, 16), (64 * 256, 16),
+                                    (64 * 256 + 1, 1), (64 * 4096, 8), (64 * 4096 + 3, 8),
+                                    (3000, 17)])
 @pytest.mark.parametrize("zp", [False, True])
 def test_decode_path_edges(V, topk, zp):
     """M = 1 runs the GEMV with its per-block top-K lists and one merge kernel
@@ -122,6 +123,32 @@ def test_decode_path_edges(V, topk, zp):
     for i, v, t in ((i1, v1, t1), (i2, v2, t2)):
         assert torch.equal(i, i0) and torch.equal(v, v0) and torch.equal(t, t0)
     assert torch.equal(y1, y0)
+
+
+@pytest.mark.parametrize("topk", [2, 8, 16])
+def test_decode_path_clustered_blocks(topk):
+    """Most of the row's top logits in a few 64-row blocks (those rows' weights
+    scaled up), the rest spread: the merge then takes several entries from
+    some lists (up to all of one) and one from others.  Equal to the separate
+    calls bit for bit, and the selection is the oracle's top-K."""
+    need_gpu()
+    V, K, bits, G = 64 * 200 + 13, 512, 4, 64
+    gen = torch.Generator(device=DEV).manual_seed(topk)
+    Wd = torch.randn(V, K, device=DEV, generator=gen) * 0.02
+    Wd[64 * 7: 64 * 7 + 5] *= 6.0          # five rows of block 7
+    Wd[64 * 120 + 30: 64 * 120 + 64] *= 4.0  # the second half of block 120
+    Wd[V - 3:] *= 5.0                        # the ragged last block
+    blob = lmh.quantize_pack(Wd, bits, G, torch.float16)
+    wref = Wd.half()
+    for seed in range(4):
+        x = to_dev(synth.random_x(1, K, seed=seed, dtype="f16"), "f16")
+        y0 = lmh.logits(x, blob, V, K, bits, G, torch.float16)
+        i0, v0, t0 = lmh.topk_rescore(x, wref, y0, topk)
+        i1, v1, t1 = lmh.logits_topk(x, blob, V, K, bits, G, torch.float16, wref, topk)
+        torch.cuda.synchronize()
+        assert torch.equal(i1, i0) and torch.equal(v1, v0) and torch.equal(t1, t0), seed
+        yq = lmh.logits(x, blob, V, K, bits, G, torch.float16).cpu().numpy()
+        assert np.array_equal(i1.cpu().numpy()[0].astype(np.int64), oracle.topk(yq[0], topk)), seed
 
 
 def test_decode_path_all_ties():
