@@ -588,6 +588,16 @@ def main() -> int:
         xdt = torch.bfloat16 if w.x_dtype == "bf16" else torch.float16
         return names[lmh.auto_path(M, w.K, w.bits, w.group, xdt)]
 
+    def mix_ceiling(out, kernel_us):
+        """The practical HBM rate for this call's mix of bytes: lmhead_stream_mix
+        reading the packed head (the same rotating copies) and writing the
+        call's logits buffer, timed the same two ways."""
+        cu, cug = both(lambda: [lmh.prepare_stream_mix(b, out) for b in blobs])
+        wb = out.numel() * out.element_size()
+        return {"us": cu, "us_graph": cug, "read_bytes": blob_bytes, "write_bytes": wb,
+                "GB/s": round((blob_bytes + wb) / (cu * 1e-6) / 1e9, 1),
+                "kernel_frac_of_mix_ceiling": round(cu / kernel_us, 4)}
+
     per_call = {}
     csink = torch.empty(lmh.MFMA_CEILING_SINK, dtype=torch.float32, device=dev)
     for M in Ms:
@@ -621,6 +631,8 @@ def main() -> int:
                 "frac_of_mfma_f16_peak": round(ctf / MFMA_F16_PEAK_TFLOPS, 4),
                 "us_with_2_fma_per_mfma": mc[2], "us_with_4_fma_per_mfma": mc[4],
                 "kernel_frac_of_ceiling": round(tfl / ctf, 4)}
+        if M > 1:
+            per_call[f"M={M}"]["mix_ceiling"] = mix_ceiling(outs[M], us)
     if not args.no_extras:
         # 16-bit logits (fp16 output: half the output bytes) at every M > 1
         for M in Ms:
@@ -631,7 +643,8 @@ def main() -> int:
             B = algorithmic_bytes(M, w.V, w.K, w.bits, w.group) - M * w.V * 2
             per_call[f"M={M} y=f16"] = {"us": us, "us_graph": usg, "algorithmic_bytes": B,
                                          "GB/s": round(B / (us * 1e-6) / 1e9, 1),
-                                         "TFLOP/s": round(2.0 * M * w.V * w.K / (us * 1e-6) / 1e12, 2)}
+                                         "TFLOP/s": round(2.0 * M * w.V * w.K / (us * 1e-6) / 1e12, 2),
+                                         "mix_ceiling": mix_ceiling(o16, us)}
             del o16
         # zero-point heads: the same kernels with a per-row, per-group zero point
         for M in Ms:

@@ -459,6 +459,24 @@ int lmhead_logits_topk_noalloc(const void* x, int x_dtype, int64_t M, const void
 int lmhead_stream_read(const void* src, size_t bytes, void* sink, void* stream);
 
 /*
+ * lmhead_stream_mix -- a measurement aid, not part of the logits path: reads
+ *   read_bytes bytes at src once and writes write_bytes bytes at dst once
+ *   (16-byte accesses; each 256-thread workgroup reads 16 KiB and then writes
+ *   its share) -- the practical HBM rate for a logits call's mix of weight
+ *   reads and logit writes beyond one activation row, where the writes are a
+ *   large part of the bytes.  dst receives a function of the words read:
+ *   thread t of workgroup b writes words b*W*256 + 256*i + t (i < W,
+ *   W = ceil((write_bytes/16) / (256 * number of workgroups)), number of
+ *   workgroups = max(1, ceil(read_bytes / 16384))) with the XOR of the words
+ *   b*1024 + 256*j + t (j < 4) it read, plus i in the first 32-bit lane;
+ *   only words below the ends are accessed.  Both sizes multiples of 16 (else
+ *   LMH_E_SHAPE), both pointers 16-byte aligned (LMH_E_ALIGN); a pointer
+ *   whose size is 0 may be NULL; both 0 is a valid empty call.
+ */
+int lmhead_stream_mix(const void* src, size_t read_bytes, void* dst, size_t write_bytes,
+                      void* stream);
+
+/*
  * lmhead_mfma_ceiling -- a measurement aid, not part of the logits path: the
  *   practical rate of the 16x16x32 fp16 MFMA (the instruction of the MFMA
  *   logits kernels) on a grid of one 16-wave workgroup per CU, each wave

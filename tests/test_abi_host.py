@@ -395,6 +395,15 @@ def test_measurement_aids_validation():
     assert L.lmhead_stream_read(None, 17, None, None) == E_SHAPE
     assert L.lmhead_stream_read(None, 0, None, None) == OK
     assert L.lmhead_stream_read(None, 16, None, None) == E_NULL
+    mix = L.lmhead_stream_mix
+    assert mix(None, 17, None, 0, None) == E_SHAPE
+    assert mix(None, 16, None, 24, None) == E_SHAPE
+    assert mix(None, 0, None, 0, None) == OK
+    assert mix(None, 16, P, 16, None) == E_NULL             # reads from nowhere
+    assert mix(P, 16, None, 16, None) == E_NULL             # writes to nowhere
+    assert mix(P + 8, 16, P, 16, None) == E_ALIGN
+    assert mix(None, 1 << 38, None, 0, None) == E_UNSUP     # 2^24 workgroups: 2^32 work-items
+    assert mix(None, 1 << 46, None, 0, None) == E_SHAPE
     assert L.lmhead_mfma_ceiling(0, 0, None, None) == E_SHAPE
     assert L.lmhead_mfma_ceiling(1 << 31, 0, None, None) == E_SHAPE
     assert L.lmhead_mfma_ceiling(10, 3, None, None) == E_UNSUP

@@ -78,6 +78,7 @@ def lib() -> ctypes.CDLL:
             "lmhead_logits_topk": (i32, [vp, i32, i64, vp, i64, i64, i32, i64, i32, vp, vp, i32, i32,
                                          vp, i64, vp, vp, vp, vp, sz, vp]),
             "lmhead_stream_read": (i32, [vp, sz, vp, vp]),
+            "lmhead_stream_mix": (i32, [vp, sz, vp, sz, vp]),
             "lmhead_mfma_ceiling": (i32, [i64, i32, vp, vp]),
             "lmhead_mfma_ceiling_mfmas": (i64, [i64]),
             "lmhead_logits_topk_noalloc": (i32, [vp, i32, i64, vp, i64, i64, i32, i64, i32, vp, vp,
@@ -353,7 +354,7 @@ def _raw() -> ctypes.CDLL:
         _raw_lib = ctypes.CDLL(LIB_PATH)
         for name in ("lmhead_logits_typed", "lmhead_logits_topk", "lmhead_topk_rescore",
                      "lmhead_embed", "lmhead_dense_logits", "lmhead_stream_read",
-                     "lmhead_mfma_ceiling"):
+                     "lmhead_stream_mix", "lmhead_mfma_ceiling"):
             getattr(_raw_lib, name).restype = ctypes.c_int
     return _raw_lib
 
@@ -426,6 +427,21 @@ def prepare_stream_read(src: torch.Tensor, sink: torch.Tensor) -> PreparedCall:
     _need_cuda(src, sink)
     nb = src.numel() * src.element_size()
     return PreparedCall("lmhead_stream_read", (_ptr(src), nb, _ptr(sink), _stream(src)), (src, sink))
+
+
+def stream_mix(src: torch.Tensor, dst: torch.Tensor) -> None:
+    """One pass reading src's bytes and writing dst's (lmhead_stream_mix; a measurement aid)."""
+    _need_cuda(src, dst)
+    _check("lmhead_stream_mix", lib().lmhead_stream_mix(
+        _ptr(src), src.numel() * src.element_size(), _ptr(dst), dst.numel() * dst.element_size(),
+        _stream(src)))
+
+
+def prepare_stream_mix(src: torch.Tensor, dst: torch.Tensor) -> PreparedCall:
+    _need_cuda(src, dst)
+    return PreparedCall("lmhead_stream_mix",
+                        (_ptr(src), src.numel() * src.element_size(), _ptr(dst),
+                         dst.numel() * dst.element_size(), _stream(src)), (src, dst))
 
 
 MFMA_CEILING_SINK = 256 * 1024  # floats lmhead_mfma_ceiling's sink receives

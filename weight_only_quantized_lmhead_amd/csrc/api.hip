@@ -533,6 +533,21 @@ int lmhead_stream_read(const void* src, size_t bytes, void* sink, void* stream) 
     return from_hip(lmh::launch_stream_read(src, (int64_t)bytes, sink, (hipStream_t)stream));
 }
 
+int lmhead_stream_mix(const void* src, size_t read_bytes, void* dst, size_t write_bytes,
+                      void* stream) {
+    if (read_bytes % 16 != 0 || write_bytes % 16 != 0) return LMH_E_SHAPE;
+    if (read_bytes >= ((size_t)1 << 46) || write_bytes >= ((size_t)1 << 46)) return LMH_E_SHAPE;
+    int64_t grid, words;
+    lmh::stream_mix_shape((int64_t)read_bytes, (int64_t)write_bytes, &grid, &words);
+    // the grid's work-item count fits 32 bits; the per-thread word count an int
+    if (grid * 256 >= (int64_t(1) << 32) || words >= (int64_t(1) << 31)) return LMH_E_UNSUPPORTED;
+    if (read_bytes == 0 && write_bytes == 0) return LMH_OK;
+    if ((read_bytes && !src) || (write_bytes && !dst)) return LMH_E_NULL;
+    if (!aligned16(src) || !aligned16(dst)) return LMH_E_ALIGN;
+    return from_hip(lmh::launch_stream_mix(src, (int64_t)read_bytes, dst, (int64_t)write_bytes,
+                                           (hipStream_t)stream));
+}
+
 int64_t lmhead_mfma_ceiling_mfmas(int64_t rounds) {
     if (rounds < 1 || rounds > 0x7FFFFFFF) return 0;
     return rounds * 8 * 16 * (int64_t)lmh::mfma_ceiling_grid();

@@ -109,6 +109,10 @@ hipError_t launch_topk_merge_rescore(const u64* lists, const void* x, int x_dtyp
 int64_t topk_max_v();  // largest row length lmhead_topk_rescore supports
 // Read-only stream over `bytes` (a multiple of 16) at src; sink >= 1 KiB.
 hipError_t launch_stream_read(const void* src, int64_t bytes, void* sink, hipStream_t st);
+// read+write stream: its workgroup count and words written per thread
+void stream_mix_shape(int64_t read_bytes, int64_t write_bytes, int64_t* grid, int64_t* words);
+hipError_t launch_stream_mix(const void* src, int64_t read_bytes, void* dst, int64_t write_bytes,
+                             hipStream_t st);
 // MFMA ceiling: mfma_ceiling_grid() workgroups of 16 waves, `rounds` rounds of
 // 8 MFMAs per wave, valu_per_mfma (0, 2 or 4) fp32 FMAs per MFMA; sink holds
 // one float per thread.

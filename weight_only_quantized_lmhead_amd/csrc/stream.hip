@@ -6,6 +6,14 @@
 // shapes measured on MI355X for a cold 83 MB buffer (5.9 TB/s, against
 // 5.3-5.7 for fewer, longer-lived workgroups or a grid-stride loop).
 //
+// Read+write HBM stream.  Each 256-thread workgroup reads a run of 4
+// 16-byte words per thread (16 KiB) and then writes its share of the output,
+// ceil(written / read) words per thread; the reads cover the source once and
+// the writes the destination once.  The best of the shapes measured on MI355X
+// for the byte mixes of the logits calls beyond one activation row (83 MB
+// read with 19 or 156 MB written, source and destination both rotating over
+// 13 copies: 5.1-5.4 TB/s combined, against 4.4-4.8 for 8- or 17-word runs).
+//
 // MFMA issue.  One workgroup of 16 waves per CU (the activation-resident
 // kernel's shape); every wave runs `rounds` rounds of 8 independent
 // v_mfma_f32_16x16x32_f16 chains on register operands, and with NV > 0 also
@@ -32,6 +40,36 @@ __global__ __launch_bounds__(kStreamThreads) void stream_read_kernel(const uint4
     }
     // keeps the loads alive; stores only when the folded word hits this value
     if (acc == 0x9E3779B9u) sink[threadIdx.x] = acc;
+}
+
+constexpr int kMixRun = 4;  // 16-byte words read per thread
+
+// Thread t of workgroup b reads words b * 1024 + 256 i + t (i < 4) and writes
+// words b * W * 256 + 256 i + t (i < W), each access only below its end:
+// word i of the output is the XOR of the words read, its first 32-bit lane
+// plus i (so that every written word depends on the reads).
+__global__ __launch_bounds__(kStreamThreads) void stream_mix_kernel(const uint4* __restrict__ src,
+                                                                    int64_t nsrc,
+                                                                    uint4* __restrict__ dst,
+                                                                    int64_t ndst, int W) {
+    const int64_t br = (int64_t)blockIdx.x * kMixRun * kStreamThreads + threadIdx.x;
+    uint4 a = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int i = 0; i < kMixRun; ++i) {
+        const int64_t p = br + (int64_t)i * kStreamThreads;
+        if (p < nsrc) {
+            const uint4 v = src[p];
+            a.x ^= v.x;
+            a.y ^= v.y;
+            a.z ^= v.z;
+            a.w ^= v.w;
+        }
+    }
+    const int64_t bw = (int64_t)blockIdx.x * W * kStreamThreads + threadIdx.x;
+    for (int i = 0; i < W; ++i) {
+        const int64_t p = bw + (int64_t)i * kStreamThreads;
+        if (p < ndst) dst[p] = make_uint4(a.x + (uint32_t)i, a.y, a.z, a.w);
+    }
 }
 
 constexpr int kCeilWaves = 16;
@@ -83,6 +121,23 @@ hipError_t launch_mfma_ceiling(int rounds, int valu_per_mfma, float* sink, hipSt
     case 2: hipLaunchKernelGGL(mfma_ceiling_kernel<2>, grid, block, 0, st, rounds, sink); break;
     default: hipLaunchKernelGGL(mfma_ceiling_kernel<4>, grid, block, 0, st, rounds, sink); break;
     }
+    return hipGetLastError();
+}
+
+void stream_mix_shape(int64_t read_bytes, int64_t write_bytes, int64_t* grid, int64_t* words) {
+    const int64_t nsrc = read_bytes / 16, ndst = write_bytes / 16;
+    int64_t g = (nsrc + kMixRun * kStreamThreads - 1) / (kMixRun * kStreamThreads);
+    if (g == 0) g = 1;
+    *grid = g;
+    *words = (ndst + g * kStreamThreads - 1) / (g * kStreamThreads);
+}
+
+hipError_t launch_stream_mix(const void* src, int64_t read_bytes, void* dst, int64_t write_bytes,
+                             hipStream_t st) {
+    int64_t grid, words;
+    stream_mix_shape(read_bytes, write_bytes, &grid, &words);
+    hipLaunchKernelGGL(stream_mix_kernel, dim3((unsigned)grid), dim3(kStreamThreads), 0, st,
+                       (const uint4*)src, read_bytes / 16, (uint4*)dst, write_bytes / 16, (int)words);
     return hipGetLastError();
 }
 
