@@ -177,7 +177,7 @@ def summarize(args) -> int:
         recs = []
         for k in sorted(fv):
             if not k.startswith(("gemv_kernel", "mfma", "topk", "quant_", "embed_", "stream_read",
-                                 "dense_kernel", "x_to_f16")):
+                                 "stream_mix", "dense_kernel", "x_to_f16")):
                 continue
             f_ = statistics.mean(fv[k])
             w_ = statistics.mean(wv.get(k, [0.0]))
