@@ -41,8 +41,8 @@
 // of order codes (value descending, then index ascending; see topk_code),
 // entry j at lists[(m*T + j)*NB + blk] (entry-major, so that the merge reads
 // the lists' heads as one contiguous run): each lane ranks its own code
-// against the 64 codes of the wave (read lane by lane into scalar registers),
-// and the lanes of rank < T store.  Rows past V take codes below every real
+// against the 64 codes of the wave (staged in LDS and read back as broadcasts,
+// two per read), and the lanes of rank < T store.  Rows past V take codes below every real
 // entry.  y may then be null (logits not stored).
 #pragma once
 
@@ -386,13 +386,17 @@ __attribute__((amdgpu_waves_per_eu(gemv_occupancy<MM, XM, NCB>()))) void gemv_ke
             r = r + b;
             if (y && v < V) ((float*)y)[(int64_t)m * ldy + v] = r;
             const u64 c = v < V ? topk_code(r, v) : (u64)(64 - lane);
-            const uint32_t chi = (uint32_t)(c >> 32), clo = (uint32_t)c;
+            // the wave's 64 codes through LDS, read back two at a time as
+            // broadcasts (one wave's LDS operations are done in order), so
+            // each code costs one 64-bit compare and one add
+            __shared__ __attribute__((aligned(16))) u64 tkc[kGemvWaves][64];
+            tkc[wv][lane] = c;
             int rank = 0;
 #pragma unroll
-            for (int j = 0; j < 64; ++j) {
-                const u64 cj = ((u64)(uint32_t)__builtin_amdgcn_readlane((int)chi, j) << 32) |
-                               (uint32_t)__builtin_amdgcn_readlane((int)clo, j);
-                rank += cj > c;
+            for (int j = 0; j < 64; j += 2) {
+                const uint4 two = *(const uint4*)&tkc[wv][j];
+                const u64 c0 = ((u64)two.y << 32) | two.x, c1 = ((u64)two.w << 32) | two.z;
+                rank += (int)(c0 > c) + (int)(c1 > c);
             }
             if (rank < T) lists[((int64_t)m * T + rank) * NB + blk] = c;
         }
