@@ -23,7 +23,11 @@ microseconds (lower is better); `per_call` has every call's time, GB/s and
 roofline fraction; `roofline` is the M = 1 kernel's achieved algorithmic
 bandwidth (HIP events on the stream the calls run on) against the 8 TB/s HBM
 peak, with the read-only ceiling measured in the same run (lmhead_stream_read
-over the same bytes); `cpu_baseline` times the fp64 oracle on the host cores.
+over the same bytes); every call beyond one activation row also carries the
+read+write ceiling for its own byte mix (lmhead_stream_mix: the head's bytes
+read, its logits buffer written) and, on an MFMA kernel, the MFMA ceiling for
+its flops (lmhead_mfma_ceiling); `cpu_baseline` times the fp64 oracle on the
+host cores.
 """
 from __future__ import annotations
 
