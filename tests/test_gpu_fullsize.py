@@ -112,6 +112,35 @@ def test_fullsize_logits_sampled(built):
             assert (y[:, w.V - w.zero_tail_rows:] == 0).all()
 
 
+SWEEP_MS = (2, 3, 8, 16, 17, 24, 25, 32, 33)
+
+
+def test_fullsize_kernel_choice_sweep_sampled(built):
+    """Every kernel the automatic choice takes between 2 and 33 activation
+    rows, at the workload's full size (split-K, the activation-resident tiles,
+    the LDS-staged and register-fed kernels, the GEMV for two bf16 rows),
+    checked on sampled rows against the oracle."""
+    w, W, Wd, q, s, blob = built
+    rows = _sample_rows(w, 128, seed=w.wid + 2)
+    ratios = oracle.MSE_RATIOS if w.clip == "mse" else oracle.RTN_RATIOS
+    qo, so = oracle.quantize(np.ascontiguousarray(W[rows]), w.bits, w.group, OD[w.scale_dtype],
+                             ratios, w_dtype=OD[w.w_dtype])
+    rows_d = torch.from_numpy(rows).to(DEV)
+    used = {}
+    for M in SWEEP_MS:
+        x = synth.activations(w, M)
+        y = lmh.logits(to_dev(x, w.x_dtype), blob, w.V, w.K, w.bits, w.group, TD[w.scale_dtype])
+        torch.cuda.synchronize()
+        ys = y[:, rows_d].cpu().numpy()
+        y_or = oracle.logits(x, qo, so, OD[w.scale_dtype], w.group, x_dtype=OD[w.x_dtype])
+        y_abs = abs_terms(x, w.x_dtype, qo, so, OD[w.scale_dtype], w.group)
+        check_logits(ys, y_or, y_abs, w.K, w.group, what=f"{w.name} M={M}")
+        used[M] = lmh.auto_path(M, w.K, w.bits, w.group, TD[w.x_dtype])
+        del y
+    print(f"{w.name}: kernel per M {used}")
+    assert len(set(used.values())) >= 2
+
+
 def test_fullsize_whole_row_argmax_m1(built):
     w, W, Wd, q, s, blob = built
     ratios = oracle.MSE_RATIOS if w.clip == "mse" else oracle.RTN_RATIOS
