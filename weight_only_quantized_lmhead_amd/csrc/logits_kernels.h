@@ -1,4 +1,4 @@
-// Fused weight-only-quantized logits, the MFMA kernels (M > 2):
+// Fused weight-only-quantized logits, the MFMA kernels for many activation rows:
 // y[m,v] = sum_k x[m,k] * q[v,k] * s[v,k/G].
 //
 // vLLM PR #48870 ("Fused WNA16 GEMM for tied quantized lm_head logits",
@@ -9,15 +9,16 @@
 // same bits as each other.
 //
 // Kernels (which one runs for which M and head is decided in api.hip; the
-// lane-per-row GEMV for one to four rows is in gemv_kernels.h)
+// lane-per-row GEMV for one to four rows is in gemv_kernels.h, the split-K
+// MFMA kernel for up to 16 rows in splitk_kernels.h)
 //   mfma         register-fed MFMA.  A wave owns one row block (4 MFMA column
 //                tiles of 16 rows) and MT row tiles of 16 activations; each
 //                16-byte slot load is one 16x16x32 B operand per 32-column
 //                word.
 //   mfma_lds     the same tiles, every operand staged in LDS by direct
 //                global-to-LDS loads; 32- or 64-row activation tiles.
-//   mfma_xres    a 64-row activation tile resident in LDS, weights streamed
-//                through a register ring (large M, K <= 1024).
+//   mfma_xres    a 64-row (or, for M <= 32, 32-row) activation tile resident
+//                in LDS, weights streamed through a register ring (K <= 1024).
 //
 // Each kernel takes ZP (zero-point heads) as a template flag; the symmetric
 // instantiations are unchanged.  logits.hip instantiates the symmetric
