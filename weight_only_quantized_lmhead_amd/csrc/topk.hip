@@ -36,12 +36,16 @@
 //
 // Fused form (one activation row, topk <= 16): the GEMV itself writes one
 // sorted list of T codes per 64-row block, so pass 1 (and its read of y)
-// disappears; the merge takes up to 4096 lists (16 per thread): each wave's
-// T-th largest thread maximum bounds the row's T-th largest from below (that
-// wave alone has T entries at or above it), the largest of the four is the
-// first threshold, the lists whose heads reach it (at most 4T threads' worth)
-// give the second threshold (their T-th largest head: exactly T lists reach
-// it), and the entries at or above it of those T lists are ranked as above.
+// disappears; the merge (1024 threads: a few list heads per thread, so that
+// they arrive in one short burst; 16 per thread took 1.9 us longer) takes up
+// to 4096 lists: in each of four runs of 64 groups of 4 threads, the T-th
+// largest group maximum bounds the row's T-th largest from below (that run
+// alone has T entries at or above it), the largest of the four is the first
+// threshold, the lists whose heads reach it (at most 4T groups' worth) give
+// the second threshold (their T-th largest
+// head: exactly T lists reach it), and the entries at or above it of those T
+// lists are ranked as above.  The rescoring keeps the 256-thread grouping of
+// pass 2, so both paths add the same products in the same order.
 #include "lmh_internal.h"
 
 #include <math.h>
@@ -375,8 +379,9 @@ __global__ __launch_bounds__(256) void topk_select_rescore_kernel(
 }
 
 constexpr int kMergeMaxT = 17;     // topk <= 16, plus the top-1 candidate
-constexpr int kMergeLPT = 16;      // lists per thread: up to 4096 lists (64-row blocks) per row
-constexpr int kMergeMaxQual = 4 * kMergeMaxT * kMergeLPT;
+constexpr int kMergeThreads = 1024;
+constexpr int kMergeLPT = 4;       // lists per thread: up to 4096 lists (64-row blocks) per row
+constexpr int kMergeMaxQual = 4 * kMergeMaxT * 4 * kMergeLPT;  // 4T groups of 4 threads
 
 struct MergeShared {
     SelectShared s;
@@ -388,32 +393,48 @@ struct MergeShared {
 
 // The top T of C <= 4096 sorted lists of T codes into sh.s.sel, sorted (see
 // the header).  The lists are stored entry-major: entry j of list l at
-// L[j*C + l].  Thread i owns lists i, i + 256, ...  Ends with a barrier.
+// L[j*C + l].  1024 threads; thread i owns lists i, i + 1024, ... (a few
+// loads per thread: the heads arrive in one short burst), and the 4 threads
+// 4g .. 4g+3 form group g (up to 16 lists), whose largest head takes part in
+// the first threshold as one of 256.  Ends with a barrier.
 __device__ __forceinline__ void merge_lists(const u64* __restrict__ L, int C, int T,
                                             MergeShared& sh) {
-    const int tid = threadIdx.x, wv = tid >> 6;
+    const int tid = threadIdx.x;
     u64 hd[kMergeLPT];
     u64 tmax = 0;
 #pragma unroll
     for (int i = 0; i < kMergeLPT; ++i) {
-        const int l = tid + 256 * i;
+        const int l = tid + kMergeThreads * i;
         hd[i] = l < C ? L[l] : 0;
         tmax = hd[i] > tmax ? hd[i] : tmax;
     }
-    sh.s.heads[tid] = tmax;
+    // the group's largest head: lanes 4g .. 4g+3 of the wave
+    u64 gmax = tmax;
+#pragma unroll
+    for (int o = 1; o <= 2; o <<= 1) {
+        const u64 other = ((u64)(uint32_t)__shfl_xor((int)(uint32_t)(gmax >> 32), o) << 32) |
+                          (uint32_t)__shfl_xor((int)(uint32_t)gmax, o);
+        gmax = other > gmax ? other : gmax;
+    }
+    if ((tid & 3) == 0) sh.s.heads[tid >> 2] = gmax;
     if (tid < 4) sh.wthr[tid] = 0;
     if (tid == 0) {
         sh.s.nq = sh.s.cnt = 0;
         sh.thr2 = 0;
     }
     lds_barrier();
-    // first threshold: the largest of the waves' T-th largest thread maxima
-    // (0 when no wave has T lists: then every list takes part)
-    if (tmax != 0) {
-        int r = 0;
+    // first threshold: the largest of the T-th largest group maxima of the
+    // four runs of 64 groups (0 when no run has T lists: then every list
+    // takes part)
+    if (tid < 256) {
+        const u64 h = sh.s.heads[tid];
+        if (h != 0) {
+            const int run = tid >> 6;
+            int r = 0;
 #pragma unroll 16
-        for (int j = 0; j < 64; ++j) r += sh.s.heads[wv * 64 + j] > tmax;
-        if (r == T - 1) sh.wthr[wv] = tmax;
+            for (int j = 0; j < 64; ++j) r += sh.s.heads[run * 64 + j] > h;
+            if (r == T - 1) sh.wthr[run] = h;
+        }
     }
     lds_barrier();
     u64 thr1 = sh.wthr[0];
@@ -425,14 +446,16 @@ __device__ __forceinline__ void merge_lists(const u64* __restrict__ L, int C, in
             if (hd[i] != 0 && hd[i] >= thr1) {
                 const int q = atomicAdd(&sh.s.nq, 1);
                 sh.qh[q] = hd[i];
-                sh.ql[q] = tid + 256 * i;
+                sh.ql[q] = tid + kMergeThreads * i;
             }
         }
     }
     lds_barrier();
-    const int nq = sh.s.nq;  // <= 4T threads x 16 lists
+    // at most T groups of the run that sets the threshold and T - 1 of each
+    // other run reach it, with up to 16 lists each
+    const int nq = sh.s.nq;
     // second threshold: the T-th largest qualifying head (0 when fewer than T)
-    for (int q = tid; q < nq; q += 256) {
+    for (int q = tid; q < nq; q += kMergeThreads) {
         const u64 me = sh.qh[q];
         int r = 0;
         for (int j = 0; j < nq; ++j) r += sh.qh[j] > me;
@@ -441,7 +464,7 @@ __device__ __forceinline__ void merge_lists(const u64* __restrict__ L, int C, in
     lds_barrier();
     const u64 thr2 = sh.thr2;
     // the entries at or above it of the (at most T) lists whose heads reach it
-    for (int e = tid; e < nq * T; e += 256) {
+    for (int e = tid; e < nq * T; e += kMergeThreads) {
         const int q = e / T;
         if (sh.qh[q] >= thr2) {
             const u64 c = L[(int64_t)(e - q * T) * C + sh.ql[q]];
@@ -450,7 +473,7 @@ __device__ __forceinline__ void merge_lists(const u64* __restrict__ L, int C, in
     }
     lds_barrier();
     const int S = sh.s.cnt;  // T <= S <= T*T
-    for (int k = tid; k < S; k += 256) {
+    for (int k = tid; k < S; k += kMergeThreads) {
         const u64 me = sh.s.cs[k];
         int r = 0;
 #pragma unroll 8
@@ -461,7 +484,7 @@ __device__ __forceinline__ void merge_lists(const u64* __restrict__ L, int C, in
 }
 
 // Merge of the GEMV's per-block lists, then rescoring as in pass 2.
-__global__ __launch_bounds__(256) void topk_merge_rescore_kernel(
+__global__ __launch_bounds__(kMergeThreads) void topk_merge_rescore_kernel(
     const u64* __restrict__ lists, int C, int T, int topk, const void* __restrict__ x, int x_dtype,
     const void* __restrict__ w, int w_dtype, int64_t V, int64_t K, int vec, float* __restrict__ y,
     int64_t ldy, int32_t* __restrict__ idx_out, float* __restrict__ val_out,
@@ -482,7 +505,7 @@ inline int rescore_vec(const void* x, const void* w, int w_dtype, int64_t K) {
 }  // namespace
 
 bool topk_fused_ok(int64_t V, int topk) {
-    return topk + 1 <= kMergeMaxT && (V + 63) / 64 <= 256 * kMergeLPT;
+    return topk + 1 <= kMergeMaxT && (V + 63) / 64 <= kMergeThreads * kMergeLPT;
 }
 
 size_t topk_fused_lists_bytes(int64_t M, int64_t V, int topk) {
@@ -495,7 +518,7 @@ hipError_t launch_topk_merge_rescore(const u64* lists, const void* x, int x_dtyp
                                      int64_t ldy, int topk, int T, int32_t* idx, float* val,
                                      int32_t* top1, hipStream_t st) {
     const int C = (int)((V + 63) / 64);
-    hipLaunchKernelGGL(topk_merge_rescore_kernel, dim3(M), dim3(256), 0, st, lists, C, T, topk, x,
+    hipLaunchKernelGGL(topk_merge_rescore_kernel, dim3(M), dim3(kMergeThreads), 0, st, lists, C, T, topk, x,
                        x_dtype, w, w_dtype, V, K, rescore_vec(x, w, w_dtype, K), y, ldy, idx, val,
                        top1);
     return hipGetLastError();
