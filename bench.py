@@ -27,7 +27,9 @@ over the same bytes); every call beyond one activation row also carries the
 read+write ceiling for its own byte mix (lmhead_stream_mix: the head's bytes
 read, its logits buffer written) and, on an MFMA kernel, the MFMA ceiling for
 its flops (lmhead_mfma_ceiling); `cpu_baseline` times the fp64 oracle on the
-host cores.
+host cores.  With --size-sweep, `size_sweep` has the read-only stream and the
+first M's logits call on heads of several times the vocabulary, each fitted
+as a fixed cost per launch plus bytes over a steady rate.
 """
 from __future__ import annotations
 
@@ -402,6 +404,10 @@ def main() -> int:
                     help="also report, over N seeded decode states (one activation row each), the "
                          "top-1 agreement with the unquantized 16-bit weight before and after exact "
                          "top-K rescoring, and the top-K set overlap")
+    ap.add_argument("--size-sweep", default=None, metavar="MULTS",
+                    help="also time the read-only stream and the first M's logits call on heads of "
+                         "these multiples of the workload's vocabulary (e.g. 2,4,8; cold), and fit "
+                         "time = fixed + bytes / rate to both")
     ap.add_argument("--cpu-seconds", type=float, default=16.0)
     ap.add_argument("--record", metavar="PATH",
                     help="also write the JSON line, with the command that made it, as a markdown file")
@@ -713,6 +719,42 @@ def main() -> int:
                                 "bytes": blob_bytes, "frac_of_hbm_peak": round(rd_gbs / HBM_PEAK_GBS, 4)}
     roofline["frac_of_read_ceiling"] = round(rd_us / value, 4) if Ms[0] == 1 else None
 
+    sweep = None
+    if args.size_sweep:
+        # the same two calls on longer vocabularies: the slope of time against
+        # bytes is the steady rate, the intercept the fixed cost of a launch
+        mults = [1] + [int(m) for m in args.size_sweep.split(",") if int(m) > 1]
+        pts = [(1, blob_bytes, R, rd_us, m1["us"])]
+        gen = torch.Generator(device=dev).manual_seed(w.wid)
+        for mult in mults[1:]:
+            Vm = w.V * mult
+            Wm = (torch.randn((Vm, w.K), generator=gen, device=dev) * 0.02).to(torch.float16)
+            bm = lmh.quantize_pack(Wm, w.bits, w.group, sdt)
+            del Wm
+            Rm = 1 if args.hot else max(2, math.ceil(1e9 / bm.numel()))
+            bms = [bm] + [bm.clone() for _ in range(Rm - 1)]
+            om = torch.empty((Ms[0], Vm), dtype=torch.float32, device=dev)
+            r_us, _ = both(lambda: [lmh.prepare_stream_read(b, sink) for b in bms])
+            l_us, _ = both(lambda: [lmh.prepare_logits(xs[Ms[0]], b, Vm, w.K, w.bits, w.group, sdt,
+                                                       out=om, workspace=wss[Ms[0]], path=args.path)
+                                    for b in bms])
+            pts.append((mult, bm.numel(), Rm, r_us, l_us))
+            log(f"size x{mult}: read {r_us:.2f} us, logits {l_us:.2f} us")
+            del bms, bm, om
+            torch.cuda.empty_cache()
+
+        def fit(col):
+            xb = np.array([p[1] for p in pts], dtype=np.float64)
+            t = np.array([p[col] for p in pts], dtype=np.float64)
+            slope, icpt = np.polyfit(xb, t, 1)  # us per byte, us
+            return {"GB/s": round(1e-3 / slope, 1), "frac_of_hbm_peak": round(1e-3 / slope / HBM_PEAK_GBS, 4),
+                    "fixed_us": round(icpt, 3)}
+
+        sweep = {"multiples": [p[0] for p in pts], "bytes": [p[1] for p in pts],
+                 "copies": [p[2] for p in pts], "read_us": [p[3] for p in pts],
+                 "logits_us": [p[4] for p in pts], "M": Ms[0],
+                 "read_fit": fit(3), "logits_fit": fit(4)}
+
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle on the host cores)")
@@ -739,6 +781,8 @@ def main() -> int:
     }
     if agreement is not None:
         line["agreement"] = agreement
+    if sweep is not None:
+        line["size_sweep"] = sweep
     print(json.dumps(line), flush=True)
     if args.record:
         argv, skip = [], False
