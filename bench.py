@@ -214,7 +214,8 @@ SQ_PASSES = [
 
 
 def summarize_sq(args) -> int:
-    """Write a profiles/ summary of SQ counters per logits kernel from the
+    """Write a profiles/ summary of SQ counters per kernel (the logits
+    kernels, the read-only stream, the quantizer and packers) from the
     counter_collection.csv files of the SQ_PASSES runs (--sq, one per pass)."""
     import csv
     import statistics
@@ -223,11 +224,11 @@ def summarize_sq(args) -> int:
     for path in args.sq:
         for r in csv.DictReader(open(path)):
             k = _short_kernel(r["Kernel_Name"])
-            if not k.startswith(("gemv_kernel", "mfma", "stream_read")):
+            if not k.startswith(("gemv_kernel", "mfma", "stream_read", "quant_", "pack_")):
                 continue
             key = f"{k} grid {r['Grid_Size']}"
             vals.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
-    out = [f"# SQ counters of the logits kernels ({args.workload or 'headline'} head), one MI355X\n",
+    out = [f"# SQ counters per kernel ({args.workload or 'headline'} head), one MI355X\n",
            "Commands (from the repository root; `export TMPDIR=/tmp` first):\n", "```"]
     out += args.cmd
     out += ["```\n",
