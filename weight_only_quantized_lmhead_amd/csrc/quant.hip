@@ -186,21 +186,56 @@ __device__ __forceinline__ double errN(const float* w, const float* q, float sv,
     return err;
 }
 
+// Staging of a wave's 64 rows through LDS, so that its global loads are
+// coalesced: a piece of up to 256 bytes of every row is read with 16-byte
+// loads whose consecutive lanes take consecutive 16 bytes of one row (a load
+// instruction covers 64 / P rows, P = piece bytes / 16), written to the
+// wave's own LDS region, rows padded by 16 bytes, and read back one row per
+// lane.  The padding makes the row stride (P + 1 words of 16 bytes) odd, so
+// the 64 lanes' reads of word p of their rows fall in distinct banks.
+constexpr int kStagePiece = 256;  // most bytes of a row staged at once
+
 // A group of NE <= 128 weights of one row held in registers: fp32 as is,
 // 16-bit weights as their raw bit patterns two to a register (widened on use).
 template <int WDT, int NE>
 struct Held {
     static constexpr int kWords = WDT == F32 ? NE : NE / 2;
+    static constexpr int kRowBytes = kWords * 4;
+    static constexpr int kPiece = kRowBytes < kStagePiece ? kRowBytes : kStagePiece;
+    static constexpr int P = kPiece / 16;  // 16-byte words per row and piece
+    static constexpr int RPI = 64 / P;     // rows per load instruction
+    static constexpr int kStageWords = 64 * (P + 1);  // a wave's LDS region, 16-byte words
     uint32_t v[kWords];
-    __device__ __forceinline__ void load(const RowSrc<WDT>& src, int col0) {
-        constexpr int per16 = WDT == F32 ? 4 : 8;  // elements per 16-byte load
+    // Columns [col0, col0 + NE) of the wave's 64 rows (block b; rows past the
+    // launch's input read as zeros), lane r receiving row 64b + r.  `st` is
+    // the wave's LDS region (kStageWords words).
+    __device__ __forceinline__ void load(const QuantArgs& a, int64_t b, int col0, uint4* st) {
+        constexpr int esz = WDT == F32 ? 4 : 2;
+        const int lane = threadIdx.x & 63;
+        const int rq = lane / P, pw = lane % P;  // this lane's row (of each RPI) and word
+        const int64_t lr0 = b * 64 - a.row0 + rq;
+        const char* wb = (const char*)a.w + (size_t)col0 * esz + pw * 16;
 #pragma unroll
-        for (int k = 0; k < NE; k += per16) {
-            uint4 u = make_uint4(0, 0, 0, 0);
-            if (src.valid)
-                u = *(const uint4*)(src.row + (size_t)(col0 + k) * (WDT == F32 ? 4 : 2));
-            const int o = WDT == F32 ? k : k / 2;
-            v[o] = u.x, v[o + 1] = u.y, v[o + 2] = u.z, v[o + 3] = u.w;
+        for (int pc = 0; pc < kRowBytes / kPiece; ++pc) {
+            uint4 u[P];
+#pragma unroll
+            for (int i = 0; i < P; ++i) {
+                const int64_t lr = lr0 + i * RPI;
+                u[i] = lr < a.rows ? *(const uint4*)(wb + lr * a.ldw * esz + pc * kPiece)
+                                   : make_uint4(0, 0, 0, 0);
+            }
+            // every lane's reads of the previous piece are done before its
+            // words are overwritten (LDS operations of a wave run in order)
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int i = 0; i < P; ++i) st[(i * RPI + rq) * (P + 1) + pw] = u[i];
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int w = 0; w < P; ++w) {
+                const uint4 x = st[lane * (P + 1) + w];
+                const int o = pc * (kPiece / 4) + 4 * w;
+                v[o] = x.x, v[o + 1] = x.y, v[o + 2] = x.z, v[o + 3] = x.w;
+            }
         }
     }
     // N weights starting at element k (a multiple of N), as fp32
@@ -431,12 +466,14 @@ quant_held_kernel(
     constexpr int UC = PACKED ? (GT > span ? GT : span) : GT;  // unit columns
     constexpr int CPS = span / 32;                             // chunks per superchunk
     const int col_u = u * UC;
+    __shared__ uint4 stage[4][Held<WDT, GT>::kStageWords];  // one region per wave
+    uint4* st = stage[threadIdx.x >> 6];
     uint32_t sw[4][4];
 #pragma unroll
     for (int gi = 0; gi < UC / GT; ++gi) {
         const int col0 = col_u + gi * GT;
         Held<WDT, GT> h;
-        h.load(src, col0);
+        h.load(a, b, col0, st);
         bool zero;
         float zf = 0.0f;
         const float sv = ASYM ? pick_asym<BITS, true>(HeldGet<WDT, GT>{h}, GT, a.cf, zero, zf)
