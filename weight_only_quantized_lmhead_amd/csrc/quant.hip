@@ -12,7 +12,9 @@
 // Work mapping.  One wavefront owns one 64-row block of the head and one unit
 // of columns; lane r owns row 64b + r.  A group of up to 128 columns stays in
 // the lane's registers for every pass (amax, each clip ratio, the final
-// codes); a longer group is streamed from memory once per pass.  Two outputs:
+// codes); a longer group is streamed from memory once per pass.  Either way
+// the weights arrive through the wave's own LDS region: coalesced loads (each
+// covering a few rows) in, one row per lane out.  Two outputs:
 //   * codes mode: q int8 [V, K] and s [V, K/G] row-major (lmhead_quantize);
 //   * packed mode: the blob itself (lmhead_quantize_pack).  The unit is one
 //     superchunk of the packed layout (or one group, when a group is longer),
@@ -96,44 +98,12 @@ struct QRange {
     static constexpr float qr = BITS == 4 ? 15.0f : 255.0f;  // unsigned code range (ASYM)
 };
 
-// Eight consecutive weights of one row, widened exactly to fp32.
-template <int WDT>
-__device__ __forceinline__ void load8(const char* row, int col, float* o) {
-    if constexpr (WDT == F32) {
-        const float4 x0 = *(const float4*)(row + (size_t)col * 4);
-        const float4 x1 = *(const float4*)(row + (size_t)col * 4 + 16);
-        o[0] = x0.x, o[1] = x0.y, o[2] = x0.z, o[3] = x0.w;
-        o[4] = x1.x, o[5] = x1.y, o[6] = x1.z, o[7] = x1.w;
-    } else {
-        const uint4 u = *(const uint4*)(row + (size_t)col * 2);
-        const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if constexpr (WDT == BF16) {
-                o[2 * j] = __uint_as_float(wd[j] << 16);
-                o[2 * j + 1] = __uint_as_float(wd[j] & 0xFFFF0000u);
-            } else {
-                o[2 * j] = f16_to_f32((uint16_t)wd[j]);
-                o[2 * j + 1] = f16_to_f32((uint16_t)(wd[j] >> 16));
-            }
-        }
-    }
-}
-
 // A lane's row; rows outside the launch's input (the padding rows of the last
 // block) read as zeros.
 template <int WDT>
 struct RowSrc {
     const char* row;
     bool valid;
-    __device__ __forceinline__ void get8(int col, float* o) const {
-        if (valid) {
-            load8<WDT>(row, col, o);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) o[i] = 0.0f;
-        }
-    }
 };
 
 __device__ __forceinline__ float round_scale(float s32, int sbf16) {
@@ -256,13 +226,6 @@ struct Held {
     }
 };
 
-// Streamed weights of one row: N from column col, read from memory.
-template <int WDT, int N>
-__device__ __forceinline__ void get_stream(const RowSrc<WDT>& src, int col, float* w) {
-#pragma unroll
-    for (int k = 0; k < N; k += 8) src.get8(col + k, w + k);
-}
-
 template <int WDT, int NE>
 struct HeldGet {
     const Held<WDT, NE>& h;
@@ -272,13 +235,57 @@ struct HeldGet {
     }
 };
 
+// A longer group's columns [col0 + k, col0 + k + N) of each lane's row for a
+// pass that walks k upwards from 0 in steps of N <= 32: every 64 columns
+// (which divide the group) the wave stages the next 64 columns of its 64
+// rows through its LDS region as above, so the pass's loads are coalesced.
 template <int WDT>
-struct StreamGet {
-    const RowSrc<WDT>& src;
+struct StageGet {
+    static constexpr int esz = WDT == F32 ? 4 : 2;
+    static constexpr int P = 64 * esz / 16;  // 16-byte words per row of a 64-column piece
+    static constexpr int RPI = 64 / P;
+    static constexpr int kStageWords = 64 * (P + 1);
+    const QuantArgs& a;
+    int64_t b;
     int col0;
+    uint4* st;
+    __device__ __forceinline__ void stage(int colp) const {
+        const int lane = threadIdx.x & 63;
+        const int rq = lane / P, pw = lane % P;
+        const int64_t lr0 = b * 64 - a.row0 + rq;
+        const char* wb = (const char*)a.w + (size_t)colp * esz + pw * 16;
+        uint4 u[P];
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            const int64_t lr = lr0 + i * RPI;
+            u[i] = lr < a.rows ? *(const uint4*)(wb + lr * a.ldw * esz) : make_uint4(0, 0, 0, 0);
+        }
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int i = 0; i < P; ++i) st[(i * RPI + rq) * (P + 1) + pw] = u[i];
+        asm volatile("" ::: "memory");
+    }
     template <int N>
     __device__ __forceinline__ void operator()(int k, float* o) const {
-        get_stream<WDT, N>(src, col0 + k, o);
+        if (k % 64 == 0) stage(col0 + k);
+        const uint4* row = st + (threadIdx.x & 63) * (P + 1) + (k % 64) * esz / 16;
+#pragma unroll
+        for (int j = 0; j < N * esz / 16; ++j) {
+            const uint4 x = row[j];
+            const uint32_t wd[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if constexpr (WDT == F32) {
+                    o[4 * j + e] = __uint_as_float(wd[e]);
+                } else if constexpr (WDT == BF16) {
+                    o[8 * j + 2 * e] = __uint_as_float(wd[e] << 16);
+                    o[8 * j + 2 * e + 1] = __uint_as_float(wd[e] & 0xFFFF0000u);
+                } else {
+                    o[8 * j + 2 * e] = f16_to_f32((uint16_t)wd[e]);
+                    o[8 * j + 2 * e + 1] = f16_to_f32((uint16_t)(wd[e] >> 16));
+                }
+            }
+        }
     }
 };
 
@@ -522,10 +529,12 @@ __global__ __launch_bounds__(256, 2) void quant_stream_kernel(const QuantArgs a)
     const int64_t v = b * 64 + r;
     const RowSrc<WDT> src = lane_row<WDT>(a, v);
     const int col0 = g * a.G;
+    __shared__ uint4 stage[4][StageGet<WDT>::kStageWords];  // one region per wave
+    const StageGet<WDT> get{a, b, col0, stage[threadIdx.x >> 6]};
     bool zero;
     float zf = 0.0f;
-    const float sv = ASYM ? pick_asym<BITS, false>(StreamGet<WDT>{src, col0}, a.G, a.cf, zero, zf)
-                          : pick_scale<BITS, false>(StreamGet<WDT>{src, col0}, a.G, a.cf, zero);
+    const float sv = ASYM ? pick_asym<BITS, false>(get, a.G, a.cf, zero, zf)
+                          : pick_scale<BITS, false>(get, a.G, a.cf, zero);
     const uint16_t sb = scale_bits(sv, zero, a.cf.sbf16);
     const double rr = 1.0 / (double)sv;
     if constexpr (PACKED) {
@@ -538,23 +547,26 @@ __global__ __launch_bounds__(256, 2) void quant_stream_kernel(const QuantArgs a)
 #pragma unroll
             for (int ch = 0; ch < span / 32; ++ch) {
                 float w[32], q[32];
-                get_stream<WDT, 32>(src, c * span + 32 * ch, w);
+                get.template operator()<32>(c * span + 32 * ch - col0, w);
                 if constexpr (ASYM) codes_asym<BITS, 32>(w, rr, zf, q);
                 else codes<BITS, 32>(w, rr, q);
                 put_chunk<BITS, ASYM>(q, ch, sw);
             }
             store_slots(a.wout, b, a.NC, c, r, sw);
         }
-    } else if (src.valid) {
-        a.s[v * a.NG + g] = sb;
-        if constexpr (ASYM) a.z[v * a.NG + g] = (uint8_t)(int)zf;
+    } else {
+        // every lane takes part in the staging; rows past the head store nothing
+        if (src.valid) {
+            a.s[v * a.NG + g] = sb;
+            if constexpr (ASYM) a.z[v * a.NG + g] = (uint8_t)(int)zf;
+        }
 #pragma unroll 1
         for (int col = col0; col < col0 + a.G; col += 32) {
             float w[32], q[32];
-            get_stream<WDT, 32>(src, col, w);
+            get.template operator()<32>(col - col0, w);
             if constexpr (ASYM) codes_asym<BITS, 32>(w, rr, zf, q);
             else codes<BITS, 32>(w, rr, q);
-            store_codes32(a.q + v * a.K + col, q);
+            if (src.valid) store_codes32(a.q + v * a.K + col, q);
         }
     }
 }
