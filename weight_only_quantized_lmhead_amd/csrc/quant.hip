@@ -623,47 +623,68 @@ QCfg make_cfg(int bits, int scale_dtype, int nratios, bool asym) {
     return cf;
 }
 
-// One thread per 16-byte weight slot of the blob.  ZP: the codes are the
-// unsigned n (stored as they are; padding rows 0), else the signed q (stored
-// biased by 8 / 128; padding rows q = 0).
+// One thread per 16-byte weight slot of the blob, one workgroup per (64-row
+// block, superchunk).  ZP: the codes are the unsigned n (stored as they are;
+// padding rows 0), else the signed q (stored biased by 8 / 128; padding rows
+// q = 0).  The superchunk's codes (64 rows x 128 or 64 bytes) are first
+// staged in LDS with coalesced 16-byte loads (consecutive threads take
+// consecutive pieces of one row; rows padded by 8 bytes), then each thread
+// builds its slot from its row there.
 template <int BITS, bool ZP>
 __global__ __launch_bounds__(256) void pack_weights_kernel(const int8_t* __restrict__ q, int64_t V,
                                                            int64_t K, int64_t nslots, int NC,
                                                            uint4* __restrict__ out) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= nslots) return;
-    const int r = (int)(i & 63);
-    const int t = (int)((i >> 6) & 3);
-    const int64_t bc = i >> 8;  // b * NC + c
+    constexpr int RB = BITS == 4 ? 128 : 64;  // code bytes of a row in one superchunk
+    constexpr int RS = RB + 8;                // LDS row stride
+    constexpr int PPR = RB / 16;              // 16-byte pieces per row
+    __shared__ __attribute__((aligned(16))) uint8_t cs[64 * RS];
+    const int64_t bc = blockIdx.x;  // b * NC + c
+    if (bc * 256 >= nslots) return;
     const int c = (int)(bc % NC);
     const int64_t b = bc / NC;
+    for (int e = threadIdx.x; e < 64 * PPR; e += 256) {
+        const int rr = e / PPR, pc = e % PPR;
+        const int64_t vr = b * 64 + rr;
+        uint4 u = make_uint4(0, 0, 0, 0);
+        if (vr < V) u = *(const uint4*)(q + vr * K + (int64_t)c * RB + 16 * pc);
+        uint2* d = (uint2*)(cs + rr * RS + 16 * pc);
+        d[0] = make_uint2(u.x, u.y);
+        d[1] = make_uint2(u.z, u.w);
+    }
+    __syncthreads();
+    const int r = threadIdx.x & 63;
+    const int t = threadIdx.x >> 6;
     const int64_t v = b * 64 + r;
+    const uint8_t* row = cs + r * RS;
     uint32_t word[4];
     if (v >= V) {
         const uint32_t pad = ZP ? 0u : (BITS == 4 ? 0x88888888u : 0x80808080u);
         for (int j = 0; j < 4; ++j) word[j] = pad;
     } else if constexpr (BITS == 4) {
         for (int j = 0; j < 4; ++j) {
-            const int8_t* src = q + v * K + (int64_t)c * 128 + 32 * j + 8 * t;
+            const uint2 w8 = *(const uint2*)(row + 32 * j + 8 * t);
             uint32_t wd = 0;
             for (int i8 = 0; i8 < 8; ++i8) {
+                const int code = (int8_t)((i8 < 4 ? w8.x >> (8 * i8) : w8.y >> (8 * (i8 - 4))) & 0xFFu);
                 // column i8 goes to nibble position p: even columns 0,2,4,6 -> p 0..3,
                 // odd columns 1,3,5,7 -> p 4..7
                 const int p = (i8 & 1) ? 4 + (i8 >> 1) : (i8 >> 1);
-                wd |= (uint32_t)((src[i8] + (ZP ? 0 : 8)) & 0xF) << (4 * p);
+                wd |= (uint32_t)((code + (ZP ? 0 : 8)) & 0xF) << (4 * p);
             }
             word[j] = wd;
         }
     } else {
         for (int j = 0; j < 4; ++j) {
-            const int8_t* src = q + v * K + (int64_t)c * 64 + 32 * (j >> 1) + 8 * t + 4 * (j & 1);
+            const uint32_t w4 = *(const uint32_t*)(row + 32 * (j >> 1) + 8 * t + 4 * (j & 1));
             uint32_t wd = 0;
-            for (int i4 = 0; i4 < 4; ++i4)
-                wd |= (uint32_t)(uint8_t)(src[i4] + (ZP ? 0 : 128)) << (8 * i4);
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const int code = (int8_t)((w4 >> (8 * i4)) & 0xFFu);
+                wd |= (uint32_t)(uint8_t)(code + (ZP ? 0 : 128)) << (8 * i4);
+            }
             word[j] = wd;
         }
     }
-    out[i] = make_uint4(word[0], word[1], word[2], word[3]);
+    out[bc * 256 + threadIdx.x] = make_uint4(word[0], word[1], word[2], word[3]);
 }
 
 __global__ __launch_bounds__(256) void pack_scales_kernel(const uint16_t* __restrict__ s, int64_t V,
