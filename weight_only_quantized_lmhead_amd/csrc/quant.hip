@@ -98,14 +98,6 @@ struct QRange {
     static constexpr float qr = BITS == 4 ? 15.0f : 255.0f;  // unsigned code range (ASYM)
 };
 
-// A lane's row; rows outside the launch's input (the padding rows of the last
-// block) read as zeros.
-template <int WDT>
-struct RowSrc {
-    const char* row;
-    bool valid;
-};
-
 __device__ __forceinline__ float round_scale(float s32, int sbf16) {
     return sbf16 ? bf16_to_f32(f32_to_bf16_rne(s32)) : f16_to_f32(f32_to_f16_rne(s32));
 }
@@ -427,12 +419,10 @@ __device__ __forceinline__ void store_codes32(int8_t* dst, const float* q) {
     *(uint4*)(dst + 16) = make_uint4(wd[4], wd[5], wd[6], wd[7]);
 }
 
-template <int WDT>
-__device__ __forceinline__ RowSrc<WDT> lane_row(const QuantArgs& a, int64_t v) {
-    constexpr int esz = WDT == F32 ? 4 : 2;
-    const int64_t lr = v - a.row0;
-    const bool valid = lr < a.rows;
-    return RowSrc<WDT>{(const char*)a.w + (valid ? lr : 0) * a.ldw * esz, valid};
+// Whether head row v lies in the launch's input (the padding rows of the last
+// block do not: they read as zeros and store nothing of their own).
+__device__ __forceinline__ bool row_present(const QuantArgs& a, int64_t v) {
+    return v - a.row0 < a.rows;
 }
 
 // Groups of GT <= 128 columns, held in registers.  Unit: one superchunk (or
@@ -468,7 +458,7 @@ quant_held_kernel(
     const int64_t b = a.blk0 + unit / a.upb;
     const int u = (int)(unit % a.upb);
     const int64_t v = b * 64 + r;
-    const RowSrc<WDT> src = lane_row<WDT>(a, v);
+    const bool present = row_present(a, v);
     constexpr int span = span_of(BITS);
     constexpr int UC = PACKED ? (GT > span ? GT : span) : GT;  // unit columns
     constexpr int CPS = span / 32;                             // chunks per superchunk
@@ -501,7 +491,7 @@ quant_held_kernel(
                 if (cu % CPS == CPS - 1) store_slots(a.wout, b, a.NC, (col_u + 32 * cu) / span, r, sw);
                 __builtin_amdgcn_sched_barrier(0);
             }
-        } else if (src.valid) {
+        } else if (present) {
             a.s[v * a.NG + col0 / GT] = sb;
             if constexpr (ASYM) a.z[v * a.NG + col0 / GT] = (uint8_t)(int)zf;
 #pragma unroll
@@ -527,7 +517,7 @@ __global__ __launch_bounds__(256, 2) void quant_stream_kernel(const QuantArgs a)
     const int64_t b = a.blk0 + unit / a.upb;
     const int g = (int)(unit % a.upb);
     const int64_t v = b * 64 + r;
-    const RowSrc<WDT> src = lane_row<WDT>(a, v);
+    const bool present = row_present(a, v);
     const int col0 = g * a.G;
     __shared__ uint4 stage[4][StageGet<WDT>::kStageWords];  // one region per wave
     const StageGet<WDT> get{a, b, col0, stage[threadIdx.x >> 6]};
@@ -556,7 +546,7 @@ __global__ __launch_bounds__(256, 2) void quant_stream_kernel(const QuantArgs a)
         }
     } else {
         // every lane takes part in the staging; rows past the head store nothing
-        if (src.valid) {
+        if (present) {
             a.s[v * a.NG + g] = sb;
             if constexpr (ASYM) a.z[v * a.NG + g] = (uint8_t)(int)zf;
         }
@@ -566,7 +556,7 @@ __global__ __launch_bounds__(256, 2) void quant_stream_kernel(const QuantArgs a)
             get.template operator()<32>(col - col0, w);
             if constexpr (ASYM) codes_asym<BITS, 32>(w, rr, zf, q);
             else codes<BITS, 32>(w, rr, q);
-            if (src.valid) store_codes32(a.q + v * a.K + col, q);
+            if (present) store_codes32(a.q + v * a.K + col, q);
         }
     }
 }
