@@ -114,7 +114,8 @@ def test_quantize_pack_byte_exact(wdt, bits, G, sdt, clip):
 
 
 @pytest.mark.parametrize("bits,G,wdt,clip", [(4, 128, "bf16", "mse"), (8, 64, "f32", "rtn"),
-                                             (8, 256, "f16", "mse"), (4, 32, "f16", "rtn")])
+                                             (8, 256, "f16", "mse"), (4, 32, "f16", "rtn"),
+                                             (4, 512, "f32", "rtn"), (8, 256, "bf16", "rtn")])
 def test_quantize_pack_chunked(bits, G, wdt, clip):
     """Chunks of whole 64-row blocks, in any order and from a strided source,
     write the same bytes as one call over the head; the last chunk may be ragged."""
