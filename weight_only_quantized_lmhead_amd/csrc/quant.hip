@@ -157,6 +157,32 @@ __device__ __forceinline__ double errN(const float* w, const float* q, float sv,
 // the 64 lanes' reads of word p of their rows fall in distinct banks.
 constexpr int kStagePiece = 256;  // most bytes of a row staged at once
 
+// Stage 16 P bytes of each of the wave's 64 rows (block b), from column colp
+// on, into st with a row stride of P + 1 words; rows past the launch's input
+// as zeros.
+template <int WDT, int P>
+__device__ __forceinline__ void stage_piece(const QuantArgs& a, int64_t b, int colp, uint4* st) {
+    constexpr int esz = WDT == F32 ? 4 : 2;
+    constexpr int RPI = 64 / P;  // rows per load instruction
+    const int lane = threadIdx.x & 63;
+    const int rq = lane / P, pw = lane % P;  // this lane's row (of each RPI) and word
+    const int64_t lr0 = b * 64 - a.row0 + rq;
+    const char* wb = (const char*)a.w + (size_t)colp * esz + pw * 16;
+    uint4 u[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        const int64_t lr = lr0 + i * RPI;
+        u[i] = lr < a.rows ? *(const uint4*)(wb + lr * a.ldw * esz) : make_uint4(0, 0, 0, 0);
+    }
+    // every lane's reads of the previous piece are done before its words are
+    // overwritten (LDS operations of a wave run in order); the empty asm
+    // statements keep the compiler from moving accesses across
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < P; ++i) st[(i * RPI + rq) * (P + 1) + pw] = u[i];
+    asm volatile("" ::: "memory");
+}
+
 // A group of NE <= 128 weights of one row held in registers: fp32 as is,
 // 16-bit weights as their raw bit patterns two to a register (widened on use).
 template <int WDT, int NE>
@@ -165,7 +191,6 @@ struct Held {
     static constexpr int kRowBytes = kWords * 4;
     static constexpr int kPiece = kRowBytes < kStagePiece ? kRowBytes : kStagePiece;
     static constexpr int P = kPiece / 16;  // 16-byte words per row and piece
-    static constexpr int RPI = 64 / P;     // rows per load instruction
     static constexpr int kStageWords = 64 * (P + 1);  // a wave's LDS region, 16-byte words
     uint32_t v[kWords];
     // Columns [col0, col0 + NE) of the wave's 64 rows (block b; rows past the
@@ -174,24 +199,9 @@ struct Held {
     __device__ __forceinline__ void load(const QuantArgs& a, int64_t b, int col0, uint4* st) {
         constexpr int esz = WDT == F32 ? 4 : 2;
         const int lane = threadIdx.x & 63;
-        const int rq = lane / P, pw = lane % P;  // this lane's row (of each RPI) and word
-        const int64_t lr0 = b * 64 - a.row0 + rq;
-        const char* wb = (const char*)a.w + (size_t)col0 * esz + pw * 16;
 #pragma unroll
         for (int pc = 0; pc < kRowBytes / kPiece; ++pc) {
-            uint4 u[P];
-#pragma unroll
-            for (int i = 0; i < P; ++i) {
-                const int64_t lr = lr0 + i * RPI;
-                u[i] = lr < a.rows ? *(const uint4*)(wb + lr * a.ldw * esz + pc * kPiece)
-                                   : make_uint4(0, 0, 0, 0);
-            }
-            // every lane's reads of the previous piece are done before its
-            // words are overwritten (LDS operations of a wave run in order)
-            asm volatile("" ::: "memory");
-#pragma unroll
-            for (int i = 0; i < P; ++i) st[(i * RPI + rq) * (P + 1) + pw] = u[i];
-            asm volatile("" ::: "memory");
+            stage_piece<WDT, P>(a, b, col0 + pc * (kPiece / esz), st);
 #pragma unroll
             for (int w = 0; w < P; ++w) {
                 const uint4 x = st[lane * (P + 1) + w];
@@ -235,31 +245,14 @@ template <int WDT>
 struct StageGet {
     static constexpr int esz = WDT == F32 ? 4 : 2;
     static constexpr int P = 64 * esz / 16;  // 16-byte words per row of a 64-column piece
-    static constexpr int RPI = 64 / P;
     static constexpr int kStageWords = 64 * (P + 1);
     const QuantArgs& a;
     int64_t b;
     int col0;
     uint4* st;
-    __device__ __forceinline__ void stage(int colp) const {
-        const int lane = threadIdx.x & 63;
-        const int rq = lane / P, pw = lane % P;
-        const int64_t lr0 = b * 64 - a.row0 + rq;
-        const char* wb = (const char*)a.w + (size_t)colp * esz + pw * 16;
-        uint4 u[P];
-#pragma unroll
-        for (int i = 0; i < P; ++i) {
-            const int64_t lr = lr0 + i * RPI;
-            u[i] = lr < a.rows ? *(const uint4*)(wb + lr * a.ldw * esz) : make_uint4(0, 0, 0, 0);
-        }
-        asm volatile("" ::: "memory");
-#pragma unroll
-        for (int i = 0; i < P; ++i) st[(i * RPI + rq) * (P + 1) + pw] = u[i];
-        asm volatile("" ::: "memory");
-    }
     template <int N>
     __device__ __forceinline__ void operator()(int k, float* o) const {
-        if (k % 64 == 0) stage(col0 + k);
+        if (k % 64 == 0) stage_piece<WDT, P>(a, b, col0 + k, st);
         const uint4* row = st + (threadIdx.x & 63) * (P + 1) + (k % 64) * esz / 16;
 #pragma unroll
         for (int j = 0; j < N * esz / 16; ++j) {
