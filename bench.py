@@ -62,6 +62,17 @@ TRAFFIC_SOURCES = ["weight_only_quantized_lmhead_amd/csrc/gemv.hip",
                    "weight_only_quantized_lmhead_amd/build.py"]
 
 
+def fit_fixed_rate(nbytes, us):
+    """Least-squares fit of time = fixed + bytes / rate to calls of several
+    sizes: the steady rate (GB/s, and as a fraction of the HBM peak) and the
+    fixed cost of a launch (us)."""
+    import numpy as np
+
+    slope, icpt = np.polyfit(np.asarray(nbytes, dtype=np.float64), np.asarray(us, dtype=np.float64), 1)
+    return {"GB/s": round(1e-3 / slope, 1), "frac_of_hbm_peak": round(1e-3 / slope / HBM_PEAK_GBS, 4),
+            "fixed_us": round(icpt, 3)}
+
+
 def sources_sha() -> str:
     import hashlib
 
@@ -744,17 +755,11 @@ def main() -> int:
             del bms, bm, om
             torch.cuda.empty_cache()
 
-        def fit(col):
-            xb = np.array([p[1] for p in pts], dtype=np.float64)
-            t = np.array([p[col] for p in pts], dtype=np.float64)
-            slope, icpt = np.polyfit(xb, t, 1)  # us per byte, us
-            return {"GB/s": round(1e-3 / slope, 1), "frac_of_hbm_peak": round(1e-3 / slope / HBM_PEAK_GBS, 4),
-                    "fixed_us": round(icpt, 3)}
-
         sweep = {"multiples": [p[0] for p in pts], "bytes": [p[1] for p in pts],
                  "copies": [p[2] for p in pts], "read_us": [p[3] for p in pts],
                  "logits_us": [p[4] for p in pts], "M": Ms[0],
-                 "read_fit": fit(3), "logits_fit": fit(4)}
+                 "read_fit": fit_fixed_rate([p[1] for p in pts], [p[3] for p in pts]),
+                 "logits_fit": fit_fixed_rate([p[1] for p in pts], [p[4] for p in pts])}
 
     cpu = None
     if not args.no_cpu_baseline:

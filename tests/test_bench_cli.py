@@ -3,7 +3,8 @@ than one GPU exits with a message before anything touches a device), the
 options it documents, and the writers of the profiles/ summaries on small
 hand-made rocprofv3 CSV files -- kernel-name shortening, the FETCH_SIZE /
 WRITE_SIZE calibration against the read-only stream and the head clones, the
-sources hash that gates `traffic`, and the SQ counters' derived columns."""
+sources hash that gates `traffic`, and the SQ counters' derived columns --
+and the size sweep's fit of a fixed cost plus a steady rate."""
 import argparse
 import csv
 import json
@@ -143,3 +144,16 @@ def test_summarize_sq_derived_columns(tmp_path):
     # instruction, waves
     assert cells[1:] == ["50.0%", "25.0%", "25.0%", "10.0%", "50.0%", "640.00", "0.50", "0.50", "4096"]
     assert "copyBuffer" not in out.read_text()
+
+
+def test_size_sweep_fit():
+    """time = fixed + bytes / rate, recovered from points on an exact line
+    (6000 GB/s and 2 us: a call of B bytes takes 2 + B / 6000 * 1e-3 us) and
+    from the same points with symmetric noise."""
+    nb = [82653184 * m for m in (1, 2, 4, 8)]
+    us = [2.0 + b / 6000.0 * 1e-3 for b in nb]
+    f = bench.fit_fixed_rate(nb, us)
+    assert f == {"GB/s": 6000.0, "frac_of_hbm_peak": 0.75, "fixed_us": 2.0}
+    noisy = [t + d for t, d in zip(us, (0.05, -0.05, -0.05, 0.05))]
+    g = bench.fit_fixed_rate(nb, noisy)
+    assert abs(g["GB/s"] - 6000.0) < 10 and abs(g["fixed_us"] - 2.0) < 0.1
